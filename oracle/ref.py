@@ -1,0 +1,258 @@
+"""Oracle for the MoE FFN step with group-affine quantized experts (fp64, CPU).
+
+TEST INFRASTRUCTURE: imported only by tests, the smoke check and the
+benchmark's CPU-baseline leg. Shares no code with the HIP path.
+
+Steps, in the order the flash-moe page runs them for one token and one layer
+("Flash-MoE - Chạy mô hình 397 tỷ tham số trên laptop", vi.news.hada.io,
+sections "Kiến trúc mô hình", "Kernel dequant tối ưu FMA", "Metal Compute
+Shaders", "Deferred GPU Expert Compute"):
+
+1. RMSNorm of the residual stream (optional: the tiny workload has none).
+2. Router logits, a plain mat-vec with float32 router weights.
+3. Top-K selection (the temporal tier first, then score, then lower index);
+   softmax over all logits and renormalisation over the selected K.
+4. Each selected expert and the shared expert: dequant mat-vec for gate and up,
+   SwiGLU (silu on gate), dequant mat-vec for down.
+5. Weighted combine plus the shared expert plus the residual.
+
+Prefill (one layer, T tokens) adds the bf16 rounding points of a bf16 GEMM:
+x_b = bf16(x); x_n = RMSNorm(x_b); router from the unrounded x_n; expert input
+bf16(x_n); weights bf16(deq); h bf16(silu(g)*u); y = x_b + sum w o + o_shared.
+
+Pins (see tests/test_oracle_*.py): integer-exact mat-vec (scale 1, bias 0),
+the bias-only closed form, one-hot column read-out, closed-form RMSNorm,
+softmax weights summing to 1, brute-force sort for selection, one-hot routing
+against a numpy float64 dense expert, zero experts giving the identity through
+a stack, the independent pure-Python brute force on tiny shapes, and the
+bf16-free prefill reducing to the decode oracle. No function is parity
+unpinned.
+"""
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qmoe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libqmoe_oracle.so")
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_F = ctypes.POINTER(ctypes.c_float)
+_U8 = ctypes.POINTER(ctypes.c_uint8)
+_U16 = ctypes.POINTER(ctypes.c_uint16)
+_I = ctypes.POINTER(ctypes.c_int)
+
+
+def build(force=False):
+    """Compile the oracle with gcc (no fusion, no reordering)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+                               "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.orc_round_bf16.restype = ctypes.c_double
+        L.orc_round_bf16.argtypes = [ctypes.c_double]
+        L.orc_rmsnorm.argtypes = [ctypes.c_int, _D, _F, ctypes.c_double, _D]
+        L.orc_router.argtypes = [ctypes.c_int, ctypes.c_int, _F, _D, _D]
+        L.orc_select.restype = ctypes.c_int
+        L.orc_select.argtypes = [ctypes.c_int, ctypes.c_int, _D, _D, ctypes.c_int, _I, ctypes.c_int,
+                                 _I, _D, _D]
+        L.orc_matvec.argtypes = [ctypes.c_int, ctypes.c_int, _U8, _U16, _U16, _D, ctypes.c_int, _D]
+        L.orc_expert.argtypes = [ctypes.c_int, ctypes.c_int] + [_U8, _U16, _U16] * 3 + \
+            [_D, ctypes.c_int, _D, _D]
+        L.orc_combine.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _D, ctypes.c_int, _D, _D, _D]
+        _lib = L
+    return _lib
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def round_bf16(v):
+    f = lib().orc_round_bf16
+    return np.vectorize(lambda z: f(float(z)), otypes=[np.float64])(np.asarray(v, dtype=np.float64))
+
+
+def rmsnorm(x, gamma=None, eps=1e-6):
+    x = _c(x, np.float64)
+    out = np.empty_like(x)
+    g = _c(gamma, np.float32) if gamma is not None else None
+    lib().orc_rmsnorm(x.size, _p(x, _D), _p(g, _F) if g is not None else None, eps, _p(out, _D))
+    return out
+
+
+def router(W, xn):
+    W = _c(W, np.float32)
+    xn = _c(xn, np.float64)
+    out = np.empty(W.shape[0], dtype=np.float64)
+    lib().orc_router(W.shape[0], W.shape[1], _p(W, _F), _p(xn, _D), _p(out, _D))
+    return out
+
+
+def select(logits, K, sel=None, by_sel=False, boosted=()):
+    """Returns (idx[K] in key order, w[K], gap)."""
+    logits = _c(logits, np.float64)
+    E = logits.size
+    s = _c(sel, np.float64) if sel is not None else None
+    b = _c(list(boosted) if len(boosted) else [0], np.int32)
+    idx = np.empty(K, dtype=np.int32)
+    w = np.empty(K, dtype=np.float64)
+    gap = np.empty(1, dtype=np.float64)
+    rc = lib().orc_select(E, K, _p(logits, _D), _p(s, _D) if s is not None else None, int(by_sel),
+                          _p(b, _I), len(boosted), _p(idx, _I), _p(w, _D), _p(gap, _D))
+    if rc != 0:
+        raise ValueError("orc_select: bad arguments")
+    return idx, w, float(gap[0])
+
+
+def weights_for(logits, idx):
+    """Renormalised softmax weights of a given selected set (used when the
+    oracle follows a set chosen elsewhere at a near-tie)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    m = logits.max()
+    p = np.exp(logits - m) / np.exp(logits - m).sum()
+    ps = p[list(idx)].sum()
+    return np.array([p[i] / ps for i in idx])
+
+
+def matvec(q, s, b, x, round_w_bf16=False):
+    q, s, b = _c(q, np.uint8), _c(s, np.uint16), _c(b, np.uint16)
+    x = _c(x, np.float64)
+    R, C = q.shape
+    y = np.empty(R, dtype=np.float64)
+    lib().orc_matvec(R, C, _p(q, _U8), _p(s, _U16), _p(b, _U16), _p(x, _D), int(round_w_bf16), _p(y, _D))
+    return y
+
+
+def expert(canon, x, bf16_points=False, return_h=False):
+    """canon = (codes[3], scales[3], biases[3]) in canonical form."""
+    cs, ss, bs = canon
+    I, H = cs[0].shape
+    arrs = []
+    for m in range(3):
+        arrs += [_c(cs[m], np.uint8), _c(ss[m], np.uint16), _c(bs[m], np.uint16)]
+    ptrs = []
+    for i, a in enumerate(arrs):
+        ptrs.append(_p(a, _U8 if i % 3 == 0 else _U16))
+    x = _c(x, np.float64)
+    o = np.empty(H, dtype=np.float64)
+    h = np.empty(I, dtype=np.float64)
+    lib().orc_expert(H, I, *ptrs, _p(x, _D), int(bf16_points), _p(o, _D), _p(h, _D))
+    return (o, h) if return_h else o
+
+
+def combine(x, w, o_routed, o_shared, residual=True):
+    x = _c(x, np.float64)
+    H = x.size
+    o = _c(np.concatenate([np.reshape(o_routed, (-1, H)), np.reshape(o_shared, (-1, H))]), np.float64)
+    w = _c(w, np.float64)
+    y = np.empty(H, dtype=np.float64)
+    n_r = np.reshape(o_routed, (-1, H)).shape[0]
+    n_s = np.reshape(o_shared, (-1, H)).shape[0]
+    lib().orc_combine(H, n_r, n_s, _p(x, _D), int(residual), _p(w, _D), _p(o, _D), _p(y, _D))
+    return y
+
+
+class LayerResult:
+    def __init__(self, y, idx, w, gap, logits, xn):
+        self.y, self.idx, self.w, self.gap, self.logits, self.xn = y, idx, w, gap, logits, xn
+
+
+def layer_decode(x, router_W, get_expert, shared, K, rmsnorm_on=True, residual=True, gamma=None,
+                 eps=1e-6, boosted=(), sel=None, by_sel=False, force_idx=None):
+    """One decode layer for one token.
+
+    get_expert(e) -> canonical expert e; shared: list of canonical shared experts.
+    force_idx: a selected set to use instead of the oracle's own (near-tie follow).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    xn = rmsnorm(x, gamma, eps) if rmsnorm_on else x.copy()
+    logits = router(router_W, xn)
+    idx, w, gap = select(logits, K, sel=sel, by_sel=by_sel, boosted=boosted)
+    if force_idx is not None:
+        idx = np.asarray(force_idx, dtype=np.int32)
+        w = weights_for(logits, idx)
+    o_r = np.stack([expert(get_expert(int(e)), xn) for e in idx])
+    o_s = np.stack([expert(c, xn) for c in shared]) if shared else np.zeros((0, x.size))
+    y = combine(x, w, o_r, o_s, residual)
+    return LayerResult(y, idx, w, gap, logits, xn)
+
+
+def prefill_token(x, router_W, get_expert, shared, K, sel, gamma=None, eps=1e-6):
+    """One token of the batched prefill with the bf16 rounding points.
+    Selection uses ``sel`` alone (Gumbel-top-k scores)."""
+    xb = np.array([float(v) for v in np.asarray(x, dtype=np.float32)], dtype=np.float64)
+    xb = round_bf16(xb)
+    xn = rmsnorm(xb, gamma, eps)
+    logits = router(router_W, xn)
+    idx, w, gap = select(logits, K, sel=sel, by_sel=True)
+    a = round_bf16(xn)
+    o_r = np.stack([expert(get_expert(int(e)), a, bf16_points=True) for e in idx])
+    o_s = np.stack([expert(c, a, bf16_points=True) for c in shared]) if shared else np.zeros((0, xb.size))
+    y = combine(xb, w, o_r, o_s, residual=True)
+    return LayerResult(y, idx, w, gap, logits, xn)
+
+
+NEAR_TIE = 1e-5
+
+
+def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=None,
+                 rmsnorm_on=True, residual=True, eps=1e-6, follow=None, tokens=None):
+    """Decode stack: for each token t in order, for each layer l, x <- layer(x).
+    Attention is the identity between MoE blocks.
+
+    boost[t][l][j] = 1 boosts slot j of token t-1's selected set at layer l, with
+    the set sorted by expert index (the temporal-correlation tier).
+    follow(t, l, idx_oracle, gap) -> set to use (or None to keep the oracle's);
+    it lets a caller follow another implementation's set at a near-tie.
+    tokens: subset of token indices to evaluate (teacher-forced: token t's
+    boosted set then needs ``prev_sets``, supplied through ``follow`` history).
+    Returns (y [T][H] float64, idx [T][L][K] sorted by expert, gaps [T][L])."""
+    T = len(x_tokens)
+    H = np.asarray(x_tokens[0]).size
+    ys = np.zeros((T, H))
+    sets = np.zeros((T, n_layers, K), dtype=np.int32)
+    gaps = np.zeros((T, n_layers))
+    prev = None
+    for t in (range(T) if tokens is None else tokens):
+        x = np.asarray(x_tokens[t], dtype=np.float64)
+        for l in range(n_layers):
+            boosted = ()
+            if boost is not None and t > 0 and prev is not None:
+                ps = np.sort(prev[l])
+                boosted = tuple(int(ps[j]) for j in range(K) if boost[t][l][j])
+            r = layer_decode(x, router_of(l), lambda e, l=l: expert_of(l, e), shared_of(l), K,
+                             rmsnorm_on=rmsnorm_on, residual=residual, eps=eps, boosted=boosted)
+            if follow is not None:
+                f = follow(t, l, r.idx, r.gap)
+                if f is not None and set(int(v) for v in f) != set(int(v) for v in r.idx):
+                    r = layer_decode(x, router_of(l), lambda e, l=l: expert_of(l, e), shared_of(l), K,
+                                     rmsnorm_on=rmsnorm_on, residual=residual, eps=eps,
+                                     boosted=boosted, force_idx=f)
+            sets[t, l] = np.sort(r.idx)
+            gaps[t, l] = r.gap
+            x = r.y
+        ys[t] = x
+        prev = sets[t]
+    return ys, sets, gaps
+
+
+def silu(z):
+    return z / (1.0 + math.exp(-z)) if z > -700 else 0.0 * z
