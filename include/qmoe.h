@@ -1,0 +1,171 @@
+/*
+ * qmoe.h -- C ABI of libqmoe: the sparse Mixture-of-Experts FFN step with
+ * group-affine quantized experts, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the flash-moe write-up describes for one decode
+ * token and one layer ("Flash-MoE - Chạy mô hình 397 tỷ tham số trên laptop",
+ * vi.news.hada.io): a router picks K of E experts per token, an always-on shared
+ * expert runs beside them, each expert is a SwiGLU FFN whose weights are 4-bit
+ * (or 2-bit) codes with one (scale, bias) pair per 64-element group, and the
+ * outputs are combined with the routing weights and added to the residual
+ * (sections "Kiến trúc mô hình", "Kernel dequant tối ưu FMA", "Metal Compute
+ * Shaders", "Deferred GPU Expert Compute").
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "dev" are device pointers; "host" pointers are host memory.
+ *    The caller owns every buffer. The library never allocates or frees device
+ *    memory; scratch space is the caller's workspace `ws`, sized by
+ *    moe_workspace_bytes(). Workspace contents need no initialisation.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on that stream and returns; nothing blocks except
+ *    moe_device_status().
+ *  - Arguments are validated before anything is enqueued. On failure the call
+ *    returns a negative moe_status, enqueues nothing, and moe_last_error()
+ *    returns a message (per host thread). A failed HIP launch returns
+ *    MOE_ERR_HIP with the HIP error text.
+ *  - Two calls may run concurrently only on different streams with disjoint
+ *    workspaces and outputs.
+ *  - Supported shapes: hidden and inter are 64 * 2^k (64 .. 4096); group 64;
+ *    bits 4 or 2; 1 <= top_k <= 8, top_k <= n_experts <= 1024; n_shared 0..2.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,         /* null pointer, negative count, bad flag */
+  MOE_ERR_SHAPE = -2,       /* inconsistent sizes */
+  MOE_ERR_ALIGN = -3,       /* a device pointer is not 256-byte aligned */
+  MOE_ERR_UNSUPPORTED = -4, /* valid but not implemented (bits, group, limits) */
+  MOE_ERR_WORKSPACE = -5,   /* ws_bytes below moe_workspace_bytes() */
+  MOE_ERR_HIP = -6,         /* a HIP runtime call failed */
+  MOE_ERR_DEVICE = -7       /* a kernel reported an error (bad index, sync time-out) */
+} moe_status;
+
+/* flags */
+#define MOE_F_RMSNORM 1        /* normalise x before routing and experts (eps, gamma) */
+#define MOE_F_RESIDUAL 2       /* add the (pre-norm) input x to the output */
+#define MOE_F_SELECT_BY_BIAS 4 /* selection score = sel_bias alone (else logit + sel_bias) */
+#define MOE_F_PREFILL_BF16 8   /* moe_layer_forward: bf16 expert-grouped GEMM path */
+#define MOE_F_PHASED 16        /* decode: one kernel launch per phase (no grid barrier) */
+
+typedef struct {
+  int32_t hidden;    /* H: model width (gate/up input, down output) */
+  int32_t inter;     /* I: expert intermediate width */
+  int32_t n_experts; /* E: routed experts per layer */
+  int32_t top_k;     /* K: routed experts per token */
+  int32_t n_shared;  /* S: always-on shared experts, added with weight 1 */
+  int32_t bits;      /* code width: 4 or 2 */
+  int32_t group;     /* quantization group along the input dimension: 64 */
+  int32_t flags;     /* MOE_F_* */
+  float eps;         /* RMSNorm epsilon (inside the square root) */
+} moe_config;
+
+/* One layer's weights, all device pointers, 256-byte aligned. */
+typedef struct {
+  const void* experts;   /* n_experts packed experts, moe_packed_expert_bytes() apart */
+  const void* shared;    /* n_shared packed experts (NULL if n_shared == 0) */
+  const float* router_w; /* [n_experts][hidden] float32, row-major */
+  const float* gamma;    /* [hidden] RMSNorm weight, or NULL for all ones */
+} moe_layer_weights;
+
+/* Bytes of one packed expert (gate, up, down). 0 if the config is invalid.
+ * With H=4096, I=1024, 4-bit codes and bf16 (scale, bias) per 64-group this is
+ * 7,077,888 B = 6.75 MiB, the per-expert size the flash-moe page gives in its
+ * "SSD Expert Streaming" section. */
+size_t moe_packed_expert_bytes(const moe_config* cfg);
+
+/* Workspace bytes that suffice for any call below with at most n_tokens tokens
+ * and n_layers layers on this config. 0 if the config is invalid. */
+size_t moe_workspace_bytes(const moe_config* cfg, int32_t n_tokens, int32_t n_layers);
+
+/* Pack canonical experts into the device layout (offline; not on the timed path).
+ *   codes  dev [n][gate I*H | up I*H | down H*I] uint8, one code per byte, each
+ *          matrix row-major [out][in]; values must be < 2^bits.
+ *   scales dev [n][gate I*H/64 | up I*H/64 | down H*I/64] bf16 bit patterns,
+ *   biases dev same layout as scales. Group j of a row covers inputs [64j, 64j+64).
+ *   packed dev [n][moe_packed_expert_bytes(cfg)], 256-B aligned; packed_bytes is
+ *          its size. Codes out of range set the device error (MOE_ERR_DEVICE from
+ *          moe_device_status) and pack as code & (2^bits-1).
+ * The dequantised weight is w = q * scale + bias, the page's nibble*scale+bias
+ * ("Kernel dequant tối ưu FMA" section). The layout is expert-major: each expert
+ * is one contiguous unit (cf. the expert-major sidecar of "LOOM",
+ * alessandroviola.dev, "Cosa hanno stabilito gli esperimenti"). */
+moe_status moe_pack_weights(const moe_config* cfg, int32_t n, const uint8_t* codes,
+                            const uint16_t* scales, const uint16_t* biases, void* packed,
+                            size_t packed_bytes, void* ws, size_t ws_bytes, void* stream);
+
+/* Routing for T tokens.
+ *   x        dev [T][H] float32 input (normalised here when MOE_F_RMSNORM is set)
+ *   router_w dev [E][H] float32;  gamma dev [H] or NULL
+ *   sel_bias dev [T][E] float32 or NULL: added to the logit for selection only
+ *            (or the whole selection score with MOE_F_SELECT_BY_BIAS)
+ *   boosted  dev [T][K] int32 or NULL: experts ranked ahead of all others
+ *            (a tier above the score), -1 = unused slot
+ *   idx_out  dev [T][K] int32: selected experts, by descending (tier, score),
+ *            ties to the lower index
+ *   w_out    dev [T][K] float32: softmax of the router logits renormalised over
+ *            the selected K (equal to a softmax over the K selected logits)
+ *   logits_out dev [T][E] float32 or NULL. */
+moe_status moe_route(const moe_config* cfg, int32_t T, const float* x, const float* router_w,
+                     const float* gamma, const float* sel_bias, const int32_t* boosted,
+                     int32_t* idx_out, float* w_out, float* logits_out, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* One expert on T tokens: y[t] = Wd (silu(Wg x[t]) * (Wu x[t])) in float32
+ * (no norm, no routing weight, no residual).
+ *   packed_expert dev, one packed expert;  x dev [T][H];  y dev [T][H]. */
+moe_status moe_expert_forward(const moe_config* cfg, const void* packed_expert, int32_t T,
+                              const float* x, float* y, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* One MoE layer on T tokens:
+ *   y = [x if MOE_F_RESIDUAL] + sum_k w_k * expert_{idx_k}(x_n) + sum_s shared_s(x_n),
+ *   x_n = RMSNorm(x) if MOE_F_RMSNORM else x.
+ * Decode path (default): float32 activations, tokens processed one after another.
+ * MOE_F_PREFILL_BF16: all T tokens at once as an expert-grouped bf16 GEMM with
+ *   float32 accumulation; rounding points x_b = bf16(x), A = bf16(x_n) (router from
+ *   the unrounded x_n), W = bf16(q*s+b), h = bf16(silu(g)*u); y = x_b + ....
+ *   x dev [T][H] float32; y dev [T][H] float32; sel_bias, boosted as in moe_route;
+ *   idx_out, w_out dev [T][K] or NULL. */
+moe_status moe_layer_forward(const moe_config* cfg, const moe_layer_weights* layer, int32_t T,
+                             const float* x, float* y, const float* sel_bias,
+                             const int32_t* boosted, int32_t* idx_out, float* w_out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* L-layer decode stack for T tokens, strictly in order, entirely on the device
+ * (one launch unless MOE_F_PHASED). Between MoE blocks the rest of the model is
+ * the identity, so token t enters layer 0 with x0[t] and layer l+1 receives
+ * layer l's output. Temporal routing correlation: at token t > 0 and layer l,
+ * slot j of token t-1's selected set at layer l (sorted by expert index) is
+ * ranked in the tier above all others when boost_mask[t][l][j] != 0.
+ *   layers     host [L] layer weights (copied into the workspace)
+ *   x0         dev [T][H];  y dev [T][H] (output of the last layer)
+ *   boost_mask dev [T][L][K] uint8 or NULL
+ *   idx_trace  dev [T][L][K] int32 or NULL (selected experts, key order)
+ *   w_trace    dev [T][L][K] float32 or NULL. */
+moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_layer_weights* layers,
+                            int32_t T, const float* x0, const uint8_t* boost_mask, float* y,
+                            int32_t* idx_trace, float* w_trace, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Message for the last non-OK status returned on this host thread. */
+const char* moe_last_error(void);
+
+/* Synchronises `stream`, then reads and clears the device error word in `ws`.
+ * Every entry point clears that word when it starts, so this reports the most
+ * recent call that used `ws`: MOE_OK, or MOE_ERR_DEVICE with a message naming
+ * the cause. */
+moe_status moe_device_status(void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H */

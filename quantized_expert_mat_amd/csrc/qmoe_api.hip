@@ -1,0 +1,342 @@
+// qmoe_api.hip -- the extern "C" entry points of libqmoe: argument validation,
+// workspace carve-up and dispatch to the kernels. See include/qmoe.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "qmoe_internal.h"
+
+namespace qmoe {
+hipError_t launch_pack(const Geo& geo, int n, const uint8_t* codes, const uint16_t* scales,
+                       const uint16_t* biases, void* packed, unsigned* err, hipStream_t stream);
+struct DecodeRequest {
+  int mode;
+  moe_config cfg;
+  int L, T;
+  const LayerPtrs* layers_dev;
+  const uint8_t* single_expert;
+  const float* x0;
+  float* y;
+  const uint8_t* boost_mask;
+  const float* sel_bias;
+  const int* boosted;
+  int* idx_out;
+  float* w_out;
+  float* logits_out;
+  uint8_t* ws;
+  WsLayout wl;
+  bool phased;
+};
+hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char** why);
+size_t prefill_ws_bytes(const moe_config& c, int T);
+moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int T,
+                           const float* x, float* y, const float* sel_bias, const int32_t* boosted,
+                           int32_t* idx_out, float* w_out, uint8_t* ws, size_t ws_bytes,
+                           hipStream_t stream, std::string* msg);
+}  // namespace qmoe
+
+using namespace qmoe;
+
+namespace {
+
+thread_local std::string g_msg;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_msg = buf;
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kKnownFlags =
+    MOE_F_RMSNORM | MOE_F_RESIDUAL | MOE_F_SELECT_BY_BIAS | MOE_F_PREFILL_BF16 | MOE_F_PHASED;
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_ARG, "config is NULL");
+  if (!pow2_dim_ok(c->hidden))
+    return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: must be 64*2^k, 64..4096", c->hidden);
+  if (!pow2_dim_ok(c->inter))
+    return fail(MOE_ERR_UNSUPPORTED, "inter=%d: must be 64*2^k, 64..4096", c->inter);
+  if (c->group != 64) return fail(MOE_ERR_UNSUPPORTED, "group=%d: only 64", c->group);
+  if (c->bits != 4 && c->bits != 2) return fail(MOE_ERR_UNSUPPORTED, "bits=%d: only 4 or 2", c->bits);
+  if (c->top_k < 1 || c->top_k > kMaxK)
+    return fail(MOE_ERR_UNSUPPORTED, "top_k=%d: must be 1..%d", c->top_k, kMaxK);
+  if (c->n_experts < c->top_k || c->n_experts > kMaxE)
+    return fail(MOE_ERR_SHAPE, "n_experts=%d: must be top_k..%d", c->n_experts, kMaxE);
+  if (c->n_shared < 0 || c->n_shared > kMaxShared)
+    return fail(MOE_ERR_UNSUPPORTED, "n_shared=%d: must be 0..%d", c->n_shared, kMaxShared);
+  if (c->flags & ~kKnownFlags) return fail(MOE_ERR_ARG, "unknown flags 0x%x", c->flags);
+  if ((c->flags & MOE_F_RMSNORM) && !(c->eps > 0.f && c->eps < 1.f))
+    return fail(MOE_ERR_ARG, "eps=%g must be in (0, 1)", (double)c->eps);
+  return MOE_OK;
+}
+
+moe_status check_ws(const moe_config* c, int T, int L, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(MOE_ERR_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_ALIGN, "workspace not 256-byte aligned");
+  const size_t need = moe_workspace_bytes(c, T, L);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  return MOE_OK;
+}
+
+#define REQUIRE(cond, status, ...)      \
+  do {                                  \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+moe_status upload_layers(const moe_config& c, int L, const moe_layer_weights* layers, uint8_t* ws,
+                         const WsLayout& wl, hipStream_t st) {
+  LayerPtrs tmp[64];
+  LayerPtrs* dev = reinterpret_cast<LayerPtrs*>(ws + wl.layers);
+  for (int l0 = 0; l0 < L; l0 += 64) {
+    const int n = L - l0 < 64 ? L - l0 : 64;
+    for (int i = 0; i < n; ++i) {
+      const moe_layer_weights& w = layers[l0 + i];
+      REQUIRE(w.experts && w.router_w, MOE_ERR_ARG, "layer %d: experts/router_w is NULL", l0 + i);
+      REQUIRE(c.n_shared == 0 || w.shared, MOE_ERR_ARG, "layer %d: shared is NULL", l0 + i);
+      REQUIRE(aligned(w.experts, 256) && aligned(w.router_w, 256) &&
+                  (!w.shared || aligned(w.shared, 256)) && (!w.gamma || aligned(w.gamma, 16)),
+              MOE_ERR_ALIGN, "layer %d: weight pointers must be 256-byte aligned", l0 + i);
+      tmp[i].experts = static_cast<const uint8_t*>(w.experts);
+      tmp[i].shared = static_cast<const uint8_t*>(w.shared);
+      tmp[i].router = w.router_w;
+      tmp[i].gamma = w.gamma;
+    }
+    hipError_t e = hipMemcpyAsync(dev + l0, tmp, sizeof(LayerPtrs) * n, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "uploading the layer table");
+    // the staging array is reused by the next chunk: make the copy complete first
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "uploading the layer table");
+  }
+  return MOE_OK;
+}
+
+moe_status run_decode(DecodeRequest& r, hipStream_t st) {
+  const char* why = nullptr;
+  hipError_t e = launch_decode(r, st, &why);
+  if (why) return fail(MOE_ERR_UNSUPPORTED, "%s", why);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_packed_expert_bytes(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return make_geo(cfg->hidden, cfg->inter, cfg->bits).expert_bytes;
+}
+
+size_t moe_workspace_bytes(const moe_config* cfg, int32_t n_tokens, int32_t n_layers) {
+  if (check_config(cfg) != MOE_OK || n_tokens < 0 || n_layers < 0) return 0;
+  size_t dec = ws_layout(*cfg, n_tokens, n_layers < 1 ? 1 : n_layers).total;
+  size_t pre = prefill_ws_bytes(*cfg, n_tokens);
+  return dec > pre ? dec : pre;
+}
+
+moe_status moe_pack_weights(const moe_config* cfg, int32_t n, const uint8_t* codes,
+                            const uint16_t* scales, const uint16_t* biases, void* packed,
+                            size_t packed_bytes, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  REQUIRE(n >= 0, MOE_ERR_ARG, "n=%d", n);
+  if (n == 0) return MOE_OK;
+  REQUIRE(codes && scales && biases && packed, MOE_ERR_ARG, "NULL pointer");
+  REQUIRE(aligned(codes, 16), MOE_ERR_ALIGN, "codes must be 16-byte aligned");
+  REQUIRE(aligned(scales, 2) && aligned(biases, 2), MOE_ERR_ALIGN, "scales/biases misaligned");
+  REQUIRE(aligned(packed, 256), MOE_ERR_ALIGN, "packed must be 256-byte aligned");
+  s = check_ws(cfg, 0, 1, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  const Geo geo = make_geo(cfg->hidden, cfg->inter, cfg->bits);
+  REQUIRE(packed_bytes >= geo.expert_bytes * (size_t)n, MOE_ERR_SHAPE,
+          "packed_bytes %zu < %d x %zu", packed_bytes, n, geo.expert_bytes);
+  const WsLayout wl = ws_layout(*cfg, 0, 1);
+  unsigned* err = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(ws) + wl.err);
+  hipError_t e = launch_pack(geo, n, codes, scales, biases, packed, err, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, int32_t T, const float* x, const float* router_w,
+                     const float* gamma, const float* sel_bias, const int32_t* boosted,
+                     int32_t* idx_out, float* w_out, float* logits_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  REQUIRE(T >= 0, MOE_ERR_ARG, "T=%d", T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(x && router_w && idx_out && w_out, MOE_ERR_ARG, "NULL pointer");
+  REQUIRE(aligned(x, 16) && aligned(router_w, 256) && (!gamma || aligned(gamma, 16)),
+          MOE_ERR_ALIGN, "x/gamma must be 16-byte and router_w 256-byte aligned");
+  REQUIRE(!(cfg->flags & MOE_F_SELECT_BY_BIAS) || sel_bias, MOE_ERR_ARG,
+          "MOE_F_SELECT_BY_BIAS needs sel_bias");
+  s = check_ws(cfg, T, 1, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  const WsLayout wl = ws_layout(*cfg, T, 1);
+  moe_layer_weights lw = {router_w, nullptr, router_w, gamma};  // experts unused when routing
+  moe_config c1 = *cfg;
+  c1.n_shared = 0;
+  s = upload_layers(c1, 1, &lw, w8, wl, st);
+  if (s != MOE_OK) return s;
+  DecodeRequest r = {};
+  r.mode = 1;  // MODE_ROUTE
+  r.cfg = c1;
+  r.L = 1;
+  r.T = T;
+  r.layers_dev = reinterpret_cast<const LayerPtrs*>(w8 + wl.layers);
+  r.x0 = x;
+  r.sel_bias = sel_bias;
+  r.boosted = boosted;
+  r.idx_out = idx_out;
+  r.w_out = w_out;
+  r.logits_out = logits_out;
+  r.ws = w8;
+  r.wl = wl;
+  r.phased = (cfg->flags & MOE_F_PHASED) != 0;
+  return run_decode(r, st);
+}
+
+moe_status moe_expert_forward(const moe_config* cfg, const void* packed_expert, int32_t T,
+                              const float* x, float* y, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  REQUIRE(T >= 0, MOE_ERR_ARG, "T=%d", T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(packed_expert && x && y, MOE_ERR_ARG, "NULL pointer");
+  REQUIRE(aligned(packed_expert, 256), MOE_ERR_ALIGN, "packed_expert must be 256-byte aligned");
+  REQUIRE(aligned(x, 16) && aligned(y, 16), MOE_ERR_ALIGN, "x/y must be 16-byte aligned");
+  s = check_ws(cfg, T, 1, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  DecodeRequest r = {};
+  r.mode = 2;  // MODE_EXPERT
+  r.cfg = *cfg;
+  r.cfg.n_shared = 0;
+  r.L = 1;
+  r.T = T;
+  r.single_expert = static_cast<const uint8_t*>(packed_expert);
+  r.x0 = x;
+  r.y = y;
+  r.ws = w8;
+  r.wl = ws_layout(*cfg, T, 1);
+  r.phased = (cfg->flags & MOE_F_PHASED) != 0;
+  return run_decode(r, (hipStream_t)stream);
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, const moe_layer_weights* layer, int32_t T,
+                             const float* x, float* y, const float* sel_bias,
+                             const int32_t* boosted, int32_t* idx_out, float* w_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  REQUIRE(T >= 0, MOE_ERR_ARG, "T=%d", T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(layer && x && y, MOE_ERR_ARG, "NULL pointer");
+  REQUIRE(aligned(x, 16) && aligned(y, 16), MOE_ERR_ALIGN, "x/y must be 16-byte aligned");
+  REQUIRE(!(cfg->flags & MOE_F_SELECT_BY_BIAS) || sel_bias, MOE_ERR_ARG,
+          "MOE_F_SELECT_BY_BIAS needs sel_bias");
+  s = check_ws(cfg, T, 1, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  if (cfg->flags & MOE_F_PREFILL_BF16) {
+    std::string msg;
+    s = prefill_forward(*cfg, layer, T, x, y, sel_bias, boosted, idx_out, w_out, w8, ws_bytes, st,
+                        &msg);
+    if (s != MOE_OK) g_msg = msg;
+    return s;
+  }
+  const WsLayout wl = ws_layout(*cfg, T, 1);
+  s = upload_layers(*cfg, 1, layer, w8, wl, st);
+  if (s != MOE_OK) return s;
+  DecodeRequest r = {};
+  r.mode = 0;  // MODE_LAYER
+  r.cfg = *cfg;
+  r.L = 1;
+  r.T = T;
+  r.layers_dev = reinterpret_cast<const LayerPtrs*>(w8 + wl.layers);
+  r.x0 = x;
+  r.y = y;
+  r.sel_bias = sel_bias;
+  r.boosted = boosted;
+  r.idx_out = idx_out;
+  r.w_out = w_out;
+  r.ws = w8;
+  r.wl = wl;
+  r.phased = (cfg->flags & MOE_F_PHASED) != 0;
+  return run_decode(r, st);
+}
+
+moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_layer_weights* layers,
+                            int32_t T, const float* x0, const uint8_t* boost_mask, float* y,
+                            int32_t* idx_trace, float* w_trace, void* ws, size_t ws_bytes,
+                            void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  REQUIRE(L >= 1 && T >= 0, MOE_ERR_ARG, "L=%d T=%d", L, T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(!(cfg->flags & (MOE_F_PREFILL_BF16 | MOE_F_SELECT_BY_BIAS)), MOE_ERR_ARG,
+          "stack decode takes neither MOE_F_PREFILL_BF16 nor MOE_F_SELECT_BY_BIAS");
+  REQUIRE(layers && x0 && y, MOE_ERR_ARG, "NULL pointer");
+  REQUIRE(aligned(x0, 16) && aligned(y, 16), MOE_ERR_ALIGN, "x0/y must be 16-byte aligned");
+  s = check_ws(cfg, T, L, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  const WsLayout wl = ws_layout(*cfg, T, L);
+  s = upload_layers(*cfg, L, layers, w8, wl, st);
+  if (s != MOE_OK) return s;
+  DecodeRequest r = {};
+  r.mode = 0;
+  r.cfg = *cfg;
+  r.L = L;
+  r.T = T;
+  r.layers_dev = reinterpret_cast<const LayerPtrs*>(w8 + wl.layers);
+  r.x0 = x0;
+  r.y = y;
+  r.boost_mask = boost_mask;
+  r.idx_out = idx_trace;
+  r.w_out = w_trace;
+  r.ws = w8;
+  r.wl = wl;
+  r.phased = (cfg->flags & MOE_F_PHASED) != 0;
+  return run_decode(r, st);
+}
+
+const char* moe_last_error(void) { return g_msg.c_str(); }
+
+moe_status moe_device_status(void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(ws && ws_bytes >= 768, MOE_ERR_ARG, "workspace is NULL or too small");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  unsigned v = 0;
+  e = hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the device error word");
+  if (v == 0) return MOE_OK;
+  const unsigned zero = 0;
+  e = hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "clearing the device error word");
+  switch (v) {
+    case DEV_BAD_INDEX: return fail(MOE_ERR_DEVICE, "device: expert index out of range");
+    case DEV_SYNC_TIMEOUT: return fail(MOE_ERR_DEVICE, "device: grid barrier timed out");
+    case DEV_BAD_CODE: return fail(MOE_ERR_DEVICE, "device: pack input code >= 2^bits");
+    default: return fail(MOE_ERR_DEVICE, "device error %u", v);
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// qmoe_internal.h -- packed layout geometry, argument structs and device helpers
+// shared by the HIP kernels of libqmoe (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qmoe.h"
+
+namespace qmoe {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 64;
+constexpr int kMaxK = 8;
+constexpr int kMaxE = 1024;
+constexpr int kMaxShared = 2;
+constexpr int kMaxDim = 4096;
+constexpr int kDigitStride = 52;  // dwords per (vector, group) in LDS: 48 digit dwords + pad
+
+// ---------------------------------------------------------------------------
+// Packed expert layout.
+//
+// Each matrix W[R][C] (R outputs, C inputs, G = C/64 groups per row) is stored as
+// blocks of P = 64/G rows. A block has 64 "slots", slot = p*G + g for row p of the
+// block and group g, so one wave of 64 lanes reads a whole block with one slot per
+// lane (lane-contiguous, fully coalesced 16-byte loads):
+//   4-bit: [chunk0: 64 slots x 16 B][chunk1: 64 slots x 16 B][sb: 64 slots x 4 B]
+//          = 2304 B; chunk c of a slot holds codes 32c..32c+31 of the group.
+//   2-bit: [codes: 64 slots x 16 B][sb: 64 slots x 4 B] = 1280 B.
+// sb = (bias_bf16 << 16) | scale_bf16.
+// Inside a 4-bit chunk, dword j holds the 8 codes 8j'..8j'+7 of the group
+// (j' = 4c + j) in "digit order": nibble 2m <- code 8j'+m, nibble 2m+1 <- code
+// 8j'+4+m (m = 0..3), each stored as (q ^ 8), i.e. q - 8 as a signed 4-bit value.
+// Inside a 2-bit slot, dword j holds codes 16j..16j+15: bits [4n, 4n+2) hold code
+// 16j + d(n) and bits [4n+2, 4n+4) hold code 16j + 8 + d(n), d(2m) = m,
+// d(2m+1) = 4 + m, unsigned.
+// An expert is [gate blocks][up blocks][down blocks]; gate/up have R = I, C = H
+// and down has R = H, C = I. Blocks are multiples of 256 B, so every block of an
+// expert that starts 256-B aligned is 256-B aligned too.
+// ---------------------------------------------------------------------------
+struct Geo {
+  int H, I, bits;
+  int Gh, Ph;        // groups per gate/up row, rows per gate/up block
+  int Gi, Pi;        // groups per down row, rows per down block
+  int blk;           // bytes per block
+  int nblk_gu;       // blocks in the gate (and in the up) matrix
+  int nblk_d;        // blocks in the down matrix
+  size_t off_up;     // byte offset of the up matrix inside an expert
+  size_t off_down;   // byte offset of the down matrix
+  size_t expert_bytes;
+};
+
+__host__ __device__ inline int log2i(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+__host__ __device__ inline bool pow2_dim_ok(int v) {
+  return v >= 64 && v <= kMaxDim && (v & (v - 1)) == 0;
+}
+
+__host__ __device__ inline Geo make_geo(int H, int I, int bits) {
+  Geo g;
+  g.H = H; g.I = I; g.bits = bits;
+  g.Gh = H / kGroup; g.Ph = kWave / g.Gh;
+  g.Gi = I / kGroup; g.Pi = kWave / g.Gi;
+  g.blk = bits == 4 ? 2304 : 1280;
+  g.nblk_gu = (I + g.Ph - 1) / g.Ph;
+  g.nblk_d = (H + g.Pi - 1) / g.Pi;
+  g.off_up = (size_t)g.nblk_gu * g.blk;
+  g.off_down = 2 * g.off_up;
+  g.expert_bytes = g.off_down + (size_t)g.nblk_d * g.blk;
+  return g;
+}
+
+// Device copy of one layer's pointers.
+struct LayerPtrs {
+  const uint8_t* experts;
+  const uint8_t* shared;
+  const float* router;
+  const float* gamma;
+};
+
+// Workspace layout (byte offsets from the workspace base; all 256-B aligned).
+struct WsLayout {
+  size_t err, sync, xbuf, logits, hbuf, sel, prev, layers, pack_err, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(const moe_config& c, int T, int L) {
+  (void)T;
+  WsLayout w;
+  size_t o = 0;
+  w.err = o; o += 256;
+  w.sync = o; o += 256;
+  w.pack_err = o; o += 256;
+  w.xbuf = o; o = align256(o + 2 * sizeof(float) * c.hidden);
+  w.logits = o; o = align256(o + sizeof(float) * c.n_experts);
+  w.hbuf = o; o = align256(o + sizeof(float) * (size_t)(kMaxK + kMaxShared) * c.inter);
+  w.sel = o; o = align256(o + 2 * sizeof(int) * kMaxK);
+  w.prev = o; o = align256(o + sizeof(int) * 2 * (size_t)(L > 0 ? L : 1) * kMaxK);
+  w.layers = o; o = align256(o + sizeof(LayerPtrs) * (size_t)(L > 0 ? L : 1));
+  w.total = o;
+  return w;
+}
+
+// Device error codes (written to the workspace error word; first error wins).
+enum DevErr : unsigned {
+  DEV_OK = 0,
+  DEV_BAD_INDEX = 1,     // an expert index outside [0, E)
+  DEV_SYNC_TIMEOUT = 2,  // a grid barrier wait exceeded its time limit
+  DEV_BAD_CODE = 3,      // pack: a code >= 2^bits
+};
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+__device__ inline float bf16lo_to_f32(unsigned v) { return __uint_as_float(v << 16); }
+__device__ inline float bf16hi_to_f32(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ inline void set_dev_err(unsigned* err, unsigned code) {
+  unsigned expected = 0;
+  __hip_atomic_compare_exchange_strong(err, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace qmoe

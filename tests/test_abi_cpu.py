@@ -1,0 +1,92 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point the
+header declares, computes the closed-form sizes, and rejects bad arguments
+before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_expert_mat_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "qmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared()
+    assert set(names) == set(q.EXPORTS)
+    L = ctypes.CDLL(q.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_packed_expert_bytes_closed_form():
+    # 3 matrices of H*I codes at bits/8 bytes + one bf16 (scale, bias) pair per 64 codes
+    for H, I, bits in [(4096, 1024, 4), (4096, 1024, 2), (1024, 256, 4), (64, 64, 2), (4096, 4096, 4)]:
+        cfg = q.Config.make(H, I, 8, 4, 1, bits)
+        assert q.moe_packed_expert_bytes(cfg) == 3 * H * I * bits // 8 + 3 * H * I // 64 * 4
+    assert q.moe_packed_expert_bytes(q.Config.make(4096, 1024, 512)) == 7_077_888  # 6.75 MiB
+    assert q.moe_packed_expert_bytes(q.Config.make(4096, 1024, 512, bits=2)) == 3_932_160
+
+
+def test_workspace_bytes_positive_and_monotone():
+    cfg = q.Config.make(4096, 1024, 512)
+    a = q.moe_workspace_bytes(cfg, 1, 1)
+    b = q.moe_workspace_bytes(cfg, 256, 60)
+    assert 0 < a <= b
+    assert q.moe_workspace_bytes(cfg, -1, 1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=3), q.MOE_ERR_UNSUPPORTED), (dict(hidden=1000), q.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=8192), q.MOE_ERR_UNSUPPORTED), (dict(top_k=9), q.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=2, top_k=4), q.MOE_ERR_SHAPE), (dict(n_experts=2000), q.MOE_ERR_SHAPE),
+    (dict(n_shared=3), q.MOE_ERR_UNSUPPORTED), (dict(group=32), q.MOE_ERR_UNSUPPORTED),
+    (dict(flags=1 << 10), q.MOE_ERR_ARG), (dict(flags=q.MOE_F_RMSNORM, eps=0.0), q.MOE_ERR_ARG),
+])
+def test_bad_config_rejected(kw, status):
+    base = dict(hidden=1024, inter=256, n_experts=64)
+    base.update(kw)
+    cfg = q.Config.make(**base)
+    assert q.moe_packed_expert_bytes(cfg) == 0
+    L = q.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    rc = L.moe_expert_forward(ctypes.byref(cfg), fake, 1, fake, fake, fake, 1 << 20, None)
+    assert rc == status
+    assert L.moe_last_error()
+
+
+def test_null_misaligned_and_small_workspace_rejected():
+    L = q.lib()
+    cfg = q.Config.make(1024, 256, 64)
+    p = ctypes.c_void_p(1 << 20)
+    big = q.moe_workspace_bytes(cfg, 4, 1)
+    assert L.moe_expert_forward(ctypes.byref(cfg), None, 1, p, p, p, big, None) == q.MOE_ERR_ARG
+    assert L.moe_expert_forward(ctypes.byref(cfg), ctypes.c_void_p((1 << 20) + 8), 1, p, p, p, big,
+                                None) == q.MOE_ERR_ALIGN
+    assert L.moe_expert_forward(ctypes.byref(cfg), p, 4, p, p, p, 10, None) == q.MOE_ERR_WORKSPACE
+    assert L.moe_expert_forward(ctypes.byref(cfg), p, -1, p, p, p, big, None) == q.MOE_ERR_ARG
+    # T == 0 is a no-op that touches nothing
+    assert L.moe_expert_forward(ctypes.byref(cfg), None, 0, None, None, None, 0, None) == q.MOE_OK
+    assert L.moe_pack_weights(ctypes.byref(cfg), 1, p, p, p, p, 10, p, big, None) == q.MOE_ERR_SHAPE
+    lw = q.LayerWeights(1 << 20, 1 << 20, 1 << 20, None)
+    cfg_sel = cfg.with_flags(q.MOE_F_SELECT_BY_BIAS)
+    assert L.moe_layer_forward(ctypes.byref(cfg_sel), ctypes.byref(lw), 1, p, p, None, None, None, None, p,
+                               big, None) == q.MOE_ERR_ARG
+    arr = (q.LayerWeights * 1)(lw)
+    assert L.moe_stack_decode(ctypes.byref(cfg_sel), 1, arr, 1, p, None, p, None, None, p, big,
+                              None) == q.MOE_ERR_ARG
+    assert L.moe_device_status(None, 0, None) == q.MOE_ERR_ARG
+
+
+def test_binding_raises_with_message():
+    cfg = q.Config.make(1024, 256, 64, bits=3)
+    with pytest.raises(q.MoeError) as ei:
+        q._check(q.lib().moe_expert_forward(ctypes.byref(cfg), None, 1, None, None, None, 0, None))
+    assert "bits=3" in str(ei.value)

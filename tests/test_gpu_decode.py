@@ -1,0 +1,272 @@
+"""GPU parity of the decode path (moe_expert_forward, moe_route, moe_layer_forward,
+moe_stack_decode) against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import quantized_expert_mat_amd as q
+import workload as wl
+from oracle import ref
+from tests.helpers import NEAR_TIE, DeviceLayer, HostLayer, config_for, parity, same_set
+from workload import device as wdev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TINY = wl.CONFIGS[0]   # H 1024, I 256, E 64, no norm / residual
+LAYER = wl.CONFIGS[1]  # H 4096, I 1024, E 512, norm + residual
+
+
+def small(**kw):
+    base = dict(name="small", hidden=512, inter=128, n_experts=24, top_k=4, n_shared=1)
+    base.update(kw)
+    return wl.WorkloadConfig(**base)
+
+
+def ws_for(cfg, T=1, L=1):
+    return torch.empty(q.moe_workspace_bytes(cfg, T, L), dtype=torch.uint8, device="cuda")
+
+
+def xs(w, T, seed_shift=0):
+    return wl.tokens_x(w.seed + 1000 + seed_shift, T, w.hidden)
+
+
+# ------------------------------------------------------------------ generator
+
+def test_device_generator_matches_host():
+    spec = wl.ExpertSpec(256, 128, bits=4)
+    codes = torch.empty((2, 3, 256 * 128), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((2, 3, 512), dtype=torch.int16, device="cuda")
+    bi = torch.empty((2, 3, 512), dtype=torch.int16, device="cuda")
+    keep = wdev.experts_canonical(spec, 7, 3, [5, 9], codes, sc, bi)
+    torch.cuda.synchronize()
+    for i, e in enumerate([5, 9]):
+        cs, ss, bs = wl.expert_canonical(spec, 7, 3, e)
+        for m in range(3):
+            assert np.array_equal(codes[i, m].cpu().numpy(), cs[m].reshape(-1))
+            assert np.array_equal(sc[i, m].cpu().numpy().view(np.uint16), ss[m].reshape(-1))
+            assert np.array_equal(bi[i, m].cpu().numpy().view(np.uint16), bs[m].reshape(-1))
+    r = torch.empty((8, 256), dtype=torch.float32, device="cuda")
+    wdev.router(7, 3, 8, 256, r)
+    x = torch.empty((3, 256), dtype=torch.float32, device="cuda")
+    wdev.tokens_x(11, 3, 256, x)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.cpu().numpy(), wl.router_weights(7, 3, 8, 256))
+    assert np.array_equal(x.cpu().numpy(), wl.tokens_x(11, 3, 256))
+    del keep
+    # 2-bit codes
+    spec2 = wl.ExpertSpec(256, 128, bits=2)
+    keep = wdev.experts_canonical(spec2, 7, 3, [5], codes[:1], sc[:1], bi[:1])
+    torch.cuda.synchronize()
+    cs, _, _ = wl.expert_canonical(spec2, 7, 3, 5)
+    assert np.array_equal(codes[0, 2].cpu().numpy(), cs[2].reshape(-1))
+
+
+# ------------------------------------------------------------------ expert forward
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("H,I", [(1024, 256), (512, 1024), (256, 64), (4096, 1024)])
+def test_expert_forward_parity(bits, H, I):
+    w = small(hidden=H, inter=I, n_experts=2, top_k=1, n_shared=0, bits=bits,
+              sigma_scale=0.02 if bits == 4 else 0.06)
+    dl = DeviceLayer(w, 0)
+    hl = HostLayer(w, 0)
+    T = 3
+    cfg = config_for(w)
+    x = xs(w, T)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    ws = ws_for(cfg, T)
+    for e in range(2):
+        q.moe_expert_forward(cfg, dl.experts[e * dl.expert_bytes:(e + 1) * dl.expert_bytes], T, xd, y, ws)
+        q.moe_device_status(ws)
+        yh = y.cpu().numpy()
+        for t in range(T):
+            parity(yh[t], ref.expert(hl.expert(e), x[t]), f"expert {e} token {t} bits {bits}")
+
+
+def test_expert_forward_integer_exact():
+    """scale 1, bias 0, integer x: gate/up are exact integers, so h and y only see
+    float32 rounding of silu; compare against the oracle at 1e-6."""
+    H, I = 512, 128
+    cfg = q.Config.make(H, I, 1, 1, 0, 4)
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 16, size=(1, 3, H * I), dtype=np.uint8)
+    ones = np.full((1, 3, H * I // 64), 0x3F80, np.uint16)
+    zeros = np.zeros_like(ones)
+    # down scaled down so that h (up to ~1e7) does not dominate rounding
+    ones[0, 2] = wl.bf16_bits_from_f32(np.full(H * I // 64, 2.0 ** -20, np.float32))
+    packed = torch.empty(q.moe_packed_expert_bytes(cfg), dtype=torch.uint8, device="cuda")
+    ws = ws_for(cfg, 2)
+    q.moe_pack_weights(cfg, 1, torch.from_numpy(codes).cuda(), torch.from_numpy(ones.view(np.int16)).cuda(),
+                       torch.from_numpy(zeros.view(np.int16)).cuda(), packed, ws)
+    x = rng.integers(-8, 9, size=(2, H)).astype(np.float32) / 64.0
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    q.moe_expert_forward(cfg, packed, 2, xd, y, ws)
+    q.moe_device_status(ws)
+    canon = ([codes[0, 0].reshape(I, H), codes[0, 1].reshape(I, H), codes[0, 2].reshape(H, I)],
+             [ones[0, 0].reshape(I, H // 64), ones[0, 1].reshape(I, H // 64), ones[0, 2].reshape(H, I // 64)],
+             [zeros[0, 0].reshape(I, H // 64), zeros[0, 1].reshape(I, H // 64), zeros[0, 2].reshape(H, I // 64)])
+    for t in range(2):
+        o, h = ref.expert(canon, x[t], return_h=True)
+        np.testing.assert_allclose(y.cpu().numpy()[t], o, rtol=2e-6, atol=1e-6 * np.abs(o).max())
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("phased", [False, True])
+def test_route_parity(phased):
+    w = small(n_experts=100, top_k=6, hidden=1024)
+    cfg = config_for(w, q.MOE_F_PHASED if phased else 0)
+    hl = HostLayer(w, 0)
+    T = 8
+    x = xs(w, T)
+    router = torch.from_numpy(hl.router).cuda()
+    idx = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((T, w.n_experts), dtype=torch.float32, device="cuda")
+    boosted = np.full((T, w.top_k), -1, np.int32)
+    boosted[2, :2] = [99, 3]
+    boosted[5, 0] = 50
+    ws = ws_for(cfg, T)
+    q.moe_route(cfg, T, torch.from_numpy(x).cuda(), router, idx, wts, ws,
+                boosted=torch.from_numpy(boosted).cuda(), logits_out=logits)
+    q.moe_device_status(ws)
+    idx_h, w_h, lg_h = idx.cpu().numpy(), wts.cpu().numpy(), logits.cpu().numpy()
+    for t in range(T):
+        xn = ref.rmsnorm(x[t])
+        lg = ref.router(hl.router, xn)
+        np.testing.assert_allclose(lg_h[t], lg, rtol=0, atol=1e-5 * np.abs(lg).max())
+        b = [int(v) for v in boosted[t] if v >= 0]
+        oi, ow, gap = ref.select(lg, w.top_k, boosted=b)
+        if not same_set(oi, idx_h[t]):
+            assert gap < NEAR_TIE, f"token {t}: sets differ {sorted(oi)} vs {sorted(idx_h[t])}, gap {gap}"
+            continue
+        assert set(b) <= set(idx_h[t].tolist())
+        wmap = dict(zip(idx_h[t].tolist(), w_h[t].tolist()))
+        np.testing.assert_allclose([wmap[int(e)] for e in oi], ow, rtol=1e-5, atol=1e-6)
+        assert abs(w_h[t].sum() - 1) < 1e-5
+
+
+# ------------------------------------------------------------------ one layer
+
+@pytest.mark.parametrize("wcfg,T,phased", [
+    (TINY, 3, False), (TINY, 2, True),
+    (small(), 4, False), (small(bits=2, sigma_scale=0.06), 3, False),
+    (small(n_shared=0, top_k=1), 2, False), (small(n_shared=2, top_k=8, n_experts=8), 2, False),
+    (small(top_k=3, n_experts=37, hidden=256, inter=64), 3, True),
+])
+def test_layer_forward_parity(wcfg, T, phased):
+    cfg = config_for(wcfg, q.MOE_F_PHASED if phased else 0)
+    dl = DeviceLayer(wcfg, 0)
+    hl = HostLayer(wcfg, 0)
+    x = xs(wcfg, T)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    idx = torch.empty((T, wcfg.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, wcfg.top_k), dtype=torch.float32, device="cuda")
+    ws = ws_for(cfg, T)
+    q.moe_layer_forward(cfg, dl.weights(), T, xd, y, ws, idx_out=idx, w_out=wts)
+    q.moe_device_status(ws)
+    yh, ih = y.cpu().numpy(), idx.cpu().numpy()
+    for t in range(T):
+        r = ref.layer_decode(x[t], hl.router, hl.expert, hl.shared(), wcfg.top_k,
+                             rmsnorm_on=wcfg.rmsnorm, residual=wcfg.residual)
+        if not same_set(r.idx, ih[t]):
+            assert r.gap < NEAR_TIE, f"token {t}: sets differ, gap {r.gap}"
+            r = ref.layer_decode(x[t], hl.router, hl.expert, hl.shared(), wcfg.top_k,
+                                 rmsnorm_on=wcfg.rmsnorm, residual=wcfg.residual, force_idx=ih[t])
+        parity(yh[t], r.y, f"{wcfg.name} token {t}")
+
+
+def test_layer_forward_full_size_one_token():
+    """The flash-moe layer shape: hidden 4096, 512 experts, I 1024, top-4 + shared."""
+    dl = DeviceLayer(LAYER, 0)
+    hl = HostLayer(LAYER, 0)
+    cfg = config_for(LAYER)
+    T = 2
+    x = xs(LAYER, T)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    idx = torch.empty((T, 4), dtype=torch.int32, device="cuda")
+    ws = ws_for(cfg, T)
+    q.moe_layer_forward(cfg, dl.weights(), T, xd, y, ws, idx_out=idx)
+    q.moe_device_status(ws)
+    for t in range(T):
+        r = ref.layer_decode(x[t], hl.router, hl.expert, hl.shared(), 4)
+        if not same_set(r.idx, idx.cpu().numpy()[t]):
+            assert r.gap < NEAR_TIE
+            r = ref.layer_decode(x[t], hl.router, hl.expert, hl.shared(), 4, force_idx=idx.cpu().numpy()[t])
+        parity(y.cpu().numpy()[t], r.y, f"full layer token {t}")
+
+
+# ------------------------------------------------------------------ stack
+
+@pytest.mark.parametrize("bits,phased", [(4, False), (2, False), (4, True)])
+def test_stack_decode_parity(bits, phased):
+    w = small(hidden=512, inter=128, n_experts=16, bits=bits, sigma_scale=0.02 if bits == 4 else 0.06,
+              n_layers=4, n_tokens=6, temporal_p=0.27)
+    L, T, K = w.n_layers, w.n_tokens, w.top_k
+    cfg = config_for(w, q.MOE_F_PHASED if phased else 0)
+    dls = [DeviceLayer(w, l) for l in range(L)]
+    hls = [HostLayer(w, l) for l in range(L)]
+    x = xs(w, T)
+    mask = wl.boost_mask(w.seed + 5, T, L, K, 0.5)
+    y = torch.empty((T, w.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, L, K), dtype=torch.int32, device="cuda")
+    ws = ws_for(cfg, T, L)
+    q.moe_stack_decode(cfg, [d.weights() for d in dls], T, torch.from_numpy(x).cuda(), y, ws,
+                       boost_mask=torch.from_numpy(mask).cuda(), idx_trace=idx)
+    q.moe_device_status(ws)
+    ih = idx.cpu().numpy()
+    flagged = []
+
+    def follow(t, l, oi, gap):
+        if same_set(oi, ih[t, l]):
+            return None
+        assert gap < NEAR_TIE, f"t={t} l={l}: sets differ, gap {gap}"
+        flagged.append((t, l))
+        return ih[t, l]
+
+    ys, sets, _ = ref.stack_decode(x, L, lambda l: hls[l].router, lambda l, e: hls[l].expert(e),
+                                   lambda l: hls[l].shared(), K, boost=mask, follow=follow)
+    for t in range(T):
+        for l in range(L):
+            assert same_set(sets[t, l], ih[t, l])
+        parity(y.cpu().numpy()[t], ys[t], f"stack token {t}")
+    # boosted experts were selected
+    for t in range(1, T):
+        for l in range(L):
+            prev = sorted(ih[t - 1, l])
+            for j in range(K):
+                if mask[t, l, j]:
+                    assert prev[j] in ih[t, l]
+
+
+def test_stack_decode_deterministic():
+    w = small(n_layers=3, n_tokens=4)
+    cfg = config_for(w)
+    dls = [DeviceLayer(w, l) for l in range(3)]
+    x = torch.from_numpy(xs(w, 4)).cuda()
+    mask = torch.from_numpy(wl.boost_mask(1, 4, 3, 4)).cuda()
+    ws = ws_for(cfg, 4, 3)
+    outs = []
+    for _ in range(2):
+        y = torch.empty_like(x)
+        q.moe_stack_decode(cfg, [d.weights() for d in dls], 4, x, y, ws, boost_mask=mask)
+        q.moe_device_status(ws)
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_zero_tokens_is_a_no_op():
+    w = small()
+    cfg = config_for(w)
+    dl = DeviceLayer(w, 0)
+    ws = ws_for(cfg)
+    x = torch.zeros((1, w.hidden), device="cuda")
+    y = torch.full_like(x, 7.0)
+    q.moe_layer_forward(cfg, dl.weights(), 0, x, y, ws)
+    q.moe_stack_decode(cfg, [dl.weights()], 0, x, y, ws)
+    torch.cuda.synchronize()
+    assert float(y.max()) == 7.0

@@ -1,0 +1,102 @@
+// gen_device.hip -- device implementation of the counter-based workload generator
+// (the definition is in workload/gen.py; both produce identical bits). Input
+// generation only: no part of the MoE computation lives here.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
+
+__device__ inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+__device__ inline uint64_t word(uint64_t key, uint64_t i) { return mix64(key + (i + 1) * kGolden); }
+
+__device__ inline double normal(uint64_t key, uint64_t i) {
+  long long s = 0;
+  for (int j = 0; j < 3; ++j) {
+    const uint64_t w = word(key, 3 * i + j);
+    for (int h = 0; h < 4; ++h) s += (long long)((w >> (16 * h)) & 0xFFFFull);
+  }
+  return (double)(s - 393210) / 65536.0;
+}
+
+__device__ inline uint16_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// codes: out[k*n + i], one code per byte; one thread per 64-bit word of codes.
+__global__ void codes_kernel(const uint64_t* keys, int nkeys, long long n, int bits, uint8_t* out) {
+  const int per = 64 / bits;
+  const long long words_per_key = (n + per - 1) / per;
+  const long long total = words_per_key * nkeys;
+  const uint64_t mask = (1ull << bits) - 1ull;
+  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
+       t += (long long)gridDim.x * blockDim.x) {
+    const int k = (int)(t / words_per_key);
+    const long long wi = t % words_per_key;
+    const uint64_t w = word(keys[k], (uint64_t)wi);
+    uint8_t* dst = out + (long long)k * n + wi * per;
+    const long long left = n - wi * per;
+    if (left >= per && ((uintptr_t)dst % 16) == 0 && per % 16 == 0) {
+      for (int q = 0; q < per; q += 16) {
+        uint32_t v[4];
+        for (int b = 0; b < 4; ++b) {
+          uint32_t x = 0;
+          for (int c = 0; c < 4; ++c) x |= (uint32_t)((w >> (bits * (q + 4 * b + c))) & mask) << (8 * c);
+          v[b] = x;
+        }
+        *reinterpret_cast<uint4*>(dst + q) = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+      for (int c = 0; c < per && c < left; ++c) dst[c] = (uint8_t)((w >> (bits * c)) & mask);
+    }
+  }
+}
+
+__global__ void normal_kernel(const uint64_t* keys, int nkeys, long long n, double sigma, int absolute,
+                              int as_bf16, void* out) {
+  const long long total = n * nkeys;
+  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
+       t += (long long)gridDim.x * blockDim.x) {
+    const int k = (int)(t / n);
+    const long long i = t % n;
+    double v = normal(keys[k], (uint64_t)i);
+    if (absolute) v = fabs(v);
+    const float f = (float)(sigma * v);
+    if (as_bf16) static_cast<uint16_t*>(out)[t] = f32_to_bf16_bits(f);
+    else static_cast<float*>(out)[t] = f;
+  }
+}
+
+unsigned grid_for(long long total) {
+  long long b = (total + 255) / 256;
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return (unsigned)b;
+}
+
+}  // namespace
+
+extern "C" {
+
+// keys: device array of nkeys stream keys. Returns a hipError_t value.
+int qgen_codes(const uint64_t* keys, int nkeys, long long n, int bits, uint8_t* out, void* stream) {
+  const long long total = ((n + 64 / bits - 1) / (64 / bits)) * nkeys;
+  hipLaunchKernelGGL(codes_kernel, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)stream, keys, nkeys,
+                     n, bits, out);
+  return (int)hipGetLastError();
+}
+
+int qgen_normal(const uint64_t* keys, int nkeys, long long n, double sigma, int absolute, int as_bf16,
+                void* out, void* stream) {
+  hipLaunchKernelGGL(normal_kernel, dim3(grid_for(n * nkeys)), dim3(256), 0, (hipStream_t)stream, keys,
+                     nkeys, n, sigma, absolute, as_bf16, out);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"
