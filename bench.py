@@ -1,0 +1,215 @@
+#!/usr/bin/env python
+"""Decode benchmark: the 60-layer quantized MoE stack on one MI355X.
+
+One step = one moe_stack_decode call: 256 sequential decode tokens through 60
+MoE layers (RMSNorm -> router -> top-4 + shared expert -> SwiGLU experts ->
+weighted combine + residual), all expert weights resident in HBM, 27% of each
+token's routed experts repeating the previous token's (temporal tier).
+
+Prints one JSON line. `value` is decode tokens/s; `roofline` prices the decode
+kernel's algorithmic bytes (weights touched per token, the per-token figure
+below) against MI355X's 8 TB/s HBM; `cpu_baseline` is the CPU oracle timed on
+a bounded sample (token 0 through the first few layers) and scaled to tokens/s.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def per_token_bytes(w):
+    """Algorithmic bytes one token reads: per layer, the packed bytes of the K routed
+    and S shared experts plus the float32 router."""
+    import quantized_expert_mat_amd as q
+    from tests.helpers import config_for
+    eb = q.moe_packed_expert_bytes(config_for(w))
+    return w.n_layers * ((w.top_k + w.n_shared) * eb + 4 * w.n_experts * w.hidden)
+
+
+def cpu_baseline_and_parity(w, dls, hls, x0_host, n_layers, stack_fn):
+    """Time the oracle on token 0 through the first n_layers layers (weights
+    regenerated beforehand, outside the timing) and compare the GPU's output of
+    the same layers."""
+    import numpy as np
+    from oracle import ref
+    from tests.helpers import NEAR_TIE, parity, same_set
+    y_gpu, idx_gpu = stack_fn(n_layers)
+    # regenerate what the oracle will touch, following the GPU's sets (checked below)
+    for l in range(n_layers):
+        for e in list(idx_gpu[0, l]) + [w.n_experts + s for s in range(w.n_shared)]:
+            hls[l].expert(int(e))
+    flagged = []
+
+    def follow(t, l, oi, gap):
+        if same_set(oi, idx_gpu[t, l]):
+            return None
+        assert gap < NEAR_TIE, f"layer {l}: expert sets differ (gap {gap})"
+        flagged.append(l)
+        return idx_gpu[t, l]
+
+    t0 = time.perf_counter()
+    ys, sets, _ = ref.stack_decode(x0_host[:1], n_layers, lambda l: hls[l].router,
+                                   lambda l, e: hls[l].expert(e), lambda l: hls[l].shared(), w.top_k,
+                                   follow=follow)
+    dt = time.perf_counter() - t0
+    rel_max, rel_l2 = parity(y_gpu[0], ys[0], "bench spot check")
+    return dt, {"layers": n_layers, "tokens": 1, "max_rel_err": float(rel_max), "rel_l2": float(rel_l2),
+                "expert_sets_equal": not flagged, "near_tie_follows": len(flagged)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=2, help="2: 4-bit stack, 3: 2-bit stack")
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--tokens", type=int, default=None)
+    ap.add_argument("--cpu-layers", type=int, default=6)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--phased", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the decode stack fits one MI355X's HBM and this build has "
+              f"no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import quantized_expert_mat_amd as q
+    import workload as wl
+    from workload import device as wdev
+    from tests.helpers import DeviceLayer, HostLayer, config_for
+
+    w = wl.CONFIGS[args.config]
+    if args.layers or args.tokens:
+        w = w.replace(n_layers=args.layers or w.n_layers, n_tokens=args.tokens or w.n_tokens)
+    L, T, K, H = w.n_layers, w.n_tokens, w.top_k, w.hidden
+    flags = q.MOE_F_PHASED if args.phased else 0
+    cfg = config_for(w, flags)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name}, {props.multi_processor_count} CUs, {props.total_memory / 2**30:.1f} GiB")
+
+    t_setup = time.perf_counter()
+    ws = torch.empty(q.moe_workspace_bytes(cfg, T, L), dtype=torch.uint8, device=dev)
+    dls = []
+    for l in range(L):
+        dls.append(DeviceLayer(w, l, chunk=8, ws=ws))
+        if l % 10 == 9 or l == L - 1:
+            log(f"layer {l + 1}/{L} generated and packed ({time.perf_counter() - t_setup:.1f} s)")
+    layers = [d.weights() for d in dls]
+    x0 = torch.empty((T, H), dtype=torch.float32, device=dev)
+    keep = wdev.tokens_x(w.seed + 1000, T, H, x0)
+    mask = torch.from_numpy(wl.boost_mask(w.seed + 7, T, L, K, w.temporal_p or 0.0)).to(dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, L, K), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    log(f"setup {setup_s:.1f} s; resident weights {sum(d.experts.numel() + d.shared.numel() for d in dls) / 1e9:.2f} GB")
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        q.moe_stack_decode(cfg, layers, T, x0, y, ws, boost_mask=mask, idx_trace=idx, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    q.moe_device_status(ws)
+    log("warmup done")
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    q.moe_device_status(ws)
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    tok_s = T * args.steps / elapsed
+    ptb = per_token_bytes(w)
+    achieved = ptb * T / avg_launch_s / 1e9
+    log(f"{tok_s:.1f} tok/s, {elapsed / args.steps * 1e3:.2f} ms/step, launch avg {avg_launch_s * 1e3:.3f} ms, "
+        f"{achieved:.0f} GB/s")
+
+    # realised temporal repeat fraction (routing workload check)
+    ih = idx.cpu().numpy()
+    rep = np.mean([len(set(ih[t, l]) & set(ih[t - 1, l])) / K for t in range(1, T) for l in range(L)])
+
+    cpu = None
+    par = None
+    if not args.no_cpu:
+        hls = [HostLayer(w, l) for l in range(min(args.cpu_layers, L))]
+        x0h = x0.cpu().numpy()
+
+        def stack_fn(n):
+            ys = torch.empty((1, H), dtype=torch.float32, device=dev)
+            it = torch.empty((1, n, K), dtype=torch.int32, device=dev)
+            q.moe_stack_decode(cfg, layers[:n], 1, x0[:1], ys, ws, idx_trace=it)
+            q.moe_device_status(ws)
+            return ys.cpu().numpy(), it.cpu().numpy()
+
+        n = min(args.cpu_layers, L)
+        dt, par = cpu_baseline_and_parity(w, dls, hls, x0h, n, stack_fn)
+        cpu = {"value": round(1.0 / (dt / n * L), 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
+               "sample": f"token 0 through layers 0-{n - 1} of the {L}-layer stack "
+                         f"({dt:.1f} s single-threaded fp64 oracle), scaled to {L} layers"}
+        log(f"cpu oracle: {dt:.1f} s for {n} layers -> {cpu['value']:.4f} tok/s")
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "decode_stack60_traffic.json")
+    if os.path.exists(tf):
+        try:
+            rec = json.load(open(tf))
+            from quantized_expert_mat_amd import build as qb
+            if rec.get("source_hash") == qb.source_hash() and rec.get("config") == w.name:
+                traffic = rec["bytes_per_launch"] * (T / rec.get("tokens", T))
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": "decode tok/s, 60-layer 4-bit MoE stack; effective HBM GB/s vs peak"
+                  if w.bits == 4 else "decode tok/s, 60-layer 2-bit MoE stack; effective HBM GB/s vs peak",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i4",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "tokens_per_step": T, "hidden": H, "inter": w.inter,
+                   "experts": w.n_experts, "top_k": K, "shared": w.n_shared, "bits": w.bits,
+                   "temporal_repeat_target": w.temporal_p, "temporal_repeat_realised": round(float(rep), 4),
+                   "bytes_per_token": ptb, "mode": "phased" if args.phased else "persistent"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "parity": par,
+        "effective_hbm_gbs": round(ptb * tok_s / 1e9, 1),
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+    del keep
+
+
+if __name__ == "__main__":
+    main()

@@ -33,3 +33,13 @@ def build(verbose=False):
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+
+
+def source_hash():
+    """Hash of the kernel sources: ties a stored counter measurement to the code it measured."""
+    import hashlib
+    h = hashlib.sha256()
+    for s in SOURCES + ["qmoe_internal.h"]:
+        with open(os.path.join(CSRC, s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]

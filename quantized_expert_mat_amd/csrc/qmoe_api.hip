@@ -8,27 +8,6 @@
 #include "qmoe_internal.h"
 
 namespace qmoe {
-hipError_t launch_pack(const Geo& geo, int n, const uint8_t* codes, const uint16_t* scales,
-                       const uint16_t* biases, void* packed, unsigned* err, hipStream_t stream);
-struct DecodeRequest {
-  int mode;
-  moe_config cfg;
-  int L, T;
-  const LayerPtrs* layers_dev;
-  const uint8_t* single_expert;
-  const float* x0;
-  float* y;
-  const uint8_t* boost_mask;
-  const float* sel_bias;
-  const int* boosted;
-  int* idx_out;
-  float* w_out;
-  float* logits_out;
-  uint8_t* ws;
-  WsLayout wl;
-  bool phased;
-};
-hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char** why);
 size_t prefill_ws_bytes(const moe_config& c, int T);
 moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int T,
                            const float* x, float* y, const float* sel_bias, const int32_t* boosted,

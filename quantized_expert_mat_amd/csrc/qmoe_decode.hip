@@ -70,6 +70,7 @@ struct DecodeArgs {
   unsigned* sync;                // [0] barrier counter, [1] abort flag
   unsigned* err;
   unsigned long long timeout_ticks;
+  unsigned long long* trace;     // optional [T][L][16] wall-clock stamps from workgroup 0
   int nwg;
   int rpw;                       // phase C output rows per workgroup
   int npass;
@@ -89,7 +90,11 @@ struct Small {
   float xs_x;
   float hsc[kMaxPass];
   float hxs[kMaxPass];
+  unsigned long long* tr;  // trace row (workgroup 0, thread 0 only)
 };
+
+#define SUBSTAMP(i) \
+  if (threadIdx.x == 0 && s.sm->tr) s.sm->tr[i] = wall_clock64();
 
 struct Lds {
   Small* sm;
@@ -481,7 +486,9 @@ __device__ void router_items(const DecodeArgs& a, const Lds& s, int t, int l) {
 template <int BITS>
 __device__ void phase_a(const DecodeArgs& a, const Lds& s, int t, int l) {
   prepare_x(a, s, t, l);
+  SUBSTAMP(8);
   router_items(a, s, t, l);
+  SUBSTAMP(9);
   if (a.mode == MODE_LAYER && a.S > 0) {
     const Geo& g = a.geo;
     const uint8_t* shared = a.layers[l].shared;
@@ -610,6 +617,7 @@ __device__ void phase_b(const DecodeArgs& a, const Lds& s, int t, int l) {
     return;
   }
   select_topk(a, s, t, l);
+  SUBSTAMP(10);
   if (a.mode != MODE_LAYER) return;
   const Geo& g = a.geo;
   const uint8_t* experts = a.layers[l].experts;
@@ -649,6 +657,7 @@ __device__ void phase_c(const DecodeArgs& a, const Lds& s, int t, int l) {
     encode_vectors(a.hbuf, (size_t)I, nlist, I, s.sm->hsc, s.hdig, s.hsum);
     __syncthreads();
   }
+  SUBSTAMP(11);
   const int rpw = a.rpw;
   const int r0 = blockIdx.x * rpw;
   const int r1 = min(H, r0 + rpw);
@@ -704,6 +713,7 @@ __device__ void phase_c(const DecodeArgs& a, const Lds& s, int t, int l) {
     }
   }
   __syncthreads();
+  SUBSTAMP(12);
   if (r0 < r1) {
     const bool res = !expert_mode && (a.flags & MOE_F_RESIDUAL);
     const float* xin = token_input(a, t, l);
@@ -729,18 +739,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int only
   const int t0 = persistent ? 0 : t_only, t1 = persistent ? a.T : t_only + 1;
   const int l0 = persistent ? 0 : l_only, l1 = persistent ? a.L : l_only + 1;
   unsigned bar = 0;
+  unsigned long long* tr = nullptr;
   for (int t = t0; t < t1; ++t) {
     for (int l = l0; l < l1; ++l) {
+      if (a.trace && blockIdx.x == 0 && threadIdx.x == 0) tr = a.trace + ((size_t)t * a.L + l) * 16;
+#define QMOE_STAMP(i) \
+  if (tr) tr[i] = wall_clock64();
+      if (threadIdx.x == 0) s.sm->tr = tr;
+      QMOE_STAMP(0);
       bool have_x = false;
       if (a.mode != MODE_EXPERT && (persistent || only_phase == 0)) {
         phase_a<BITS>(a, s, t, l);
         have_x = true;
+        QMOE_STAMP(1);
         if (persistent && !grid_sync(a, s.sm, ++bar)) return;
+        QMOE_STAMP(2);
       }
       if (persistent || only_phase == 1) {
         if (!have_x && a.mode != MODE_ROUTE) prepare_x(a, s, t, l);
         phase_b<BITS>(a, s, t, l);
+        QMOE_STAMP(3);
         if (persistent && !grid_sync(a, s.sm, ++bar)) return;
+        QMOE_STAMP(4);
       }
       if (a.mode != MODE_ROUTE && (persistent || only_phase == 2)) {
         if (!persistent && a.mode == MODE_LAYER) {
@@ -751,8 +771,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int only
           __syncthreads();
         }
         phase_c<BITS>(a, s, t, l);
+        QMOE_STAMP(5);
         if (persistent && !grid_sync(a, s.sm, ++bar)) return;
+        QMOE_STAMP(6);
       }
+#undef QMOE_STAMP
     }
   }
 }
@@ -764,6 +787,7 @@ __global__ void zero_words(unsigned* p, int n, unsigned* q, int m) {
 
 // ------------------------------------------------------------ host side
 static int g_num_cu = -1;
+unsigned long long* g_trace = nullptr;  // set only by instrumented builds
 static long long g_wall_khz = -1;
 
 static hipError_t device_info() {
@@ -780,25 +804,6 @@ static hipError_t device_info() {
   g_wall_khz = khz;
   return hipSuccess;
 }
-
-struct DecodeRequest {
-  int mode;
-  moe_config cfg;
-  int L, T;
-  const LayerPtrs* layers_dev;
-  const uint8_t* single_expert;
-  const float* x0;
-  float* y;
-  const uint8_t* boost_mask;
-  const float* sel_bias;
-  const int* boosted;
-  int* idx_out;
-  float* w_out;
-  float* logits_out;
-  uint8_t* ws;
-  WsLayout wl;
-  bool phased;
-};
 
 hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char** why) {
   hipError_t e = device_info();
@@ -834,6 +839,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.sync = reinterpret_cast<unsigned*>(ws + r.wl.sync);
   a.err = reinterpret_cast<unsigned*>(ws + r.wl.err);
   a.timeout_ticks = (unsigned long long)g_wall_khz * 2000ull;  // 2 seconds per barrier wait
+  a.trace = g_trace;
 
   // Expert passes for phase C: routed experts in power-of-two groups that fit a
   // wave (lanes = rows x experts x groups), then the shared experts.

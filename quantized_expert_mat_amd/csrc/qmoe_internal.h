@@ -106,6 +106,30 @@ inline WsLayout ws_layout(const moe_config& c, int T, int L) {
   return w;
 }
 
+// One decode-engine call (route, expert forward, layer forward or stack decode).
+struct DecodeRequest {
+  int mode;  // 0 layer/stack, 1 route only, 2 single expert
+  moe_config cfg;
+  int L, T;
+  const LayerPtrs* layers_dev;
+  const uint8_t* single_expert;
+  const float* x0;
+  float* y;
+  const uint8_t* boost_mask;
+  const float* sel_bias;
+  const int* boosted;
+  int* idx_out;
+  float* w_out;
+  float* logits_out;
+  uint8_t* ws;
+  WsLayout wl;
+  bool phased;
+};
+
+hipError_t launch_pack(const Geo& geo, int n, const uint8_t* codes, const uint16_t* scales,
+                       const uint16_t* biases, void* packed, unsigned* err, hipStream_t stream);
+hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char** why);
+
 // Device error codes (written to the workspace error word; first error wins).
 enum DevErr : unsigned {
   DEV_OK = 0,
