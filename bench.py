@@ -36,35 +36,37 @@ def per_token_bytes(w):
     return w.n_layers * ((w.top_k + w.n_shared) * eb + 4 * w.n_experts * w.hidden)
 
 
-def cpu_baseline_and_parity(w, dls, hls, x0_host, n_layers, stack_fn):
-    """Time the oracle on token 0 through the first n_layers layers (weights
-    regenerated beforehand, outside the timing) and compare the GPU's output of
-    the same layers."""
+def cpu_baseline_and_parity(w, x0_host, y_gpu, idx_gpu, n_tokens):
+    """Replay tokens 0..n_tokens-1 through every layer with the CPU oracle (the
+    weights it touches regenerated on the side; generation time excluded) and
+    compare with the GPU's outputs of the same tokens."""
     import numpy as np
     from oracle import ref
-    from tests.helpers import NEAR_TIE, parity, same_set
-    y_gpu, idx_gpu = stack_fn(n_layers)
-    # regenerate what the oracle will touch, following the GPU's sets (checked below)
-    for l in range(n_layers):
-        for e in list(idx_gpu[0, l]) + [w.n_experts + s for s in range(w.n_shared)]:
-            hls[l].expert(int(e))
+    from tests.helpers import NEAR_TIE, DeviceCanonicalLayer, parity, same_set
+    import workload as wl
+    hls = [DeviceCanonicalLayer(w, l) for l in range(w.n_layers)]
+    boost = wl.boost_mask(w.seed + 7, w.n_tokens, w.n_layers, w.top_k, w.temporal_p or 0.0)
     flagged = []
 
     def follow(t, l, oi, gap):
         if same_set(oi, idx_gpu[t, l]):
             return None
-        assert gap < NEAR_TIE, f"layer {l}: expert sets differ (gap {gap})"
-        flagged.append(l)
+        assert gap < NEAR_TIE, f"token {t} layer {l}: expert sets differ (gap {gap})"
+        flagged.append((t, l))
         return idx_gpu[t, l]
 
     t0 = time.perf_counter()
-    ys, sets, _ = ref.stack_decode(x0_host[:1], n_layers, lambda l: hls[l].router,
+    ys, sets, _ = ref.stack_decode(x0_host[:n_tokens], w.n_layers, lambda l: hls[l].router,
                                    lambda l, e: hls[l].expert(e), lambda l: hls[l].shared(), w.top_k,
-                                   follow=follow)
-    dt = time.perf_counter() - t0
-    rel_max, rel_l2 = parity(y_gpu[0], ys[0], "bench spot check")
-    return dt, {"layers": n_layers, "tokens": 1, "max_rel_err": float(rel_max), "rel_l2": float(rel_l2),
-                "expert_sets_equal": not flagged, "near_tie_follows": len(flagged)}
+                                   boost=boost[:n_tokens], follow=follow)
+    dt = time.perf_counter() - t0 - sum(h.gen_seconds for h in hls)
+    worst = (0.0, 0.0)
+    for t in range(n_tokens):
+        rm, rl = parity(y_gpu[t], ys[t], f"bench token {t}")
+        worst = (max(worst[0], rm), max(worst[1], rl))
+    return dt, {"layers": w.n_layers, "tokens": n_tokens, "max_rel_err": float(worst[0]),
+                "rel_l2": float(worst[1]), "expert_sets_equal": not flagged,
+                "near_tie_follows": len(flagged)}
 
 
 def main():
@@ -75,7 +77,7 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="2: 4-bit stack, 3: 2-bit stack")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--tokens", type=int, default=None)
-    ap.add_argument("--cpu-layers", type=int, default=6)
+    ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--phased", action="store_true")
     args = ap.parse_args()
@@ -89,7 +91,7 @@ def main():
     import quantized_expert_mat_amd as q
     import workload as wl
     from workload import device as wdev
-    from tests.helpers import DeviceLayer, HostLayer, config_for
+    from tests.helpers import DeviceLayer, config_for
 
     w = wl.CONFIGS[args.config]
     if args.layers or args.tokens:
@@ -154,22 +156,12 @@ def main():
     cpu = None
     par = None
     if not args.no_cpu:
-        hls = [HostLayer(w, l) for l in range(min(args.cpu_layers, L))]
-        x0h = x0.cpu().numpy()
-
-        def stack_fn(n):
-            ys = torch.empty((1, H), dtype=torch.float32, device=dev)
-            it = torch.empty((1, n, K), dtype=torch.int32, device=dev)
-            q.moe_stack_decode(cfg, layers[:n], 1, x0[:1], ys, ws, idx_trace=it)
-            q.moe_device_status(ws)
-            return ys.cpu().numpy(), it.cpu().numpy()
-
-        n = min(args.cpu_layers, L)
-        dt, par = cpu_baseline_and_parity(w, dls, hls, x0h, n, stack_fn)
-        cpu = {"value": round(1.0 / (dt / n * L), 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
-               "sample": f"token 0 through layers 0-{n - 1} of the {L}-layer stack "
-                         f"({dt:.1f} s single-threaded fp64 oracle), scaled to {L} layers"}
-        log(f"cpu oracle: {dt:.1f} s for {n} layers -> {cpu['value']:.4f} tok/s")
+        n = min(args.cpu_tokens, T)
+        dt, par = cpu_baseline_and_parity(w, x0.cpu().numpy(), y.cpu().numpy(), ih, n)
+        cpu = {"value": round(n / dt, 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
+               "sample": f"tokens 0-{n - 1} through all {L} layers (temporal tier replayed), "
+                         f"{dt:.1f} s of single-threaded fp64 oracle arithmetic"}
+        log(f"cpu oracle: {dt:.1f} s for {n} tokens x {L} layers -> {cpu['value']:.4f} tok/s")
 
     traffic = None
     tf = os.path.join(ROOT, "profiles", "decode_stack60_traffic.json")

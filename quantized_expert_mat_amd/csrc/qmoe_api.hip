@@ -312,7 +312,7 @@ moe_status moe_device_status(void* ws, size_t ws_bytes, void* stream) {
   if (e != hipSuccess) return hip_fail(e, "clearing the device error word");
   switch (v) {
     case DEV_BAD_INDEX: return fail(MOE_ERR_DEVICE, "device: expert index out of range");
-    case DEV_SYNC_TIMEOUT: return fail(MOE_ERR_DEVICE, "device: grid barrier timed out");
+    case DEV_SYNC_TIMEOUT: return fail(MOE_ERR_DEVICE, "device: a wait for another workgroup's data timed out");
     case DEV_BAD_CODE: return fail(MOE_ERR_DEVICE, "device: pack input code >= 2^bits");
     default: return fail(MOE_ERR_DEVICE, "device error %u", v);
   }

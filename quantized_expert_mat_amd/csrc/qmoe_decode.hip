@@ -17,6 +17,18 @@
 // command buffers remove a per-layer dispatch gap for the same reason,
 // "Optimizaciones Efectivas" section of the autoresearch page).
 //
+// Cross-workgroup traffic. The 256 workgroups sit on 8 XCDs with separate L2
+// caches, and a grid-wide barrier costs several microseconds there. So there is
+// no barrier: every value one phase hands to the next (x, logits, h) is written
+// as an 8-byte (value, epoch) pair with a device-coherent store, in 8 replicas,
+// and each consumer polls exactly the values it needs until they carry the
+// current epoch. A producer can only reach its next write of a slot after every
+// workgroup has consumed the current one (each phase needs all of the previous
+// phase's output), so a slot is never overwritten before it is read. While data
+// is in flight the workgroups stream weights into LDS with global_load_lds: once
+// top-K is known the down rows they will need, and during phase C the next
+// layer's router rows and shared-expert gate/up blocks.
+//
 // Dequant mat-vec. The page rewrites (nibble*scale + bias)*x as
 // fma(nibble, scale*x, bias*x) ("Kernel dequant tối ưu FMA"). Carried one step
 // further, a 64-group contributes scale*sum(q*x) + bias*sum(x); sum(x) per group
@@ -27,11 +39,6 @@
 // instruction with exact int32 accumulation. One weight element then costs about
 // one VALU operation instead of two and a half for convert + FMA, which keeps the
 // 4-bit path under the HBM roofline instead of next to it.
-//
-// Work split. A block of the packed layout is one wave's worth: lane = (row,
-// group). Gate/up items are (expert, block); down items are rows owned by a
-// workgroup, with lanes spread over (row, expert, group) so a lane's activation
-// digits stay in registers for every row it visits.
 #include <algorithm>
 #include <cstring>
 
@@ -43,7 +50,8 @@ constexpr int kThreads = 256;
 constexpr int kNW = kThreads / kWave;  // waves per workgroup
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an integer in the low mantissa
 constexpr int kMaxPass = kMaxK + kMaxShared;
-constexpr int kBatch = 4;  // items whose loads are issued before the first is reduced
+constexpr int kBatch = 4;              // items whose loads are issued before the first is reduced
+constexpr int kMaxLdsBytes = 160 * 1024;
 
 enum Mode { MODE_LAYER = 0, MODE_ROUTE = 1, MODE_EXPERT = 2 };
 
@@ -62,30 +70,34 @@ struct DecodeArgs {
   int* idx_out;                  // [T][L][K]
   float* w_out;                  // [T][L][K]
   float* logits_out;             // [T][E]
-  float* xbuf;                   // [2][H]
-  float* logits;                 // [E]
-  float* hbuf;                   // [K+S][I]
+  unsigned long long* xx;        // [kRep][H] (value, epoch) pairs: next layer's input
+  unsigned long long* lx;        // [kRep][E_pad] router logits
+  unsigned long long* hx;        // [kRep][(K+S)*I] expert intermediates
+  int e_pad;                     // E rounded up to even
   int* sel;                      // [2*kMaxK]
   int* prev;                     // [2][L][kMaxK]
-  unsigned* sync;                // [0] barrier counter, [1] abort flag
+  unsigned* sync;                // [0] abort flag
   unsigned* err;
   unsigned long long timeout_ticks;
   unsigned long long* trace;     // optional [T][L][16] wall-clock stamps from workgroup 0
+  unsigned long long* trace_wg;  // optional [L][nwg][4] stamps of every workgroup at token 2
   int nwg;
   int rpw;                       // phase C output rows per workgroup
   int npass;
   int pass_first[kMaxPass], pass_count[kMaxPass];
-  int lds_xn, lds_xdig, lds_xsum, lds_hdig, lds_hsum, lds_acc, lds_words;
+  int pf;                        // 1: router / shared weights are prefetched into LDS tiles
+  int pf_down;                   // 1: down blocks are prefetched into LDS
+  int nbd;                       // down blocks per list entry in the down tile
+  int lds_xn, lds_xdig, lds_xsum, lds_hdig, lds_hsum, lds_acc, lds_xres, lds_tile_a, lds_tile_sh,
+      lds_tile_c;
+  int lds_words;
 };
 
 // Small per-workgroup state kept in LDS across phases.
 struct Small {
-  unsigned long long red64[kNW];
   float redf[kNW][kMaxPass + 2];
   int sel_idx[kMaxK];
   float sel_w[kMaxK];
-  int boosted[kMaxK];
-  int nboost;
   int ok;
   float xs_x;
   float hsc[kMaxPass];
@@ -104,6 +116,11 @@ struct Lds {
   unsigned* hdig;
   float* hsum;
   float* acc;
+  float* xres;       // this workgroup's rows of the (pre-norm) layer input
+  float* hstage;     // phase C: h vectors (aliases xn and xdig, dead by then)
+  uint8_t* tile_a;   // router rows of this workgroup
+  uint8_t* tile_sh;  // shared-expert gate/up items of this workgroup
+  uint8_t* tile_c;   // down blocks of this workgroup, per expert list entry
 };
 
 __device__ inline Lds lds_view(unsigned* raw, const DecodeArgs& a) {
@@ -115,28 +132,171 @@ __device__ inline Lds lds_view(unsigned* raw, const DecodeArgs& a) {
   s.hdig = raw + a.lds_hdig;
   s.hsum = reinterpret_cast<float*>(raw + a.lds_hsum);
   s.acc = reinterpret_cast<float*>(raw + a.lds_acc);
+  s.xres = reinterpret_cast<float*>(raw + a.lds_xres);
+  s.hstage = reinterpret_cast<float*>(raw + a.lds_xn);
+  s.tile_a = reinterpret_cast<uint8_t*>(raw + a.lds_tile_a);
+  s.tile_sh = reinterpret_cast<uint8_t*>(raw + a.lds_tile_sh);
+  s.tile_c = reinterpret_cast<uint8_t*>(raw + a.lds_tile_c);
   return s;
 }
 
-// ---------------------------------------------------------------- reductions
-__device__ inline float seg_sum(float v, int width) {
-  for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ inline void split_range(int n, int parts, int p, int& b, int& e) {
+  b = (int)((long long)n * p / parts);
+  e = (int)((long long)n * (p + 1) / parts);
 }
-__device__ inline float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+
+// ------------------------------------------------------------ coherent accesses
+__device__ inline void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ inline void st_coh(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
-  for (int o = 32; o >= 1; o >>= 1) {
-    unsigned long long w = __shfl_xor(v, o);
-    v = w > v ? w : v;
+__device__ inline float ld_coh(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int ld_coh(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's outstanding memory operations (stores included) are done.
+__device__ inline void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+constexpr int kCachePolicySC1 = 16;           // device-coherent (bypasses non-coherent caches)
+constexpr int kBufferRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+// 16-byte device-coherent loads through a buffer resource of `bytes` bytes; reads
+// past the end return zeros (the hardware range check), so callers may over-read.
+__device__ inline __amdgpu_buffer_rsrc_t coh_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferRsrcWord3);
+}
+__device__ inline v4u ld_coh4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCachePolicySC1);
+}
+
+// ------------------------------------------------------------ epoch-tagged exchange
+// An exchanged vector of n values is kRep replicas of n (value, epoch) pairs; a
+// replica holds n_pad = n rounded up to even pairs so it splits into 16-byte chunks.
+struct Xv {
+  unsigned long long* base;
+  int n, n_pad;
+};
+
+__device__ inline void xput(const Xv& x, int i, float v, unsigned epoch) {
+  const unsigned long long pv = ((unsigned long long)epoch << 32) | __float_as_uint(v);
+#pragma unroll
+  for (int r = 0; r < kRep; ++r)
+    __hip_atomic_store(x.base + (size_t)r * x.n_pad + i, pv, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool poll_abort(const DecodeArgs& a, unsigned long long t0, int lane0);
+
+// Wait until every pair of this workgroup's replica carries `epoch` and copy the
+// values into LDS (dst[i]). All threads take part; each polls its own chunks.
+// Returns false if the kernel is aborting.
+__device__ __forceinline__ bool xget(const DecodeArgs& a, const Xv& x, float* dst, unsigned epoch) {
+  constexpr int kPer = 8;
+  const unsigned long long* src = x.base + (size_t)(blockIdx.x % kRep) * x.n_pad;
+  const __amdgpu_buffer_rsrc_t r = coh_rsrc(src, x.n_pad * 8);
+  const int nch = (x.n + 1) / 2;  // only the n produced values are awaited
+  bool ok = true;
+  for (int base = 0; base < nch; base += kThreads * kPer) {
+    v4u v[kPer];
+    unsigned pending = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) v[k] = ld_coh4(r, (base + (int)threadIdx.x + k * kThreads) * 16);
+    const unsigned long long t0 = wall_clock64();
+    for (unsigned it = 0;; ++it) {
+      pending = 0;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int c = base + (int)threadIdx.x + k * kThreads;
+        if (c >= nch) continue;
+        const bool ok0 = v[k].y == epoch, ok1 = v[k].w == epoch || 2 * c + 1 >= x.n;
+        if (ok0 && ok1) {
+          dst[2 * c] = __uint_as_float(v[k].x);
+          if (2 * c + 1 < x.n) dst[2 * c + 1] = __uint_as_float(v[k].z);
+        } else {
+          pending |= 1u << k;
+        }
+      }
+      if (!pending) break;
+      if ((it & 31u) == 31u && !poll_abort(a, t0, 1)) {
+        ok = false;
+        break;
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        if (pending & (1u << k)) v[k] = ld_coh4(r, (base + (int)threadIdx.x + k * kThreads) * 16);
+    }
+    if (!ok) break;
   }
+  return ok;
+}
+
+// ---------------------------------------------------------------- reductions (DPP)
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+constexpr int kQuad1032 = 0xB1, kQuad2301 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+
+// Sum over aligned segments of `width` lanes (power of two); every lane of a
+// segment receives the segment's total.
+__device__ inline float seg_sum(float v, int width) {
+  if (width >= 2) v += dpp_f<kQuad1032>(v);
+  if (width >= 4) v += dpp_f<kQuad2301>(v);
+  if (width >= 8) v += dpp_f<kRowHalfMirror>(v);
+  if (width >= 16) v += dpp_f<kRowMirror>(v);
+  if (width >= 32) v += __shfl_xor(v, 16);
+  if (width >= 64) v += __shfl_xor(v, 32);
   return v;
+}
+__device__ inline int seg_sum8_i(int v) {
+  v += dpp_i<kQuad1032>(v);
+  v += dpp_i<kQuad2301>(v);
+  v += dpp_i<kRowHalfMirror>(v);
+  return v;
+}
+__device__ inline float seg_max(float v, int width) {
+  if (width >= 2) v = fmaxf(v, dpp_f<kQuad1032>(v));
+  if (width >= 4) v = fmaxf(v, dpp_f<kQuad2301>(v));
+  if (width >= 8) v = fmaxf(v, dpp_f<kRowHalfMirror>(v));
+  if (width >= 16) v = fmaxf(v, dpp_f<kRowMirror>(v));
+  if (width >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if (width >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ inline float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Whole-wave sum, returned uniform (one lane of each 16-lane row read out).
+__device__ inline float wave_sum(float v) {
+  v = seg_sum(v, 16);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ inline float wave_max(float v) { return seg_max(v, 64); }
+
+template <int CTRL>
+__device__ inline unsigned long long dpp_max_step(unsigned long long k) {
+  const unsigned hi = (unsigned)dpp_i<CTRL>((int)(k >> 32)), lo = (unsigned)dpp_i<CTRL>((int)k);
+  const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+  return o > k ? o : k;
+}
+__device__ inline unsigned long long wave_max_u64(unsigned long long k) {
+  k = dpp_max_step<kQuad1032>(k);
+  k = dpp_max_step<kQuad2301>(k);
+  k = dpp_max_step<kRowHalfMirror>(k);
+  k = dpp_max_step<kRowMirror>(k);
+  unsigned long long o = __shfl_xor(k, 16);
+  k = o > k ? o : k;
+  o = __shfl_xor(k, 32);
+  return o > k ? o : k;
 }
 
 // Power-of-two scale that maps |v| <= m into (-2^22, 2^22).
@@ -195,17 +355,17 @@ __device__ inline int encode_chunk(const float v[8], float sc, unsigned out[6]) 
   return isum;
 }
 
-// Encode nvec vectors of length n (multiple of 64), vector j at src + j*stride,
-// with per-vector scales sc[j]. Digits for (vector j, group g) go to
+// Encode nvec vectors of length n (multiple of 64) held in LDS at src + j*n, with
+// per-vector scales sc[j]. Digits for (vector j, group g) go to
 // dig[(j*G + g)*kDigitStride + dw*6 + d]; sums to sum[2*(j*G+g)] = 8*sum(ints),
 // sum[2*(j*G+g)+1] = float sum of the values. Whole workgroup participates.
-__device__ void encode_vectors(const float* src, size_t stride, int nvec, int n, const float* sc,
-                               unsigned* dig, float* sum) {
+__device__ __forceinline__ void encode_vectors(const float* src, int nvec, int n, const float* sc, unsigned* dig,
+                               float* sum) {
   const int G = n / kGroup;
   const int chunks_per_vec = n / 8;
   const int total = nvec * chunks_per_vec;
-  // total is a multiple of 8 and kThreads is a multiple of 64: the 8 chunks of a
-  // group always sit in 8 consecutive lanes of one wave.
+  // total is a multiple of 8 and kThreads a multiple of 64: the 8 chunks of a group
+  // always sit in 8 consecutive lanes (one DPP half-row) of one wave.
   for (int base = 0; base < total; base += kThreads) {
     const int c = base + (int)threadIdx.x;
     int isum = 0;
@@ -215,7 +375,7 @@ __device__ void encode_vectors(const float* src, size_t stride, int nvec, int n,
     if (active) {
       j = c / chunks_per_vec;
       cc = c % chunks_per_vec;
-      const float4* p = reinterpret_cast<const float4*>(src + (size_t)j * stride + (size_t)cc * 8);
+      const float4* p = reinterpret_cast<const float4*>(src + (size_t)j * n + (size_t)cc * 8);
       const float4 v0 = p[0], v1 = p[1];
       const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       unsigned o[6];
@@ -223,14 +383,13 @@ __device__ void encode_vectors(const float* src, size_t stride, int nvec, int n,
 #pragma unroll
       for (int i = 0; i < 8; ++i) fsum += v[i];
       const int g = cc / 8, dw = cc % 8;
-      unsigned* dst = dig + (size_t)(j * G + g) * kDigitStride + dw * 6;
-#pragma unroll
-      for (int d = 0; d < 6; ++d) dst[d] = o[d];
+      uint2* dst = reinterpret_cast<uint2*>(dig + (size_t)(j * G + g) * kDigitStride + dw * 6);
+      dst[0] = make_uint2(o[0], o[1]);
+      dst[1] = make_uint2(o[2], o[3]);
+      dst[2] = make_uint2(o[4], o[5]);
     }
-    for (int o = 1; o < 8; o <<= 1) {
-      isum += __shfl_xor(isum, o);
-      fsum += __shfl_xor(fsum, o);
-    }
+    isum = seg_sum8_i(isum);  // |sum of 64 ints| <= 2^28: exact in int32
+    fsum = seg_sum(fsum, 8);
     if (active && (cc % 8) == 0) {
       const int g = cc / 8;
       sum[2 * (j * G + g)] = 8.f * (float)isum;
@@ -265,9 +424,30 @@ struct Slot {
   unsigned sb;
 };
 
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+
+typedef __attribute__((address_space(3))) const v4u lds_v4u;
+typedef __attribute__((address_space(3))) const unsigned lds_u32;
+
+__device__ inline uint4 to_uint4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+// blk points to global memory, or (in_lds) to an LDS copy of the block.
 template <int BITS>
-__device__ inline Slot ld_slot(const uint8_t* blk, int slot) {
+__device__ inline Slot ld_slot(const uint8_t* blk, int slot, bool in_lds) {
   Slot s;
+  if (in_lds) {
+    const unsigned off = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)blk;
+    lds_v4u* c = (lds_v4u*)(uintptr_t)off;
+    s.c0 = to_uint4(c[slot]);
+    if (BITS == 4) {
+      s.c1 = to_uint4(c[64 + slot]);
+      s.sb = ((lds_u32*)(uintptr_t)(off + 2048))[slot];
+    } else {
+      s.c1 = make_uint4(0, 0, 0, 0);
+      s.sb = ((lds_u32*)(uintptr_t)(off + 1024))[slot];
+    }
+    return s;
+  }
   s.c0 = reinterpret_cast<const uint4*>(blk)[slot];
   if (BITS == 4) {
     s.c1 = reinterpret_cast<const uint4*>(blk + 1024)[slot];
@@ -315,58 +495,79 @@ __device__ inline float slot_dot(const Slot& s, const Dig& D) {
 
 __device__ inline float silu(float z) { return z / (1.f + expf(-z)); }
 
-// ------------------------------------------------------------ grid barrier
-__device__ bool grid_sync(const DecodeArgs& a, Small* sm, unsigned index) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned target = index * (unsigned)a.nwg;
-    const unsigned long long t0 = wall_clock64();
-    unsigned spins = 0;
-    while (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if ((++spins & 255u) == 0) {
-        if (__hip_atomic_load(a.sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-          ok = 0;
-          break;
-        }
-        if (wall_clock64() - t0 > a.timeout_ticks) {
-          __hip_atomic_store(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          set_dev_err(a.err, DEV_SYNC_TIMEOUT);
-          ok = 0;
-          break;
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    sm->ok = ok;
+// ------------------------------------------------------------ LDS prefetch
+// Copy `bytes` (multiple of 16) from global memory into LDS with the direct
+// global->LDS path, 1 KB per wave instruction, using waves [w0, kNW).
+__device__ inline void dma_to_lds(uint8_t* lds, const uint8_t* g, int bytes, int w0) {
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (w < w0) return;
+  for (int c = (w - w0) * 1024; c < bytes; c += (kNW - w0) * 1024) {
+    if (c + lane * 16 < bytes)
+      __builtin_amdgcn_global_load_lds(g + c + lane * 16,
+                                       (__attribute__((address_space(3))) void*)(lds + c), 16, 0, 0);
   }
+}
+
+// ------------------------------------------------------------ abort / time-out
+// Every wait is bounded: after timeout_ticks a waiter raises the abort flag and the
+// device error, and every waiter that sees the flag gives up, so all workgroups
+// leave the kernel.
+__device__ __forceinline__ bool poll_abort(const DecodeArgs& a, unsigned long long t0, int) {
+  if (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
+  if (wall_clock64() - t0 > a.timeout_ticks) {
+    __hip_atomic_store(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    set_dev_err(a.err, DEV_SYNC_TIMEOUT);
+    return false;
+  }
+  return true;
+}
+
+// Workgroup-wide "all waits succeeded".
+__device__ inline bool wg_all(Small* sm, bool ok) {
+  if (threadIdx.x == 0) sm->ok = 1;
+  __syncthreads();
+  if (!ok) sm->ok = 0;
   __syncthreads();
   return sm->ok != 0;
 }
 
 // ------------------------------------------------------------ phase pieces
-__device__ inline const float* token_input(const DecodeArgs& a, int t, int l) {
-  return l == 0 ? a.x0 + (size_t)t * a.geo.H : a.xbuf + (size_t)(l & 1) * a.geo.H;
+__device__ inline unsigned epoch_of(const DecodeArgs& a, int t, int l) {
+  return (unsigned)(t * a.L + l + 1);
+}
+__device__ inline Xv xv_x(const DecodeArgs& a) { return Xv{a.xx, a.geo.H, a.geo.H}; }
+__device__ inline Xv xv_logits(const DecodeArgs& a) { return Xv{a.lx, a.E, a.e_pad}; }
+__device__ inline Xv xv_h(const DecodeArgs& a) {
+  const int n = (kMaxK + kMaxShared) * a.geo.I;
+  return Xv{a.hx, n, n};
 }
 
-// x -> LDS (normalised if requested) -> digits for the gate/up mat-vecs.
-__device__ void prepare_x(const DecodeArgs& a, const Lds& s, int t, int l) {
+// x -> LDS (normalised if requested) -> digits for the gate/up mat-vecs. The raw
+// rows this workgroup combines in phase C are kept for the residual.
+__device__ __forceinline__ bool prepare_x(const DecodeArgs& a, const Lds& s, int t, int l) {
   const int H = a.geo.H;
-  const float* x = token_input(a, t, l);
   const float* gamma = a.mode == MODE_EXPERT ? nullptr : a.layers[l].gamma;
   const bool norm = a.mode != MODE_EXPERT && (a.flags & MOE_F_RMSNORM);
+  bool ok = true;
+  if (a.mode == MODE_LAYER && l > 0) {
+    ok = xget(a, xv_x(a), s.xn, epoch_of(a, t, l));
+  } else {
+    const float* x = a.x0 + (size_t)t * H;
+    for (int i = threadIdx.x * 4; i < H; i += kThreads * 4)
+      *reinterpret_cast<float4*>(s.xn + i) = *reinterpret_cast<const float4*>(x + i);
+  }
+  if (!wg_all(s.sm, ok)) return false;
+  const int r0 = blockIdx.x * a.rpw;
+  if ((int)threadIdx.x < a.rpw && r0 + (int)threadIdx.x < H) s.xres[threadIdx.x] = s.xn[r0 + threadIdx.x];
   float ss = 0.f, mx = 0.f;
   for (int i = threadIdx.x * 4; i < H; i += kThreads * 4) {
-    float4 v = *reinterpret_cast<const float4*>(x + i);
+    float4 v = *reinterpret_cast<float4*>(s.xn + i);
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     if (gamma) {
       const float4 gm = *reinterpret_cast<const float4*>(gamma + i);
       v.x *= gm.x; v.y *= gm.y; v.z *= gm.z; v.w *= gm.w;
+      *reinterpret_cast<float4*>(s.xn + i) = v;
     }
-    *reinterpret_cast<float4*>(s.xn + i) = v;
     mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   }
   ss = wave_sum(ss);
@@ -394,63 +595,70 @@ __device__ void prepare_x(const DecodeArgs& a, const Lds& s, int t, int l) {
   float sc, xs;
   digit_scale(mx * rinv, &sc, &xs);
   __syncthreads();
-  encode_vectors(s.xn, 0, 1, H, &sc, s.xdig, s.xsum);
+  encode_vectors(s.xn, 1, H, &sc, s.xdig, s.xsum);
   if (threadIdx.x == 0) s.sm->xs_x = xs;
   __syncthreads();
+  return true;
 }
 
-// Gate/up + SwiGLU over n_items (expert, block) items. Item k runs on global
-// wave (rot + k) mod (nwg * kNW), where global wave = blockIdx.x + nwg * wave, so
-// consecutive items land on different compute units. item(k, base, hout, blk)
-// names the expert, the block and the h vector of item k.
-template <int BITS, typename ItemFn>
-__device__ void gateup_items(const DecodeArgs& a, const Lds& s, int n_items, int rot,
-                             ItemFn item) {
+// Gate/up + SwiGLU over this workgroup's items [i0, i1); item i runs on wave
+// (i - i0) % kNW. src(i, gate, up, hidx, row0) names the gate and up blocks (global
+// or LDS) and the index of the item's h vector in the exchange. after_issue() runs
+// once, right after the first batch of loads is issued (or at once if the wave has
+// no items).
+template <int BITS, typename ItemFn, typename Hook>
+__device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, int i0, int i1, bool in_lds,
+                             unsigned epoch, ItemFn src, Hook after_issue) {
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const int waves = a.nwg * kNW;
-  const int gw = blockIdx.x + a.nwg * w;
-  const int k0 = (gw - rot % waves + waves) % waves;
-  if (k0 >= n_items) return;
+  if (i0 + w >= i1) {
+    after_issue();
+    return;
+  }
+  const Xv hxv = xv_h(a);
   const int p = lane / g.Gh, grp = lane % g.Gh;
   Dig D;
   load_dig(D, s.xdig, s.xsum, grp, s.sm->xs_x);
-  for (int i0 = k0; i0 < n_items; i0 += kBatch * waves) {
+  bool first = true;
+  for (int ib = i0 + w; ib < i1; ib += kBatch * kNW) {
     Slot G[kBatch], U[kBatch];
-    float* hout[kBatch];
-    int row[kBatch];
+    int hv[kBatch], row[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int i = i0 + j * waves;
-      hout[j] = nullptr;
+      const int i = ib + j * kNW;
+      hv[j] = -1;
       row[j] = 0;
-      if (i < n_items) {
-        const uint8_t* base;
-        int blk;
-        item(i, base, hout[j], blk);
-        G[j] = ld_slot<BITS>(base + (size_t)blk * g.blk, lane);
-        U[j] = ld_slot<BITS>(base + g.off_up + (size_t)blk * g.blk, lane);
-        row[j] = blk * g.Ph + p;
+      if (i < i1) {
+        const uint8_t *gb, *ub;
+        int row0;
+        src(i, gb, ub, hv[j], row0);
+        G[j] = ld_slot<BITS>(gb, lane, in_lds);
+        U[j] = ld_slot<BITS>(ub, lane, in_lds);
+        row[j] = row0 + p;
       }
+    }
+    if (first) {
+      after_issue();
+      first = false;
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      if (hout[j] == nullptr) continue;
+      if (hv[j] < 0) continue;
       const float pg = seg_sum(slot_dot<BITS>(G[j], D), g.Gh);
       const float pu = seg_sum(slot_dot<BITS>(U[j], D), g.Gh);
-      if (grp == 0 && row[j] < g.I) hout[j][row[j]] = silu(pg) * pu;
+      if (grp == 0 && row[j] < g.I) xput(hxv, hv[j] * g.I + row[j], silu(pg) * pu, epoch);
     }
   }
 }
 
-// Router logits for rows assigned to this wave (items 0..E-1 of phase A).
-__device__ void router_items(const DecodeArgs& a, const Lds& s, int t, int l) {
+// Router logits for rows [e0, e1) of this workgroup; row e - e0 on wave (e - e0) % kNW.
+__device__ __forceinline__ void router_rows(const DecodeArgs& a, const Lds& s, int t, int l, int e0, int e1,
+                            bool from_tile) {
   const int H = a.geo.H, E = a.E;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const int stride = a.nwg * kNW;
-  const int my0 = blockIdx.x + a.nwg * w;
-  if (my0 >= E) return;
-  const float* W = a.layers[l].router;
+  if (e0 + w >= e1) return;
+  const float* W =
+      from_tile ? reinterpret_cast<const float*>(s.tile_a) : a.layers[l].router + (size_t)e0 * H;
   const int nq = H / 4;  // float4 columns
   constexpr int kMaxC = kMaxDim / 256;
   float4 xr[kMaxC];
@@ -459,8 +667,8 @@ __device__ void router_items(const DecodeArgs& a, const Lds& s, int t, int l) {
     const int q = lane + kWave * c;
     xr[c] = q < nq ? reinterpret_cast<const float4*>(s.xn)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int e = my0; e < E; e += stride) {
-    const float4* row = reinterpret_cast<const float4*>(W + (size_t)e * H);
+  for (int e = e0 + w; e < e1; e += kNW) {
+    const float4* row = reinterpret_cast<const float4*>(W + (size_t)(e - e0) * H);
     float4 wv[kMaxC];
 #pragma unroll
     for (int c = 0; c < kMaxC; ++c) {
@@ -476,31 +684,63 @@ __device__ void router_items(const DecodeArgs& a, const Lds& s, int t, int l) {
       acc = fmaf(wv[c].w, xr[c].w, acc);
     }
     acc = wave_sum(acc);
-    if (lane == 0) {
-      a.logits[e] = acc;
-      if (a.logits_out) a.logits_out[(size_t)t * E + e] = acc;
+    if (lane < kRep) {
+      const unsigned long long pv = ((unsigned long long)epoch_of(a, t, l) << 32) | __float_as_uint(acc);
+      __hip_atomic_store(a.lx + (size_t)lane * a.e_pad + e, pv, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane == 0 && a.logits_out) a.logits_out[(size_t)t * E + e] = acc;
+  }
+}
+
+// Prefetch (into LDS) the router rows and shared gate/up items that phase A of
+// layer l will use, on waves [w0, kNW).
+__device__ __forceinline__ void prefetch_a(const DecodeArgs& a, const Lds& s, int l, int w0) {
+  const Geo& g = a.geo;
+  int e0, e1;
+  split_range(a.E, a.nwg, blockIdx.x, e0, e1);
+  dma_to_lds(s.tile_a, reinterpret_cast<const uint8_t*>(a.layers[l].router + (size_t)e0 * g.H),
+             (e1 - e0) * g.H * 4, w0);
+  if (a.S > 0) {
+    int i0, i1;
+    split_range(a.S * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
+    for (int i = i0; i < i1; ++i) {
+      const uint8_t* ex = a.layers[l].shared + (size_t)(i / g.nblk_gu) * g.expert_bytes +
+                          (size_t)(i % g.nblk_gu) * g.blk;
+      dma_to_lds(s.tile_sh + (size_t)(i - i0) * 2 * g.blk, ex, g.blk, w0);
+      dma_to_lds(s.tile_sh + (size_t)((i - i0) * 2 + 1) * g.blk, ex + g.off_up, g.blk, w0);
     }
   }
 }
 
 template <int BITS>
-__device__ void phase_a(const DecodeArgs& a, const Lds& s, int t, int l) {
-  prepare_x(a, s, t, l);
+__device__ __forceinline__ bool phase_a(const DecodeArgs& a, const Lds& s, int t, int l, bool tiles) {
+  const Geo& g = a.geo;
+  if (!prepare_x(a, s, t, l)) return false;
   SUBSTAMP(8);
-  router_items(a, s, t, l);
+  int e0, e1;
+  split_range(a.E, a.nwg, blockIdx.x, e0, e1);
+  router_rows(a, s, t, l, e0, e1, tiles);
   SUBSTAMP(9);
   if (a.mode == MODE_LAYER && a.S > 0) {
-    const Geo& g = a.geo;
+    int i0, i1;
+    split_range(a.S * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
     const uint8_t* shared = a.layers[l].shared;
-    // shared items continue the round-robin on the waves after the router rows
-    auto fn = [&](int i, const uint8_t*& base, float*& hout, int& blk) {
-      const int sh = i / g.nblk_gu;
-      blk = i % g.nblk_gu;
-      base = shared + (size_t)sh * g.expert_bytes;
-      hout = a.hbuf + (size_t)(a.K + sh) * g.I;
+    auto src = [&](int i, const uint8_t*& gb, const uint8_t*& ub, int& hvec, int& row0) {
+      const int sh = i / g.nblk_gu, b = i % g.nblk_gu;
+      if (tiles) {
+        gb = s.tile_sh + (size_t)(i - i0) * 2 * g.blk;
+        ub = gb + g.blk;
+      } else {
+        gb = shared + (size_t)sh * g.expert_bytes + (size_t)b * g.blk;
+        ub = gb + g.off_up;
+      }
+      hvec = a.K + sh;
+      row0 = b * g.Ph;
     };
-    gateup_items<BITS>(a, s, a.S * g.nblk_gu, a.E, fn);
+    gateup_items<BITS>(a, s, i0, i1, tiles, epoch_of(a, t, l), src, [] {});
   }
+  return true;
 }
 
 __device__ inline unsigned ord_f32(float f) {
@@ -508,140 +748,257 @@ __device__ inline unsigned ord_f32(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Top-K with the temporal tier, then softmax over the selected logits.
-__device__ void select_topk(const DecodeArgs& a, const Lds& s, int t, int l) {
-  const int E = a.E, K = a.K;
-  if (threadIdx.x == 0) {
-    int nb = 0;
-    if (a.mode == MODE_LAYER && a.boost_mask && t > 0) {
-      const uint8_t* m = a.boost_mask + ((size_t)t * a.L + l) * K;
-      const int* ps = a.prev + ((size_t)((t - 1) & 1) * a.L + l) * kMaxK;
-      for (int j = 0; j < K; ++j)
-        if (m[j]) s.sm->boosted[nb++] = ps[j];
-    } else if (a.boosted) {
-      const int* b = a.boosted + (size_t)t * K;
-      for (int j = 0; j < K; ++j) {
+// Top-K with the temporal tier, then softmax over the selected logits. Runs on
+// wave 0; the result is left in LDS (sel_idx, sel_w).
+__device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, int t, int l) {
+  if (threadIdx.x >= kWave) return;
+  const int E = a.E, K = a.K, lane = threadIdx.x;
+  // boosted experts (at most K), kept in fixed registers
+  int bst[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) bst[j] = -1;
+  if (a.mode == MODE_LAYER && a.boost_mask && t > 0) {
+    const uint8_t* m = a.boost_mask + ((size_t)t * a.L + l) * K;
+    const int* ps = a.prev + ((size_t)((t - 1) & 1) * a.L + l) * kMaxK;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < K && m[j]) bst[j] = ld_coh(ps + j);
+  } else if (a.boosted) {
+    const int* b = a.boosted + (size_t)t * K;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < K) {
         const int e = b[j];
-        if (e >= 0 && e < E) s.sm->boosted[nb++] = e;
-        else if (e >= E || e < -1) set_dev_err(a.err, DEV_BAD_INDEX);
+        if (e >= 0 && e < E) bst[j] = e;
+        else if ((e >= E || e < -1) && lane == 0) set_dev_err(a.err, DEV_BAD_INDEX);
       }
     }
-    s.sm->nboost = nb;
   }
-  __syncthreads();
-  const int nb = s.sm->nboost;
   const bool by_bias = (a.flags & MOE_F_SELECT_BY_BIAS) != 0;
   const float* sb = a.sel_bias ? a.sel_bias + (size_t)t * E : nullptr;
-  constexpr int kPer = kMaxE / kThreads;
+  constexpr int kCh = kMaxE / (4 * kWave);  // groups of 4 logits per lane
+  constexpr int kPer = 4 * kCh;
   unsigned long long key[kPer];
+  float lgv[kPer];
+  {
+    // poll this workgroup's replica of the logits until they carry this epoch
+    const unsigned epoch = epoch_of(a, t, l);
+    const unsigned long long* src = a.lx + (size_t)(blockIdx.x % kRep) * a.e_pad;
+    const __amdgpu_buffer_rsrc_t r = coh_rsrc(src, a.e_pad * 8);
+    v4u raw[2 * kCh];  // chunk c covers experts 4*(lane + 64c) .. +3 as two 16-byte halves
+    const unsigned long long t0 = wall_clock64();
+    for (unsigned it = 0;; ++it) {
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int e = threadIdx.x + kThreads * r;
-    key[r] = 0;
-    if (e < E) {
-      const float lg = a.logits[e];
-      const float sc = by_bias ? (sb ? sb[e] : 0.f) : lg + (sb ? sb[e] : 0.f);
-      unsigned tier = 0;
-      for (int j = 0; j < nb; ++j) tier |= (s.sm->boosted[j] == e) ? 1u : 0u;
-      key[r] = ((unsigned long long)(tier + 1u) << 42) | ((unsigned long long)ord_f32(sc) << 10) |
-               (unsigned long long)(kMaxE - 1 - e);
+      for (int c = 0; c < kCh; ++c) {
+        raw[2 * c] = ld_coh4(r, (lane + kWave * c) * 32);
+        raw[2 * c + 1] = ld_coh4(r, (lane + kWave * c) * 32 + 16);
+      }
+      int good = 1;
+#pragma unroll
+      for (int c = 0; c < kCh; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = 4 * (lane + kWave * c) + q;
+          const unsigned ep = (q & 1) ? raw[2 * c + q / 2].w : raw[2 * c + q / 2].y;
+          good &= (e >= E || ep == epoch) ? 1 : 0;
+        }
+      if (__all(good)) break;
+      if ((it & 31u) == 31u) {
+        bool go = true;
+        if (lane == 0) go = poll_abort(a, t0, 1);
+        if (!__shfl(go ? 1 : 0, 0)) {
+          s.sm->ok = 0;
+          return;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r4 = 4 * c + q;
+        const int e = 4 * (lane + kWave * c) + q;
+        const unsigned bits = (q & 1) ? raw[2 * c + q / 2].z : raw[2 * c + q / 2].x;
+        const float lg = __uint_as_float(bits);
+        lgv[r4] = lg;
+        float sc = lg;
+        if (sb) sc = by_bias ? sb[min(e, E - 1)] : lg + sb[min(e, E - 1)];
+        unsigned tier = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) tier |= (bst[j] == e) ? 1u : 0u;
+        key[r4] = e < E ? ((unsigned long long)(tier + 1u) << 42) |
+                              ((unsigned long long)ord_f32(sc) << 10) |
+                              (unsigned long long)(kMaxE - 1 - e)
+                        : 0ull;
+      }
     }
   }
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  // K rounds of a wave-wide argmax; winners land in lane k of isel/lsel
+  int my_idx = 0;
+  float my_lg = 0.f;
   for (int k = 0; k < K; ++k) {
     unsigned long long best = 0;
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) best = key[r] > best ? key[r] : best;
-    best = wave_max_u64(best);
-    if (lane == 0) s.sm->red64[w] = best;
-    __syncthreads();
-    best = 0;
-    for (int i = 0; i < kNW; ++i) best = s.sm->red64[i] > best ? s.sm->red64[i] : best;
-    const int e = kMaxE - 1 - (int)(best & 1023ull);
+    float bl = 0.f;
 #pragma unroll
     for (int r = 0; r < kPer; ++r)
-      if (key[r] == best) key[r] = 0;
-    if (threadIdx.x == 0) s.sm->sel_idx[k] = e;
-    __syncthreads();
+      if (key[r] > best) {
+        best = key[r];
+        bl = lgv[r];
+      }
+    const unsigned long long wbest = wave_max_u64(best);
+    const int e = kMaxE - 1 - (int)(wbest & 1023ull);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r)
+      if (key[r] == wbest) key[r] = 0;
+    const float lw = __shfl(bl, (e / 4) % kWave);  // the owner lane holds the winner's logit
+    if (lane == k) {
+      my_idx = e;
+      my_lg = lw;
+    }
   }
-  if (threadIdx.x == 0) {
-    float lg[kMaxK], m = -INFINITY;
-    for (int k = 0; k < K; ++k) {
-      lg[k] = a.logits[s.sm->sel_idx[k]];
-      m = fmaxf(m, lg[k]);
-    }
-    float z = 0.f;
-    for (int k = 0; k < K; ++k) {
-      lg[k] = expf(lg[k] - m);
-      z += lg[k];
-    }
-    for (int k = 0; k < K; ++k) s.sm->sel_w[k] = lg[k] / z;
+  // softmax over the K selected logits (lanes 0..K-1)
+  const bool mine = lane < K;
+  float m = mine ? my_lg : -INFINITY;
+  m = wave_max(m);
+  float ex = mine ? expf(my_lg - m) : 0.f;
+  const float z = wave_sum(ex);
+  const float wk = ex / z;
+  if (mine) {
+    s.sm->sel_idx[lane] = my_idx;
+    s.sm->sel_w[lane] = wk;
   }
-  __syncthreads();
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    // publish for the next phase's launch (phased mode), the outputs, and the
-    // sorted set for the next token's temporal tier
-    for (int k = 0; k < K; ++k) {
-      a.sel[k] = s.sm->sel_idx[k];
-      a.sel[kMaxK + k] = __float_as_int(s.sm->sel_w[k]);
+  if (blockIdx.x == 0) {
+    // publish for a following phase launch, the outputs, and the sorted set for the
+    // next token's temporal tier
+    if (mine) {
+      st_coh(a.sel + lane, my_idx);
+      st_coh(a.sel + kMaxK + lane, __float_as_int(wk));
+      const size_t o = ((size_t)t * a.L + l) * K;
+      if (a.idx_out) a.idx_out[o + lane] = my_idx;
+      if (a.w_out) a.w_out[o + lane] = wk;
     }
-    size_t o = ((size_t)t * a.L + l) * K;
-    if (a.idx_out)
-      for (int k = 0; k < K; ++k) a.idx_out[o + k] = s.sm->sel_idx[k];
-    if (a.w_out)
-      for (int k = 0; k < K; ++k) a.w_out[o + k] = s.sm->sel_w[k];
     if (a.mode == MODE_LAYER) {
-      int srt[kMaxK];
-      for (int k = 0; k < K; ++k) srt[k] = s.sm->sel_idx[k];
-      for (int i = 1; i < K; ++i)
-        for (int j = i; j > 0 && srt[j - 1] > srt[j]; --j) {
-          const int tmp = srt[j];
-          srt[j] = srt[j - 1];
-          srt[j - 1] = tmp;
-        }
+      // rank of my_idx among the selected set = its position in sorted order
+      int rank = 0;
+      for (int j = 0; j < K; ++j) {
+        const int other = __shfl(my_idx, j);
+        rank += (j != lane && other < my_idx) ? 1 : 0;
+      }
       int* ps = a.prev + ((size_t)(t & 1) * a.L + l) * kMaxK;
-      for (int k = 0; k < K; ++k) ps[k] = srt[k];
+      if (mine) st_coh(ps + rank, my_idx);
     }
+    wait_mem();  // published before any later exchange write of this workgroup
   }
 }
 
-template <int BITS>
-__device__ void phase_b(const DecodeArgs& a, const Lds& s, int t, int l) {
-  if (a.mode == MODE_EXPERT) {
-    auto fn = [&](int i, const uint8_t*& base, float*& hout, int& blk) {
-      base = a.single_expert;
-      blk = i;
-      hout = a.hbuf;
-    };
-    gateup_items<BITS>(a, s, a.geo.nblk_gu, 0, fn);
-    return;
-  }
-  select_topk(a, s, t, l);
-  SUBSTAMP(10);
-  if (a.mode != MODE_LAYER) return;
+// The expert-list entry li of phase C: its packed expert and routing weight.
+__device__ inline const uint8_t* list_expert(const DecodeArgs& a, const Lds& s, int l, int li,
+                                             float& wk) {
   const Geo& g = a.geo;
-  const uint8_t* experts = a.layers[l].experts;
-  auto fn = [&](int i, const uint8_t*& base, float*& hout, int& blk) {
-    const int k = i / g.nblk_gu;
-    blk = i % g.nblk_gu;
-    base = experts + (size_t)s.sm->sel_idx[k] * g.expert_bytes;
-    hout = a.hbuf + (size_t)k * g.I;
-  };
-  gateup_items<BITS>(a, s, a.K * g.nblk_gu, 0, fn);
+  if (a.mode == MODE_EXPERT) {
+    wk = 1.f;
+    return a.single_expert;
+  }
+  if (li < a.K) {
+    wk = s.sm->sel_w[li];
+    return a.layers[l].experts + (size_t)s.sm->sel_idx[li] * g.expert_bytes;
+  }
+  wk = 1.f;
+  return a.layers[l].shared + (size_t)(li - a.K) * g.expert_bytes;
+}
+
+// Prefetch (into LDS) the down blocks phase C of this workgroup reads, for every
+// list entry, on waves [w0, kNW). Needs the selection in LDS.
+__device__ __forceinline__ void prefetch_c(const DecodeArgs& a, const Lds& s, int l, int w0) {
+  const Geo& g = a.geo;
+  const int r0 = blockIdx.x * a.rpw;
+  if (r0 >= g.H) return;
+  const int b0 = r0 / g.Pi;
+  const int nb = min(a.nbd, g.nblk_d - b0);
+  const int nlist = a.K + a.S;
+  for (int li = 0; li < nlist; ++li) {
+    float wk;
+    const uint8_t* ex = list_expert(a, s, l, li, wk);
+    dma_to_lds(s.tile_c + (size_t)li * a.nbd * g.blk, ex + g.off_down + (size_t)b0 * g.blk,
+               nb * g.blk, w0);
+  }
 }
 
 template <int BITS>
-__device__ void phase_c(const DecodeArgs& a, const Lds& s, int t, int l) {
+__device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t, int l, bool tiles) {
+  const Geo& g = a.geo;
+  if (a.mode == MODE_EXPERT) {
+    int i0, i1;
+    split_range(g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
+    auto src = [&](int i, const uint8_t*& gb, const uint8_t*& ub, int& hvec, int& row0) {
+      gb = a.single_expert + (size_t)i * g.blk;
+      ub = gb + g.off_up;
+      hvec = 0;
+      row0 = i * g.Ph;
+    };
+    gateup_items<BITS>(a, s, i0, i1, false, epoch_of(a, t, l), src, [] {});
+    return true;
+  }
+  if (threadIdx.x == 0) s.sm->ok = 1;
+  __syncthreads();
+  select_topk(a, s, t, l);
+  __syncthreads();
+  if (!s.sm->ok) return false;
+  SUBSTAMP(10);
+  if (a.trace_wg && t == 2 && threadIdx.x == 0)
+    a.trace_wg[((size_t)l * a.nwg + blockIdx.x) * 4 + 1] = wall_clock64();
+  if (a.mode != MODE_LAYER) return true;
+  const uint8_t* experts = a.layers[l].experts;
+  int i0, i1;
+  split_range(a.K * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
+  auto src = [&](int i, const uint8_t*& gb, const uint8_t*& ub, int& hvec, int& row0) {
+    const int k = i / g.nblk_gu, b = i % g.nblk_gu;
+    gb = experts + (size_t)s.sm->sel_idx[k] * g.expert_bytes + (size_t)b * g.blk;
+    ub = gb + g.off_up;
+    hvec = k;
+    row0 = b * g.Ph;
+  };
+  // the down blocks of phase C stream into LDS behind this wave's gate/up loads
+  auto hook = [&] {
+    if (tiles) prefetch_c(a, s, l, 0);
+  };
+  gateup_items<BITS>(a, s, i0, i1, false, epoch_of(a, t, l), src, hook);
+  return true;
+}
+
+template <int BITS>
+__device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t, int l, bool tiles,
+                                        bool down_tile) {
   const Geo& g = a.geo;
   const int H = g.H, I = g.I;
   const bool expert_mode = a.mode == MODE_EXPERT;
   const int nlist = expert_mode ? 1 : a.K + a.S;
-  // digits of every h vector (each workgroup encodes all of them)
+  const int rpw = a.rpw;
+  const int r0 = blockIdx.x * rpw;
+  const int r1 = min(H, r0 + rpw);
+  // h vectors of this layer (polled; in-order completion also retires the down-tile
+  // prefetch this wave issued in phase B)
+  float* hs = s.hstage;
+  {
+    const Xv hv = xv_h(a);
+    const Xv part{hv.base, nlist * I, hv.n_pad};
+    const bool ok = xget(a, part, hs, epoch_of(a, t, l));
+    if (!wg_all(s.sm, ok)) return false;
+  }
+  // the next layer's router rows and shared blocks stream into LDS meanwhile
+  if (tiles) {
+    const bool last = (l == a.L - 1);
+    if (!(last && t == a.T - 1)) prefetch_a(a, s, last ? 0 : l + 1, 0);
+  }
   {
     float mx[kMaxPass];
-    for (int j = 0; j < nlist; ++j) mx[j] = 0.f;
-    for (int i = threadIdx.x; i < I; i += kThreads)
-      for (int j = 0; j < nlist; ++j) mx[j] = fmaxf(mx[j], fabsf(a.hbuf[(size_t)j * I + i]));
+    for (int j = 0; j < nlist; ++j) {
+      mx[j] = 0.f;
+      for (int i = threadIdx.x * 4; i < I; i += kThreads * 4) {
+        const float4 v = *reinterpret_cast<const float4*>(hs + (size_t)j * I + i);
+        mx[j] = fmaxf(mx[j], fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      }
+    }
     const int w = threadIdx.x / kWave;
     for (int j = 0; j < nlist; ++j) {
       const float m = wave_max(mx[j]);
@@ -654,15 +1011,13 @@ __device__ void phase_c(const DecodeArgs& a, const Lds& s, int t, int l) {
       digit_scale(m, &s.sm->hsc[threadIdx.x], &s.sm->hxs[threadIdx.x]);
     }
     __syncthreads();
-    encode_vectors(a.hbuf, (size_t)I, nlist, I, s.sm->hsc, s.hdig, s.hsum);
+    encode_vectors(hs, nlist, I, s.sm->hsc, s.hdig, s.hsum);
     __syncthreads();
   }
   SUBSTAMP(11);
-  const int rpw = a.rpw;
-  const int r0 = blockIdx.x * rpw;
-  const int r1 = min(H, r0 + rpw);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int npass = expert_mode ? 1 : a.npass;
+  const int b0 = r0 / g.Pi;
   if (r0 < r1) {
     for (int pi = 0; pi < npass; ++pi) {
       const int first = expert_mode ? 0 : a.pass_first[pi];
@@ -671,19 +1026,10 @@ __device__ void phase_c(const DecodeArgs& a, const Lds& s, int t, int l) {
       const int Pp = kWave / seg;
       const int grp = lane % g.Gi, kl = (lane / g.Gi) % n, p = lane / seg;
       const int li = first + kl;  // index in the expert list
-      const uint8_t* ex;
       float wk;
-      if (expert_mode) {
-        ex = a.single_expert;
-        wk = 1.f;
-      } else if (li < a.K) {
-        ex = a.layers[l].experts + (size_t)s.sm->sel_idx[li] * g.expert_bytes;
-        wk = s.sm->sel_w[li];
-      } else {
-        ex = a.layers[l].shared + (size_t)(li - a.K) * g.expert_bytes;
-        wk = 1.f;
-      }
-      const uint8_t* down = ex + g.off_down;
+      const uint8_t* ex = list_expert(a, s, l, li, wk);
+      const uint8_t* down = down_tile ? s.tile_c + (size_t)li * a.nbd * g.blk : ex + g.off_down;
+      const int bbase = down_tile ? b0 : 0;
       const int nchunk = (r1 - r0 + Pp - 1) / Pp;
       if (w >= nchunk) continue;
       Dig D;
@@ -697,7 +1043,7 @@ __device__ void phase_c(const DecodeArgs& a, const Lds& s, int t, int l) {
           row[j] = r0 + c * Pp + p;
           if (c < nchunk && row[j] < r1) {
             const int b = row[j] / g.Pi, pd = row[j] % g.Pi;
-            S[j] = ld_slot<BITS>(down + (size_t)b * g.blk, pd * g.Gi + grp);
+            S[j] = ld_slot<BITS>(down + (size_t)(b - bbase) * g.blk, pd * g.Gi + grp, down_tile);
           }
         }
 #pragma unroll
@@ -714,80 +1060,105 @@ __device__ void phase_c(const DecodeArgs& a, const Lds& s, int t, int l) {
   }
   __syncthreads();
   SUBSTAMP(12);
-  if (r0 < r1) {
+  const int rr = r0 + (int)threadIdx.x;
+  if (rr < r1 && (int)threadIdx.x < rpw) {
     const bool res = !expert_mode && (a.flags & MOE_F_RESIDUAL);
-    const float* xin = token_input(a, t, l);
-    float* out;
-    if (expert_mode || l == a.L - 1) out = a.y + (size_t)t * H;
-    else out = a.xbuf + (size_t)((l + 1) & 1) * H;
-    for (int r = r0 + threadIdx.x; r < r1; r += kThreads) {
-      float v = res ? xin[r] : 0.f;
-      for (int pi = 0; pi < npass; ++pi) v += s.acc[pi * rpw + (r - r0)];
-      out[r] = v;
-    }
+    float v = res ? s.xres[threadIdx.x] : 0.f;
+    for (int pi = 0; pi < npass; ++pi) v += s.acc[pi * rpw + (rr - r0)];
+    if (expert_mode || l == a.L - 1) a.y[(size_t)t * H + rr] = v;
+    else xput(xv_x(a), rr, v, epoch_of(a, t, l + 1));
   }
+  return true;
 }
 
-// only_phase < 0: persistent (all tokens, all layers, grid barriers between phases).
-// only_phase = 0/1/2: run that phase for token t_only, layer l_only.
+// only_phase < 0: persistent (all tokens, all layers; phases wait on their inputs'
+// epochs). only_phase = 0/1/2: run that phase for token t_only, layer l_only.
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int only_phase, int t_only,
                                                           int l_only) {
   extern __shared__ __align__(16) unsigned lds_raw[];
   const Lds s = lds_view(lds_raw, a);
   const bool persistent = only_phase < 0;
+  const bool pf = persistent && a.pf && a.mode == MODE_LAYER;
+  const bool pfd = pf && a.pf_down;
   const int t0 = persistent ? 0 : t_only, t1 = persistent ? a.T : t_only + 1;
   const int l0 = persistent ? 0 : l_only, l1 = persistent ? a.L : l_only + 1;
-  unsigned bar = 0;
+  if (pf) prefetch_a(a, s, 0, 0);
   unsigned long long* tr = nullptr;
   for (int t = t0; t < t1; ++t) {
     for (int l = l0; l < l1; ++l) {
       if (a.trace && blockIdx.x == 0 && threadIdx.x == 0) tr = a.trace + ((size_t)t * a.L + l) * 16;
+      if (threadIdx.x == 0) s.sm->tr = tr;
 #define QMOE_STAMP(i) \
   if (tr) tr[i] = wall_clock64();
-      if (threadIdx.x == 0) s.sm->tr = tr;
       QMOE_STAMP(0);
+      unsigned long long* twg = (a.trace_wg && t == 2 && threadIdx.x == 0)
+                                    ? a.trace_wg + ((size_t)l * a.nwg + blockIdx.x) * 4
+                                    : nullptr;
       bool have_x = false;
       if (a.mode != MODE_EXPERT && (persistent || only_phase == 0)) {
-        phase_a<BITS>(a, s, t, l);
+        if (pf) {
+          wait_mem();  // this wave's router / shared prefetch has landed
+          __syncthreads();
+        }
+        if (!phase_a<BITS>(a, s, t, l, pf)) return;
         have_x = true;
         QMOE_STAMP(1);
-        if (persistent && !grid_sync(a, s.sm, ++bar)) return;
-        QMOE_STAMP(2);
+        if (twg) twg[0] = wall_clock64();
       }
       if (persistent || only_phase == 1) {
-        if (!have_x && a.mode != MODE_ROUTE) prepare_x(a, s, t, l);
-        phase_b<BITS>(a, s, t, l);
+        if (!have_x && a.mode != MODE_ROUTE && !prepare_x(a, s, t, l)) return;
+        if (!phase_b<BITS>(a, s, t, l, pfd)) return;
         QMOE_STAMP(3);
-        if (persistent && !grid_sync(a, s.sm, ++bar)) return;
-        QMOE_STAMP(4);
+        if (twg) twg[2] = wall_clock64();
       }
       if (a.mode != MODE_ROUTE && (persistent || only_phase == 2)) {
         if (!persistent && a.mode == MODE_LAYER) {
-          if (threadIdx.x < a.K) {
-            s.sm->sel_idx[threadIdx.x] = a.sel[threadIdx.x];
-            s.sm->sel_w[threadIdx.x] = __int_as_float(a.sel[kMaxK + threadIdx.x]);
+          // phased launch: the residual rows come straight from memory (the
+          // producing launch has completed)
+          const int r0 = blockIdx.x * a.rpw;
+          if ((int)threadIdx.x < a.rpw && r0 + (int)threadIdx.x < a.geo.H) {
+            const int r = r0 + threadIdx.x;
+            s.xres[threadIdx.x] = l == 0 ? a.x0[(size_t)t * a.geo.H + r]
+                                         : __uint_as_float((unsigned)a.xx[r]);
+          }
+          if ((int)threadIdx.x < a.K) {
+            s.sm->sel_idx[threadIdx.x] = ld_coh(a.sel + threadIdx.x);
+            s.sm->sel_w[threadIdx.x] = __int_as_float(ld_coh(a.sel + kMaxK + threadIdx.x));
           }
           __syncthreads();
         }
-        phase_c<BITS>(a, s, t, l);
+        if (pfd) {
+          wait_mem();  // this wave's down-block prefetch has landed
+          __syncthreads();
+        }
+        if (!phase_c<BITS>(a, s, t, l, pf, pfd)) return;
         QMOE_STAMP(5);
-        if (persistent && !grid_sync(a, s.sm, ++bar)) return;
-        QMOE_STAMP(6);
+        if (twg) twg[3] = wall_clock64();
       }
 #undef QMOE_STAMP
     }
   }
 }
 
-__global__ void zero_words(unsigned* p, int n, unsigned* q, int m) {
-  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
-  if ((int)threadIdx.x < m) q[threadIdx.x] = 0u;
+// Clears the abort flag, the error word and every exchange slot (epoch 0 never
+// matches a live epoch, which start at 1).
+__global__ void zero_words(unsigned* sync, unsigned* err, unsigned long long* xch, size_t nx) {
+  const size_t i0 = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i0 == 0) {
+    sync[0] = 0u;
+    err[0] = 0u;
+  }
+  for (size_t i = i0; i < nx; i += (size_t)gridDim.x * blockDim.x) xch[i] = 0ull;
 }
 
 // ------------------------------------------------------------ host side
 static int g_num_cu = -1;
-unsigned long long* g_trace = nullptr;  // set only by instrumented builds
+unsigned long long* g_trace = nullptr;     // set only by instrumented builds
+unsigned long long* g_trace_wg = nullptr;  // set only by instrumented builds
+int g_prefetch_mask = 0;  // LDS prefetch of router/shared tiles (bit 0) and down tiles (bit 1); off:
+                          // measured slower than direct loads (the DMA competes with the
+                          // latency-bound exchanges)
 static long long g_wall_khz = -1;
 
 static hipError_t device_info() {
@@ -831,15 +1202,17 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.w_out = r.w_out;
   a.logits_out = r.logits_out;
   uint8_t* ws = r.ws;
-  a.xbuf = reinterpret_cast<float*>(ws + r.wl.xbuf);
-  a.logits = reinterpret_cast<float*>(ws + r.wl.logits);
-  a.hbuf = reinterpret_cast<float*>(ws + r.wl.hbuf);
+  a.xx = reinterpret_cast<unsigned long long*>(ws + r.wl.xbuf);
+  a.lx = reinterpret_cast<unsigned long long*>(ws + r.wl.logits);
+  a.hx = reinterpret_cast<unsigned long long*>(ws + r.wl.hbuf);
+  a.e_pad = (a.E + 1) & ~1;
   a.sel = reinterpret_cast<int*>(ws + r.wl.sel);
   a.prev = reinterpret_cast<int*>(ws + r.wl.prev);
   a.sync = reinterpret_cast<unsigned*>(ws + r.wl.sync);
   a.err = reinterpret_cast<unsigned*>(ws + r.wl.err);
   a.timeout_ticks = (unsigned long long)g_wall_khz * 2000ull;  // 2 seconds per barrier wait
   a.trace = g_trace;
+  a.trace_wg = g_trace_wg;
 
   // Expert passes for phase C: routed experts in power-of-two groups that fit a
   // wave (lanes = rows x experts x groups), then the shared experts.
@@ -869,19 +1242,12 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   int maxP = 1;
   for (int i = 0; i < np; ++i) maxP = std::max(maxP, kWave / (a.pass_count[i] * Gi));
 
-  // LDS carve-up
-  int words = (int)((sizeof(Small) + 15) / 4);
-  words = (words + 3) & ~3;
-  a.lds_xn = words; words += c.hidden;
-  a.lds_xdig = words; words += a.geo.Gh * kDigitStride;
-  a.lds_xsum = words; words += 2 * a.geo.Gh;
-  words = (words + 3) & ~3;
-  a.lds_hdig = words; words += (c.top_k + c.n_shared) * Gi * kDigitStride;
-  a.lds_hsum = words; words += 2 * (c.top_k + c.n_shared) * Gi;
-  a.lds_acc = words;
-
-  // workgroups: one per CU, capped so that phase C rows per workgroup stay <= 64
-  int nwg = g_num_cu;
+  // one workgroup per compute unit; phase C rows per workgroup stay <= 64
+  const int nwg = g_num_cu;
+  if (nwg > kMaxNwg) {
+    *why = "more compute units than the decode kernel supports";
+    return hipErrorInvalidValue;
+  }
   int rpw = (c.hidden + nwg - 1) / nwg;
   rpw = ((rpw + maxP - 1) / maxP) * maxP;
   if (rpw > 64) {
@@ -889,20 +1255,61 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
     return hipErrorInvalidValue;
   }
   a.rpw = rpw;
-  words += kMaxPass * rpw;
+  a.nwg = nwg;
+  const int nlist = r.mode == MODE_EXPERT ? 1 : c.top_k + c.n_shared;
+
+  // LDS carve-up (32-bit words). The h staging area of phase C overlays the x
+  // region (x, its digits and sums), which is dead by then.
+  auto up4 = [](int v) { return (v + 3) & ~3; };
+  const int hstage_words = nlist * c.inter;
+  int words = up4((int)((sizeof(Small) + 3) / 4));
+  const int xregion = words;
+  a.lds_xn = words; words = up4(words + c.hidden);
+  a.lds_xdig = words; words = up4(words + a.geo.Gh * kDigitStride);
+  a.lds_xsum = words; words = up4(words + 2 * a.geo.Gh);
+  words = std::max(words, up4(xregion + hstage_words));
+  a.lds_hdig = words; words = up4(words + nlist * Gi * kDigitStride);
+  a.lds_hsum = words; words = up4(words + 2 * nlist * Gi);
+  a.lds_acc = words; words = up4(words + kMaxPass * rpw);
+  a.lds_xres = words; words = up4(words + rpw);
+  // tiles: router rows and shared gate/up items of this workgroup; down blocks
+  const int rows_pw = (a.E + nwg - 1) / nwg;
+  const int sh_pw = (a.S * a.geo.nblk_gu + nwg - 1) / nwg;
+  const int router_words = rows_pw * c.hidden;
+  const int sh_words = sh_pw * 2 * a.geo.blk / 4;
+  // down tile: the blocks covering rows [r0, r0 + rpw) (one extra for a straddle)
+  a.nbd = (rpw + a.geo.Pi - 1) / a.geo.Pi + (rpw % a.geo.Pi ? 1 : 0);
+  const int down_words = nlist * a.nbd * a.geo.blk / 4;
+  const bool want_pf = r.mode == MODE_LAYER && !r.phased;
+  const int with_pf = words + router_words + sh_words + down_words + 12;
+  a.pf = want_pf && (size_t)with_pf * 4 <= (size_t)kMaxLdsBytes;
+  a.pf_down = a.pf && (g_prefetch_mask & 2);
+  if (!(g_prefetch_mask & 1)) a.pf = 0;
+  if (!a.pf && a.pf_down) a.pf = 0, a.pf_down = 0;
+  a.lds_tile_a = a.lds_tile_sh = a.lds_tile_c = words;
+  if (a.pf) {
+    words = up4(words + router_words);
+    a.lds_tile_sh = words; words = up4(words + sh_words);
+    a.lds_tile_c = words; words = up4(words + down_words);
+  }
   a.lds_words = words;
   const size_t lds = (size_t)words * 4;
-  a.nwg = nwg;
+  if (lds > (size_t)kMaxLdsBytes) {
+    *why = "shape needs more LDS than a workgroup has";
+    return hipErrorInvalidValue;
+  }
 
   auto kern = c.bits == 4 ? decode_kernel<4> : decode_kernel<2>;
   static bool attr_set[2] = {false, false};
   if (lds > 64 * 1024 && !attr_set[c.bits == 4]) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
     if (e != hipSuccess) return e;
     attr_set[c.bits == 4] = true;
   }
-  hipLaunchKernelGGL(zero_words, dim3(1), dim3(64), 0, stream, a.sync, 2, a.err, 1);
+  // every exchange slot of this call starts at epoch 0
+  const size_t nx = (size_t)(r.wl.prev - r.wl.xbuf) / sizeof(unsigned long long);
+  hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, stream, a.sync, a.err, a.xx, nx);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (r.phased) {

@@ -15,6 +15,8 @@ constexpr int kMaxK = 8;
 constexpr int kMaxE = 1024;
 constexpr int kMaxShared = 2;
 constexpr int kMaxDim = 4096;
+constexpr int kMaxNwg = 1024;     // workgroups a decode launch may use
+constexpr int kRep = 8;           // replicas of every exchanged vector (spreads polling)
 constexpr int kDigitStride = 52;  // dwords per (vector, group) in LDS: 48 digit dwords + pad
 
 // ---------------------------------------------------------------------------
@@ -94,11 +96,12 @@ inline WsLayout ws_layout(const moe_config& c, int T, int L) {
   WsLayout w;
   size_t o = 0;
   w.err = o; o += 256;
-  w.sync = o; o += 256;
+  w.sync = o; o = align256(o + sizeof(unsigned) * (64 + kMaxNwg));
   w.pack_err = o; o += 256;
-  w.xbuf = o; o = align256(o + 2 * sizeof(float) * c.hidden);
-  w.logits = o; o = align256(o + sizeof(float) * c.n_experts);
-  w.hbuf = o; o = align256(o + sizeof(float) * (size_t)(kMaxK + kMaxShared) * c.inter);
+  // exchanged vectors: kRep replicas of (value, epoch) pairs
+  w.xbuf = o; o = align256(o + kRep * sizeof(uint64_t) * c.hidden);
+  w.logits = o; o = align256(o + kRep * sizeof(uint64_t) * c.n_experts);
+  w.hbuf = o; o = align256(o + kRep * sizeof(uint64_t) * (size_t)(kMaxK + kMaxShared) * c.inter);
   w.sel = o; o = align256(o + 2 * sizeof(int) * kMaxK);
   w.prev = o; o = align256(o + sizeof(int) * 2 * (size_t)(L > 0 ? L : 1) * kMaxK);
   w.layers = o; o = align256(o + sizeof(LayerPtrs) * (size_t)(L > 0 ? L : 1));
@@ -134,7 +137,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
 enum DevErr : unsigned {
   DEV_OK = 0,
   DEV_BAD_INDEX = 1,     // an expert index outside [0, E)
-  DEV_SYNC_TIMEOUT = 2,  // a grid barrier wait exceeded its time limit
+  DEV_SYNC_TIMEOUT = 2,  // a wait for another workgroup's data exceeded its time limit
   DEV_BAD_CODE = 3,      // pack: a code >= 2^bits
 };
 

@@ -81,6 +81,57 @@ class HostLayer:
         return [self.expert(self.w.n_experts + s) for s in range(self.w.n_shared)]
 
 
+class DeviceCanonicalLayer:
+    """Canonical experts of one layer for the oracle, produced with the device
+    generator (same bits as the host generator) and copied to the host: fast
+    enough to regenerate the experts a 60-layer replay touches. Time spent
+    generating is accumulated in ``gen_seconds``."""
+
+    def __init__(self, w: wl.WorkloadConfig, layer: int, router=None):
+        import time
+        import torch
+        self.w, self.layer = w, layer
+        self.spec = w.expert_spec()
+        self._cache = {}
+        self.gen_seconds = 0.0
+        t0 = time.perf_counter()
+        if router is not None:
+            self.router = router
+        else:
+            r = torch.empty((w.n_experts, w.hidden), dtype=torch.float32, device="cuda")
+            wdev.router(w.seed, layer, w.n_experts, w.hidden, r, sigma=w.sigma_router)
+            self.router = r.cpu().numpy()
+        self.gen_seconds += time.perf_counter() - t0
+
+    def expert(self, e):
+        import time
+        import torch
+        if e in self._cache:
+            return self._cache[e]
+        t0 = time.perf_counter()
+        H, I = self.w.hidden, self.w.inter
+        codes = torch.empty((1, 3, H * I), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((1, 3, H * I // 64), dtype=torch.int16, device="cuda")
+        bi = torch.empty((1, 3, H * I // 64), dtype=torch.int16, device="cuda")
+        keep = wdev.experts_canonical(self.spec, self.w.seed, self.layer, [e], codes, sc, bi)
+        torch.cuda.synchronize()
+        c, s_, b = codes.cpu().numpy()[0], sc.cpu().numpy()[0].view(np.uint16), bi.cpu().numpy()[0].view(np.uint16)
+        del keep
+        shapes = [(I, H), (I, H), (H, I)]
+        canon = ([c[m].reshape(shapes[m]) for m in range(3)],
+                 [s_[m].reshape(shapes[m][0], -1) for m in range(3)],
+                 [b[m].reshape(shapes[m][0], -1) for m in range(3)])
+        if len(self._cache) > self.w.n_shared + self.w.top_k:
+            # keep the shared experts; routed ones are reused only within one token
+            self._cache = {k: v for k, v in self._cache.items() if k >= self.w.n_experts}
+        self._cache[e] = canon
+        self.gen_seconds += time.perf_counter() - t0
+        return canon
+
+    def shared(self):
+        return [self.expert(self.w.n_experts + s) for s in range(self.w.n_shared)]
+
+
 def parity(y, y_ref, what=""):
     """The bar for float32 outputs: max|err| <= 2e-3 max|y_ref| and rel-L2 <= 1e-4."""
     y = np.asarray(y, dtype=np.float64)
