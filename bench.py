@@ -69,6 +69,125 @@ def cpu_baseline_and_parity(w, x0_host, y_gpu, idx_gpu, n_tokens):
                 "near_tie_follows": len(flagged)}
 
 
+def prefill_bench(args, w):
+    """One step = one moe_layer_forward(MOE_F_PREFILL_BF16) call on the prefill workload:
+    every token of the prompt through one layer, grouped by expert."""
+    import numpy as np
+    import torch
+    import quantized_expert_mat_amd as q
+    import workload as wl
+    from workload import device as wdev
+    from tests.helpers import DeviceLayer, config_for
+
+    T, H, K, S, E = w.n_tokens, w.hidden, w.top_k, w.n_shared, w.n_experts
+    cfg = config_for(w, q.MOE_F_PREFILL_BF16 | q.MOE_F_SELECT_BY_BIAS)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    ws = torch.empty(q.moe_workspace_bytes(cfg, T, 1), dtype=torch.uint8, device=dev)
+    dl = DeviceLayer(w, 0, chunk=8, ws=ws)
+    x = torch.empty((T, H), dtype=torch.float32, device=dev)
+    keep = wdev.tokens_x(w.seed + 1000, T, H, x)
+    sel_h, _ = wl.zipf_gumbel_scores(w.seed + 11, T, E, w.zipf)
+    sel = torch.from_numpy(sel_h).to(dev)
+    y = torch.empty_like(x)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, K), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    stream = torch.cuda.current_stream()
+    lw = dl.weights()
+
+    def step():
+        q.moe_layer_forward(cfg, lw, T, x, y, ws, sel_bias=sel, idx_out=idx, w_out=wts, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    q.moe_device_status(ws)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    q.moe_device_status(ws)
+    avg_s = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps / 1e3
+    ih = idx.cpu().numpy()
+    counts = np.bincount(ih.reshape(-1), minlength=E)
+    distinct = int((counts > 0).sum())
+    eb = q.moe_packed_expert_bytes(cfg)
+    # algorithmic bytes: weights of every touched expert, the selected router rows,
+    # the input, the selection scores and the output
+    router_rows = distinct
+    nbytes = (distinct + S) * eb + router_rows * H * 4 + T * H * 4 * 2 + T * E * 4
+    flops = 2.0 * (T * K + S * T) * 3 * H * w.inter
+    achieved = nbytes / avg_s / 1e9
+    tflops = flops / avg_s / 1e12
+    log(f"prefill: {T * args.steps / elapsed:.1f} tok/s, launch avg {avg_s * 1e3:.3f} ms, {achieved:.0f} GB/s, "
+        f"{tflops:.1f} TFLOP/s bf16, distinct experts {distinct}, largest group {counts.max()}")
+
+    cpu = None
+    par = None
+    if not args.no_cpu:
+        from oracle import ref
+        from tests.helpers import DeviceCanonicalLayer, parity
+        cl = DeviceCanonicalLayer(w, 0)
+        xh, yh, wh = x.cpu().numpy(), y.cpu().numpy(), wts.cpu().numpy()
+        n = min(args.cpu_tokens, T)
+        toks = [int(t) for t in np.linspace(0, T - 1, n)]
+        dt = 0.0
+        worst = (0.0, 0.0)
+        for t in toks:
+            for e in ih[t]:  # generate this token's experts outside the timed region
+                cl.expert(int(e))
+            g0 = cl.gen_seconds
+            t1 = time.perf_counter()
+            r = ref.prefill_token(xh[t], cl.router, cl.expert, cl.shared(), K, sel_h[t])
+            dt += time.perf_counter() - t1 - (cl.gen_seconds - g0)
+            assert np.array_equal(np.asarray(r.idx), ih[t]), f"token {t}: experts differ"
+            rm, rl = parity(yh[t], r.y, f"prefill token {t}")
+            worst = (max(worst[0], rm), max(worst[1], rl))
+        cpu = {"value": round(n / dt, 4), "unit": "tok/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} of the {T} tokens (evenly spaced), one layer each, {dt:.1f} s of "
+                         f"single-threaded fp64 oracle arithmetic"}
+        par = {"tokens": n, "max_rel_err": float(worst[0]), "rel_l2": float(worst[1]),
+               "experts_equal": True}
+        log(f"cpu oracle: {dt:.1f} s for {n} tokens -> {cpu['value']} tok/s")
+
+    out = {
+        "metric": "prefill tok/s, one 4-bit MoE layer, expert-grouped bf16 GEMM",
+        "value": round(T * args.steps / elapsed, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "hidden": H, "inter": w.inter, "experts": E,
+                   "top_k": K, "shared": S, "bits": w.bits, "zipf": w.zipf,
+                   "distinct_experts": distinct, "largest_group": int(counts.max()),
+                   "bytes_per_step": nbytes, "flops_per_step": flops},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "scope": "whole prefill layer (prep, select, group, gate/up, down, combine)"},
+        "mfma": {"achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                 "frac": round(tflops / 2500.0, 4)},
+        "cpu_baseline": cpu,
+        "parity": par,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+    del keep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,16 +199,24 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--phased", action="store_true")
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+                    help="decode: the 60-layer stack (default); prefill: 1155 tokens through one layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the decode stack fits one MI355X's HBM and this build has "
               f"no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
+    import workload as wl
+    if args.workload == "prefill":
+        w = wl.CONFIGS[4]
+        if args.tokens:
+            w = w.replace(n_tokens=args.tokens)
+        return prefill_bench(args, w)
+
     import numpy as np
     import torch
     import quantized_expert_mat_amd as q
-    import workload as wl
     from workload import device as wdev
     from tests.helpers import DeviceLayer, config_for
 

@@ -195,18 +195,25 @@ def layer_decode(x, router_W, get_expert, shared, K, rmsnorm_on=True, residual=T
     return LayerResult(y, idx, w, gap, logits, xn)
 
 
-def prefill_token(x, router_W, get_expert, shared, K, sel, gamma=None, eps=1e-6):
-    """One token of the batched prefill with the bf16 rounding points.
-    Selection uses ``sel`` alone (Gumbel-top-k scores)."""
+def prefill_token(x, router_W, get_expert, shared, K, sel, gamma=None, eps=1e-6, by_sel=True,
+                  boosted=(), rmsnorm_on=True, residual=True, force_idx=None):
+    """One token of the batched prefill with the bf16 rounding points (the input,
+    the expert input, every dequantised weight and the SwiGLU output are rounded
+    to bf16; the router sees the unrounded normalised input). Selection uses
+    ``sel`` alone by default (Gumbel-top-k scores); by_sel=False ranks by
+    logit + sel instead. force_idx: a set chosen elsewhere at a near-tie."""
     xb = np.array([float(v) for v in np.asarray(x, dtype=np.float32)], dtype=np.float64)
     xb = round_bf16(xb)
-    xn = rmsnorm(xb, gamma, eps)
+    xn = rmsnorm(xb, gamma, eps) if rmsnorm_on else xb.copy()
     logits = router(router_W, xn)
-    idx, w, gap = select(logits, K, sel=sel, by_sel=True)
+    idx, w, gap = select(logits, K, sel=sel, by_sel=by_sel, boosted=boosted)
+    if force_idx is not None:
+        idx = np.asarray(force_idx, dtype=np.int32)
+        w = weights_for(logits, idx)
     a = round_bf16(xn)
     o_r = np.stack([expert(get_expert(int(e)), a, bf16_points=True) for e in idx])
     o_s = np.stack([expert(c, a, bf16_points=True) for c in shared]) if shared else np.zeros((0, xb.size))
-    y = combine(xb, w, o_r, o_s, residual=True)
+    y = combine(xb, w, o_r, o_s, residual=residual)
     return LayerResult(y, idx, w, gap, logits, xn)
 
 

@@ -233,6 +233,12 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_layer_weights* lay
   hipStream_t st = (hipStream_t)stream;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   if (cfg->flags & MOE_F_PREFILL_BF16) {
+    REQUIRE(layer->experts && layer->router_w, MOE_ERR_ARG, "experts/router_w is NULL");
+    REQUIRE(cfg->n_shared == 0 || layer->shared, MOE_ERR_ARG, "shared is NULL");
+    REQUIRE(aligned(layer->experts, 256) && aligned(layer->router_w, 256) &&
+                (!layer->shared || aligned(layer->shared, 256)) &&
+                (!layer->gamma || aligned(layer->gamma, 16)),
+            MOE_ERR_ALIGN, "weight pointers must be 256-byte aligned (gamma 16-byte)");
     std::string msg;
     s = prefill_forward(*cfg, layer, T, x, y, sel_bias, boosted, idx_out, w_out, w8, ws_bytes, st,
                         &msg);
