@@ -45,10 +45,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunkT = 2048;      // tokens per pass (bounds the workspace)
-constexpr int kBM = 128;           // rows (token-expert pairs) per m-tile
-constexpr int kMT = kBM / 16;      // 16-row MFMA subtiles per m-tile
-constexpr int kKC = 128;           // reduction chunk: two 64-groups
-constexpr int kArow = kKC * 2 + 16;  // LDS bytes per staged activation row (+pad)
+constexpr int kBM = 64;            // rows (token-expert pairs) per thick m-tile
 constexpr int kGuCols = 64;        // intermediate columns per gate/up workgroup
 constexpr int kDnCols = 128;       // output columns per down workgroup
 constexpr int kSortMax = 16384;    // pairs per pass (kChunkT * kMaxK)
@@ -59,7 +56,7 @@ constexpr int kPairBits = 14;      // pair index bits in a sort key
 // ---------------------------------------------------------------------------
 struct PLayout {
   int Tc, rows, max_tiles;
-  size_t err, a, xn, logits, idx, wts, pos, rowtok, tiles, hbuf, obuf, total;
+  size_t err, a, xn, logits, idx, wts, pos, rowtok, thin, thick, hbuf, obuf, total;
 };
 
 PLayout p_layout(const moe_config& c, int T) {
@@ -78,7 +75,8 @@ PLayout p_layout(const moe_config& c, int T) {
   p.wts = o; o = align256(o + (size_t)TK * 4);
   p.pos = o; o = align256(o + (size_t)TK * 4);
   p.rowtok = o; o = align256(o + (size_t)p.rows * 4);
-  p.tiles = o; o = align256(o + 16 * (size_t)(p.max_tiles + 1));
+  p.thin = o; o = align256(o + 16 * (size_t)(p.max_tiles + 1));
+  p.thick = o; o = align256(o + 16 * (size_t)(p.max_tiles + 1));
   p.hbuf = o; o = align256(o + (size_t)p.rows * c.inter * 2);
   p.obuf = o; o = align256(o + (size_t)p.rows * c.hidden * 4);
   p.total = o;
@@ -108,7 +106,8 @@ struct PArgs {
   float* wts;             // [Tc][K] routing weights
   int* pos;               // [Tc][K] row of pair (t, k) in the grouped order
   int* rowtok;            // [rows] token of each grouped row
-  int4* tiles;            // [0] = {count}; [1 + i] = {expert slot, row0, nrows, 0}
+  int4* thin;             // m-tiles of <= 16 rows: [0] = {count}; [1 + i] = {expert slot, row0, nrows, 0}
+  int4* thick;            // m-tiles of 17..64 rows, same format
   uint16_t* hbuf;         // [rows][I] bf16 SwiGLU output
   float* obuf;            // [rows][H] float32 expert outputs
 };
@@ -307,6 +306,24 @@ __global__ __launch_bounds__(256) void select_kernel(PArgs a) {
 // sort. Writes rowtok, pos and the m-tile table (routed experts in index order, then
 // the shared experts, whose rows are all tokens in order).
 // ---------------------------------------------------------------------------
+// (thin << 16) | thick: the m-tiles of an expert with c > 0 rows: full thick tiles
+// of kBM rows, then the remainder as a thin (<= 16 rows) or a thick tile.
+__device__ inline int tile_counts(int c) {
+  const int full = c / kBM, rem = c % kBM;
+  const int thick = full + (rem > 16 ? 1 : 0);
+  const int thin = (rem > 0 && rem <= 16) ? 1 : 0;
+  return (thin << 16) | thick;
+}
+
+__device__ inline void write_tiles(const PArgs& a, int e, int row0, int c, int thin_at,
+                                   int thick_at) {
+  const int full = c / kBM, rem = c % kBM;
+  for (int m = 0; m < full; ++m)
+    a.thick[1 + thick_at + m] = make_int4(e, row0 + m * kBM, kBM, 0);
+  if (rem > 16) a.thick[1 + thick_at + full] = make_int4(e, row0 + full * kBM, rem, 0);
+  else if (rem > 0) a.thin[1 + thin_at] = make_int4(e, row0 + full * kBM, rem, 0);
+}
+
 __global__ __launch_bounds__(1024) void group_kernel(PArgs a, int n2) {
   extern __shared__ unsigned gl[];
   unsigned* keys = gl;                               // [n2]
@@ -352,13 +369,15 @@ __global__ __launch_bounds__(1024) void group_kernel(PArgs a, int n2) {
   for (int s = 0; s < a.S; ++s)
     for (int t = tid; t < a.n; t += 1024) a.rowtok[np + s * a.n + t] = t;
   __syncthreads();
-  // m-tiles per expert, exclusive scan over experts (E <= 1024 = one per thread)
-  int nm = 0;
+  // m-tiles of an expert with c rows: full 128-row tiles, then the remainder as a
+  // thin tile (<= 16 rows) or a thick one. Exclusive scan over experts of the packed
+  // counts (thin << 16 | thick), one expert per thread (E <= 1024).
+  int c = 0, cnt = 0;
   if (tid < a.E) {
-    const int c = last[tid] - first[tid] + 1;
-    nm = c > 0 ? (c + kBM - 1) / kBM : 0;
+    c = last[tid] - first[tid] + 1;
+    if (c > 0) cnt = tile_counts(c);
   }
-  scan[tid] = nm;
+  scan[tid] = cnt;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
     const int v = tid >= off ? scan[tid - off] : 0;
@@ -366,65 +385,73 @@ __global__ __launch_bounds__(1024) void group_kernel(PArgs a, int n2) {
     scan[tid] += v;
     __syncthreads();
   }
-  const int routed_tiles = scan[1023];
-  if (tid < a.E && nm > 0) {
-    const int t0 = scan[tid] - nm;
-    const int c = last[tid] - first[tid] + 1;
-    for (int m = 0; m < nm; ++m) {
-      const int r = m * kBM;
-      a.tiles[1 + t0 + m] = make_int4(tid, first[tid] + r, c - r < kBM ? c - r : kBM, 0);
+  const int tot = scan[1023];
+  if (cnt > 0) {
+    const int ex = scan[tid] - cnt;
+    write_tiles(a, tid, first[tid], c, ex >> 16, ex & 0xFFFF);
+  }
+  // shared experts after the routed ones (one thread each; S <= 2)
+  if (tid == 0) {
+    int thin_n = tot >> 16, thick_n = tot & 0xFFFF;
+    for (int s = 0; s < a.S; ++s) {
+      const int k = tile_counts(a.n);
+      write_tiles(a, a.E + s, np + s * a.n, a.n, thin_n, thick_n);
+      thin_n += k >> 16;
+      thick_n += k & 0xFFFF;
     }
+    a.thin[0] = make_int4(thin_n, 0, 0, 0);
+    a.thick[0] = make_int4(thick_n, 0, 0, 0);
   }
-  const int per_shared = (a.n + kBM - 1) / kBM;
-  for (int i = tid; i < a.S * per_shared; i += 1024) {
-    const int s = i / per_shared, m = i % per_shared;
-    const int r = m * kBM;
-    a.tiles[1 + routed_tiles + i] =
-        make_int4(a.E + s, np + s * a.n + r, a.n - r < kBM ? a.n - r : kBM, 0);
-  }
-  if (tid == 0) a.tiles[0] = make_int4(routed_tiles + a.S * per_shared, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM building blocks
+// Grouped GEMM
+//
+// A work item is one m-tile of one expert (<= 16 rows: "thin", or 17..64 rows:
+// "thick") and a slice of output columns. Every wave owns two 16-column MFMA tiles
+// ("sets"): the gate and the up rows j..j+15 of the gate/up GEMM (so silu(g) * u is
+// lane-local), or two adjacent 16-row blocks of the down matrix.
+//
+// Reduction chunks are 256 wide (four 64-groups). Lane (n, kk) loads the codes of
+// group kk of the chunk for weight row n -- the four lanes of a row read 64
+// contiguous bytes of each code plane, which keeps the HBM stream dense -- and
+// feeds octet i of that group to MFMA step i (i = 0..7). The activation operand
+// uses the same order: lane (m, kk) at step i holds row m, chunk positions
+// 64kk + 8i .. 64kk + 8i + 7. Activations are copied into LDS
+// through registers, two stages deep, in a fragment-major layout
+// [subtile][kk][i][row][16 B] that the MFMA reads without bank conflicts.
 // ---------------------------------------------------------------------------
+constexpr int kKC2 = 256;                 // reduction chunk
+constexpr int kSubBytes = 16 * kKC2 * 2;  // one 16-row subtile of a chunk in LDS (8 KB)
+constexpr int kThinRows = 16;
+constexpr int kThickMT = 4;               // subtiles of a thick m-tile (64 rows)
 
-// Codes and (scale, bias) of one lane for one reduction chunk of one weight row:
-// 4-bit: 16 bytes = octets 0..3 of the lane's range; 2-bit: 8 bytes.
+// Codes and (scale, bias) of one lane's group for one chunk.
 struct WFrag {
-  u32x4 c;
+  u32x4 c0, c1;  // 4-bit: codes 0..31 and 32..63 of the group; 2-bit: c0 holds all 64
   unsigned sb;
 };
 
-template <int BITS>
-__device__ inline WFrag load_wfrag(const uint8_t* blk, int slot, int half, bool valid) {
-  WFrag f;
-  f.c = u32x4{0u, 0u, 0u, 0u};
-  f.sb = 0u;
-  if (!valid) return f;
-  if (BITS == 4) {
-    f.c = *reinterpret_cast<const u32x4*>(blk + half * 1024 + slot * 16);
-    f.sb = *reinterpret_cast<const unsigned*>(blk + 2048 + slot * 4);
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(blk + slot * 16 + half * 8);
-    f.c = u32x4{v.x, v.y, 0u, 0u};
-    f.sb = *reinterpret_cast<const unsigned*>(blk + 1024 + slot * 4);
-  }
-  return f;
+// Hides a value's known bits from the optimiser so that byte-to-float conversions
+// of masked code bytes stay single v_cvt_f32_ubyteN instructions.
+__device__ inline unsigned opaque(unsigned v) {
+  asm("" : "+v"(v));
+  return v;
 }
 
-// bf16(q*s + b) for the 8 codes of octet i of a fragment, in reduction order.
+// bf16(q*s + b) for the 8 codes of octet i of a group, in reduction order.
+// q*s is exact in float32, so the fma rounds the exact q*s + b once.
 template <int BITS>
 __device__ inline bf16x8 deq_octet(const WFrag& f, int i) {
   unsigned lo, hi;
   if (BITS == 4) {
-    const unsigned d = f.c[i] ^ 0x88888888u;  // stored as q ^ 8
-    lo = d & 0x0F0F0F0Fu;
-    hi = (d >> 4) & 0x0F0F0F0Fu;
+    const unsigned d = (i < 4 ? f.c0[i & 3] : f.c1[i & 3]) ^ 0x88888888u;  // stored q ^ 8
+    lo = opaque(d & 0x0F0F0F0Fu);
+    hi = opaque((d >> 4) & 0x0F0F0F0Fu);
   } else {
-    const unsigned d = f.c[i >> 1] >> (2 * (i & 1));
-    lo = d & 0x03030303u;
-    hi = (d >> 4) & 0x03030303u;
+    const unsigned d = f.c0[i >> 1] >> (2 * (i & 1));
+    lo = opaque(d & 0x03030303u);
+    hi = opaque((d >> 4) & 0x03030303u);
   }
   const float s = bf16lo_to_f32(f.sb), b = bf16hi_to_f32(f.sb);
   const float w0 = fmaf((float)(lo & 0xFFu), s, b);
@@ -437,39 +464,6 @@ __device__ inline bf16x8 deq_octet(const WFrag& f, int i) {
   const float w7 = fmaf((float)(hi >> 24), s, b);
   u32x4 r = {pack_bf16(w0, w1), pack_bf16(w2, w3), pack_bf16(w4, w5), pack_bf16(w6, w7)};
   return __builtin_bit_cast(bf16x8, r);
-}
-
-// Activation rows of one m-tile, one reduction chunk: thread handles row
-// (tid >> 4) + 16 q for q < mt_valid, 16-byte segment tid & 15.
-struct AStage {
-  u32x4 v[kMT];
-};
-
-__device__ inline void load_astage(AStage& st, const uint16_t* const* rowp, int k0, int Kdim,
-                                   int mt_valid) {
-  const int seg = threadIdx.x & 15;
-  const bool ok = k0 + seg * 8 < Kdim;
-#pragma unroll
-  for (int q = 0; q < kMT; ++q) {
-    st.v[q] = u32x4{0u, 0u, 0u, 0u};
-    if (q < mt_valid && ok)
-      st.v[q] = *reinterpret_cast<const u32x4*>(rowp[q] + k0 + seg * 8);
-  }
-}
-
-__device__ inline void store_astage(const AStage& st, uint8_t* lds, int mt_valid) {
-  const int seg = threadIdx.x & 15, r = threadIdx.x >> 4;
-#pragma unroll
-  for (int q = 0; q < kMT; ++q)
-    if (q < mt_valid)
-      *reinterpret_cast<u32x4*>(lds + (r + 16 * q) * kArow + seg * 16) = st.v[q];
-}
-
-__device__ inline bf16x8 lds_afrag(const uint8_t* lds, int mt, int i) {
-  const int lane = threadIdx.x & 63;
-  const int row = 16 * mt + (lane & 15), kk = lane >> 4;
-  return __builtin_bit_cast(bf16x8,
-                            *reinterpret_cast<const u32x4*>(lds + row * kArow + kk * 64 + i * 16));
 }
 
 // Maps a workgroup to a work item so that each XCD (blockIdx % 8) takes a contiguous
@@ -488,194 +482,205 @@ __device__ inline const uint8_t* expert_base(const PArgs& a, int e) {
                  : a.shared + (size_t)(e - a.E) * a.geo.expert_bytes;
 }
 
-// ---------------------------------------------------------------------------
-// gate/up: one m-tile (<= 128 rows of one expert) x 64 intermediate columns.
-// Wave w owns columns j0 + 16w .. +15 of both gate and up.
-// ---------------------------------------------------------------------------
+// One work item as seen by one lane. Chunk ch of a lane's weight row starts 64*ch
+// bytes after wc (each code plane) and 4*ch words after wsb ((scale, bias)).
+struct Job {
+  int row0, nrows, K, nch;
+  const uint8_t* wc[2];    // codes of chunk 0 of this lane's row in each set
+  const unsigned* wsb[2];  // (scale, bias) word of chunk 0
+  unsigned sbmask;         // 0 where the lane's group lies beyond K (K < 256)
+  int col[2];              // output column of this lane in each set
+  bool on[2];              // the set has columns (wave-uniform)
+};
+
 template <int BITS>
-__global__ __launch_bounds__(256) void gateup_kernel(PArgs a) {
-  extern __shared__ uint8_t lds[];
-  const int NT = a.I / kGuCols;
-  const int item = work_item(a.tiles[0].x * NT);
-  if (item < 0) return;
-  const int4 td = a.tiles[1 + item / NT];
+__device__ inline void job_row(const Geo& g, const uint8_t* mat, int row, int P, int G, int kk,
+                               const uint8_t*& wc, const unsigned*& wsb) {
+  const int grp = kk < G ? kk : 0;
+  const uint8_t* blk = mat + (size_t)(row / P) * g.blk;
+  const int slot = (row % P) * G + grp;
+  wc = blk + slot * 16;  // 4-bit: plane 1 is 1024 bytes further
+  wsb = reinterpret_cast<const unsigned*>(blk + (BITS == 4 ? 2048 : 1024)) + slot;
+}
+
+template <int BITS, bool DOWN>
+__device__ inline bool make_job(const PArgs& a, const int4* list, Job& jb) {
+  const int NT = DOWN ? (a.H + kDnCols - 1) / kDnCols : a.I / kGuCols;
+  const int item = work_item(list[0].x * NT);
+  if (item < 0) return false;
+  const int4 td = list[1 + item / NT];
   const int nt = item % NT;
-  const int e = td.x, row0 = td.y, nrows = td.z;
-  const int mt_valid = (nrows + 15) >> 4;
-  const uint8_t* W = expert_base(a, e);
+  jb.row0 = td.y;
+  jb.nrows = td.z;
   const Geo& g = a.geo;
+  const uint8_t* W = expert_base(a, td.x);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kk = lane >> 4;
-  const int j = nt * kGuCols + wave * 16 + (lane & 15);
-  const uint8_t* blk_g = W + (size_t)(j / g.Ph) * g.blk;
-  const uint8_t* blk_u = W + g.off_up + (size_t)(j / g.Ph) * g.blk;
-  const int slot0 = (j % g.Ph) * g.Gh;
-
-  const uint16_t* rowp[kMT];
+  jb.K = DOWN ? a.I : a.H;
+  jb.nch = (jb.K + kKC2 - 1) / kKC2;
+  const int G = DOWN ? g.Gi : g.Gh;
+  jb.sbmask = kk < G ? 0xFFFFFFFFu : 0u;
+  if (!DOWN) {
+    const int j = nt * kGuCols + wave * 16 + (lane & 15);
+    job_row<BITS>(g, W, j, g.Ph, g.Gh, kk, jb.wc[0], jb.wsb[0]);
+    job_row<BITS>(g, W + g.off_up, j, g.Ph, g.Gh, kk, jb.wc[1], jb.wsb[1]);
+    jb.col[0] = jb.col[1] = j;
+    jb.on[0] = jb.on[1] = true;
+  } else {
+    const int base = nt * kDnCols + wave * 32;
 #pragma unroll
-  for (int q = 0; q < kMT; ++q) {
-    int r = (threadIdx.x >> 4) + 16 * q;
-    r = r < nrows ? r : nrows - 1;
-    rowp[q] = a.a + (size_t)a.rowtok[row0 + r] * a.H;
-  }
-  const int nch = (a.H + kKC - 1) / kKC;
-
-  f32x4 acc_g[kMT], acc_u[kMT];
-#pragma unroll
-  for (int q = 0; q < kMT; ++q) {
-    acc_g[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc_u[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  auto wload = [&](int ch, WFrag& fg, WFrag& fu) {
-    const int grp = 2 * ch + (kk >> 1);
-    const bool ok = ch < nch && grp < g.Gh;
-    fg = load_wfrag<BITS>(blk_g, slot0 + grp, kk & 1, ok);
-    fu = load_wfrag<BITS>(blk_u, slot0 + grp, kk & 1, ok);
-  };
-  WFrag g0, u0, g1, u1;
-  AStage st;
-  wload(0, g0, u0);
-  wload(1, g1, u1);
-  load_astage(st, rowp, 0, a.H, mt_valid);
-
-  auto chunk = [&](int ch, WFrag& fg, WFrag& fu) {
-    __syncthreads();
-    store_astage(st, lds, mt_valid);
-    __syncthreads();
-    if (ch + 1 < nch) load_astage(st, rowp, (ch + 1) * kKC, a.H, mt_valid);
-    const WFrag cg = fg, cu = fu;
-    wload(ch + 2, fg, fu);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x8 bg = deq_octet<BITS>(cg, i);
-      const bf16x8 bu = deq_octet<BITS>(cu, i);
-#pragma unroll
-      for (int q = 0; q < kMT; ++q) {
-        if (q < mt_valid) {
-          const bf16x8 af = lds_afrag(lds, q, i);
-          acc_g[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bg, acc_g[q], 0, 0, 0);
-          acc_u[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bu, acc_u[q], 0, 0, 0);
-        }
-      }
+    for (int s = 0; s < 2; ++s) {
+      jb.on[s] = base + 16 * s < a.H;
+      const int n = jb.on[s] ? base + 16 * s + (lane & 15) : 0;
+      jb.col[s] = n;
+      job_row<BITS>(g, W + g.off_down, n, g.Pi, g.Gi, kk, jb.wc[s], jb.wsb[s]);
     }
-  };
-  for (int ch = 0; ch < nch; ch += 2) {
-    chunk(ch, g0, u0);
-    if (ch + 1 < nch) chunk(ch + 1, g1, u1);
   }
+  return true;
+}
 
-  // epilogue: h = bf16(silu(g) * u) -> hbuf[row][j]
+// Weight fragments of chunk ch (clamped to the last chunk: loads past the end are
+// in bounds and their values are never used).
+template <int BITS>
+__device__ inline void load_wpair(const Job& jb, int ch, WFrag& f0, WFrag& f1) {
+  ch = ch < jb.nch ? ch : jb.nch - 1;
+  f0.c0 = *reinterpret_cast<const u32x4*>(jb.wc[0] + ch * 64);
+  f1.c0 = *reinterpret_cast<const u32x4*>(jb.wc[1] + ch * 64);
+  if (BITS == 4) {
+    f0.c1 = *reinterpret_cast<const u32x4*>(jb.wc[0] + 1024 + ch * 64);
+    f1.c1 = *reinterpret_cast<const u32x4*>(jb.wc[1] + 1024 + ch * 64);
+  } else {
+    f0.c1 = u32x4{0u, 0u, 0u, 0u};
+    f1.c1 = u32x4{0u, 0u, 0u, 0u};
+  }
+  f0.sb = jb.wsb[0][4 * ch];  // masked by the consumer: arithmetic on a prefetched
+  f1.sb = jb.wsb[1][4 * ch];  // value here would make the compiler wait for it early
+}
+
+template <bool DOWN>
+__device__ inline const uint16_t* a_row(const PArgs& a, const Job& jb, int r) {
+  r = r < jb.nrows ? r : jb.nrows - 1;
+  return DOWN ? a.hbuf + (size_t)(jb.row0 + r) * a.I
+              : a.a + (size_t)a.rowtok[jb.row0 + r] * a.H;
+}
+
+// Activations of chunk ch for one LDS stage. A stage holds MT subtiles of 32
+// (kk, i) pieces x 16 rows x 16 B; thread t moves pieces t + 256 v, v < 2 MT:
+// row m = t & 15 of subtile v >> 1, piece c = (t >> 4) + 16 (v & 1). Positions
+// past K (K < 256) re-read the row start: those products meet zero weights.
+template <int MT>
+struct AStage {
+  u32x4 v[2 * MT];
+};
+
+template <int MT>
+__device__ inline void load_achunk(AStage<MT>& st, const uint16_t* const* rowp, int ch, int K,
+                                   int mt_valid) {
 #pragma unroll
-  for (int q = 0; q < kMT; ++q) {
-    if (q < mt_valid) {
+  for (int v = 0; v < 2 * MT; ++v) {
+    if ((v >> 1) >= mt_valid) continue;
+    const int c = (threadIdx.x >> 4) + 16 * (v & 1);
+    int k = ch * kKC2 + 64 * (c >> 3) + 8 * (c & 7);
+    k = k < K ? k : 8 * (c & 7);
+    st.v[v] = *reinterpret_cast<const u32x4*>(rowp[v >> 1] + k);
+  }
+}
+
+template <int MT>
+__device__ inline void store_achunk(const AStage<MT>& st, uint8_t* stage, int mt_valid) {
+  const int m = threadIdx.x & 15;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 16 * q + 4 * kk + r;
-        if (m < nrows) {
-          const float gv = acc_g[q][r], uv = acc_u[q][r];
-          const float h = gv / (1.f + __expf(-gv)) * uv;
-          a.hbuf[(size_t)(row0 + m) * a.I + j] = (uint16_t)(pack_bf16(h, 0.f) & 0xFFFFu);
-        }
-      }
+  for (int v = 0; v < 2 * MT; ++v) {
+    if ((v >> 1) >= mt_valid) continue;
+    const int c = (threadIdx.x >> 4) + 16 * (v & 1);
+    *reinterpret_cast<u32x4*>(stage + (v >> 1) * kSubBytes + c * 256 + m * 16) = st.v[v];
+  }
+}
+
+__device__ inline bf16x8 lds_afrag(const uint8_t* stage, int q, int i) {
+  const int lane = threadIdx.x & 63;
+  const int kk = lane >> 4, m = lane & 15;
+  return __builtin_bit_cast(
+      bf16x8, *reinterpret_cast<const u32x4*>(stage + q * kSubBytes + (kk * 8 + i) * 256 + m * 16));
+}
+
+// Results of rows mbase..mbase+3 (this lane's C rows of one MFMA subtile).
+template <bool DOWN>
+__device__ inline void store_rows(const PArgs& a, const Job& jb, const f32x4& c0, const f32x4& c1,
+                                  int mbase) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = mbase + r;
+    if (m >= jb.nrows) continue;
+    if (!DOWN) {
+      const float gv = c0[r], uv = c1[r];
+      const float h = gv / (1.f + __expf(-gv)) * uv;
+      a.hbuf[(size_t)(jb.row0 + m) * a.I + jb.col[0]] = (uint16_t)(pack_bf16(h, 0.f) & 0xFFFFu);
+    } else {
+      float* orow = a.obuf + (size_t)(jb.row0 + m) * a.H;
+      if (jb.on[0]) orow[jb.col[0]] = c0[r];
+      if (jb.on[1]) orow[jb.col[1]] = c1[r];
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// down: one m-tile x 128 output columns; wave w owns columns n0 + 32w .. +31
-// (two 16-column MFMA tiles).
-// ---------------------------------------------------------------------------
-template <int BITS>
-__global__ __launch_bounds__(256) void down_kernel(PArgs a) {
+template <int BITS, bool DOWN, int MT>
+__global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
   extern __shared__ uint8_t lds[];
-  const int NT = (a.H + kDnCols - 1) / kDnCols;
-  const int item = work_item(a.tiles[0].x * NT);
-  if (item < 0) return;
-  const int4 td = a.tiles[1 + item / NT];
-  const int nt = item % NT;
-  const int e = td.x, row0 = td.y, nrows = td.z;
-  const int mt_valid = (nrows + 15) >> 4;
-  const uint8_t* W = expert_base(a, e) + a.geo.off_down;
-  const Geo& g = a.geo;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kk = lane >> 4;
-  const int nA = nt * kDnCols + wave * 32 + (lane & 15);
-  const int nB = nA + 16;
-  const bool wave_on = nt * kDnCols + wave * 32 < a.H;  // wave-uniform
-  const bool bon = wave_on && nt * kDnCols + wave * 32 + 16 < a.H;
-  const uint8_t* blk_a = W + (size_t)((wave_on ? nA : 0) / g.Pi) * g.blk;
-  const uint8_t* blk_b = W + (size_t)((bon ? nB : 0) / g.Pi) * g.blk;
-  const int slot_a = ((wave_on ? nA : 0) % g.Pi) * g.Gi;
-  const int slot_b = ((bon ? nB : 0) % g.Pi) * g.Gi;
-
-  const uint16_t* rowp[kMT];
+  Job jb;
+  if (!make_job<BITS, DOWN>(a, MT == 1 ? a.thin : a.thick, jb)) return;
+  const int mt_valid = (jb.nrows + 15) >> 4;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* rowp[MT];
 #pragma unroll
-  for (int q = 0; q < kMT; ++q) {
-    int r = (threadIdx.x >> 4) + 16 * q;
-    r = r < nrows ? r : nrows - 1;
-    rowp[q] = a.hbuf + (size_t)(row0 + r) * a.I;
+  for (int q = 0; q < MT; ++q) rowp[q] = a_row<DOWN>(a, jb, 16 * q + (threadIdx.x & 15));
+  const int nch = jb.nch;
+  f32x4 acc0[MT], acc1[MT];
+#pragma unroll
+  for (int q = 0; q < MT; ++q) {
+    acc0[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int nch = (a.I + kKC - 1) / kKC;
+  // activations: LDS stage ch & 1 holds chunk ch, chunk ch + 1 is in registers;
+  // weights: chunks ch and ch + 1 in registers, ch + 2 requested during chunk ch
+  AStage<MT> st;
+  WFrag p0, p1, r0, r1;
+  load_achunk<MT>(st, rowp, 0, jb.K, mt_valid);
+  load_wpair<BITS>(jb, 0, p0, p1);
+  load_wpair<BITS>(jb, 1, r0, r1);
+  store_achunk<MT>(st, lds, mt_valid);
 
-  f32x4 acc_a[kMT], acc_b[kMT];
+  auto chunk = [&](int ch, WFrag& f0, WFrag& f1) {
+    const uint8_t* cur = lds + (ch & 1) * (MT * kSubBytes);
+    uint8_t* nxt = lds + ((ch + 1) & 1) * (MT * kSubBytes);
+    __syncthreads();  // stage cur is written; stage nxt is no longer read
+    if (ch + 1 < nch) load_achunk<MT>(st, rowp, ch + 1, jb.K, mt_valid);
+    WFrag c0 = f0, c1 = f1;
+    load_wpair<BITS>(jb, ch + 2, f0, f1);
+    c0.sb &= jb.sbmask;
+    c1.sb &= jb.sbmask;
 #pragma unroll
-  for (int q = 0; q < kMT; ++q) {
-    acc_a[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc_b[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  auto wload = [&](int ch, WFrag& fa, WFrag& fb) {
-    const int grp = 2 * ch + (kk >> 1);
-    const bool ok = ch < nch && grp < g.Gi;
-    fa = load_wfrag<BITS>(blk_a, slot_a + grp, kk & 1, ok && wave_on);
-    fb = load_wfrag<BITS>(blk_b, slot_b + grp, kk & 1, ok && bon);
-  };
-  WFrag a0, b0, a1, b1;
-  AStage st;
-  wload(0, a0, b0);
-  wload(1, a1, b1);
-  load_astage(st, rowp, 0, a.I, mt_valid);
-
-  auto chunk = [&](int ch, WFrag& fa, WFrag& fb) {
-    __syncthreads();
-    store_astage(st, lds, mt_valid);
-    __syncthreads();
-    if (ch + 1 < nch) load_astage(st, rowp, (ch + 1) * kKC, a.I, mt_valid);
-    const WFrag ca = fa, cb = fb;
-    wload(ch + 2, fa, fb);
-    if (!wave_on) return;
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8 b0 = deq_octet<BITS>(c0, i);
+      const bf16x8 b1 = deq_octet<BITS>(c1, i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x8 ba = deq_octet<BITS>(ca, i);
-      const bf16x8 bb = deq_octet<BITS>(cb, i);
-#pragma unroll
-      for (int q = 0; q < kMT; ++q) {
+      for (int q = 0; q < MT; ++q) {
         if (q < mt_valid) {
-          const bf16x8 af = lds_afrag(lds, q, i);
-          acc_a[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ba, acc_a[q], 0, 0, 0);
-          acc_b[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bb, acc_b[q], 0, 0, 0);
+          const bf16x8 af = lds_afrag(cur, q, i);
+          acc0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b0, acc0[q], 0, 0, 0);
+          acc1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b1, acc1[q], 0, 0, 0);
         }
       }
     }
+    if (ch + 1 < nch) store_achunk<MT>(st, nxt, mt_valid);
   };
   for (int ch = 0; ch < nch; ch += 2) {
-    chunk(ch, a0, b0);
-    if (ch + 1 < nch) chunk(ch + 1, a1, b1);
+    chunk(ch, p0, p1);
+    if (ch + 1 < nch) chunk(ch + 1, r0, r1);
   }
-  if (!wave_on) return;
 #pragma unroll
-  for (int q = 0; q < kMT; ++q) {
-    if (q < mt_valid) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 16 * q + 4 * kk + r;
-        if (m < nrows) {
-          float* orow = a.obuf + (size_t)(row0 + m) * a.H;
-          orow[nA] = acc_a[q][r];
-          if (bon) orow[nB] = acc_b[q][r];
-        }
-      }
-    }
-  }
+  for (int q = 0; q < MT; ++q)
+    if (q < mt_valid) store_rows<DOWN>(a, jb, acc0[q], acc1[q], 16 * q + 4 * (lane >> 4));
 }
 
 // ---------------------------------------------------------------------------
@@ -750,7 +755,8 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
   a.wts = reinterpret_cast<float*>(ws + pl.wts);
   a.pos = reinterpret_cast<int*>(ws + pl.pos);
   a.rowtok = reinterpret_cast<int*>(ws + pl.rowtok);
-  a.tiles = reinterpret_cast<int4*>(ws + pl.tiles);
+  a.thin = reinterpret_cast<int4*>(ws + pl.thin);
+  a.thick = reinterpret_cast<int4*>(ws + pl.thick);
   a.hbuf = reinterpret_cast<uint16_t*>(ws + pl.hbuf);
   a.obuf = reinterpret_cast<float*>(ws + pl.obuf);
 
@@ -768,7 +774,6 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
   }
 
   hipLaunchKernelGGL(clear_err, dim3(1), dim3(64), 0, stream, a.err);
-  const size_t lds_ab = (size_t)kBM * kArow;
   for (int t0 = 0; t0 < T; t0 += pl.Tc) {
     const int n = T - t0 < pl.Tc ? T - t0 : pl.Tc;
     a.n = n;
@@ -787,20 +792,33 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
     const int n2 = next_pow2(n * c.top_k < 2 ? 2 : n * c.top_k);
     const size_t glds = sizeof(unsigned) * ((size_t)n2 + 2 * c.n_experts + 1024);
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), glds, stream, a, n2);
-    // grids: an upper bound of the m-tiles this pass can have, rounded to whole XCDs
+    // grids: upper bounds of the m-tiles this pass can have, rounded to whole XCDs.
+    // Every expert has at most one thin tile; a thick tile has at least 17 rows.
     const int TK = n * c.top_k;
     const int nz = c.n_experts < TK ? c.n_experts : TK;
-    const int tiles_max = nz + (TK + kBM - 1) / kBM + c.n_shared * ((n + kBM - 1) / kBM);
-    const int gu_items = tiles_max * (c.inter / kGuCols);
-    const int dn_items = tiles_max * ((c.hidden + kDnCols - 1) / kDnCols);
-    const unsigned gu_grid = (unsigned)(8 * ((gu_items + 7) / 8));
-    const unsigned dn_grid = (unsigned)(8 * ((dn_items + 7) / 8));
+    const int thin_max = nz + c.n_shared;
+    const int thick_max = TK / 17 + c.n_shared * (n / 17);
+    const int nt_gu = c.inter / kGuCols, nt_dn = (c.hidden + kDnCols - 1) / kDnCols;
+    auto grid = [](int items) { return dim3((unsigned)(8 * ((items + 7) / 8))); };
+    const size_t lds_thin = 2 * kSubBytes, lds_thick = 2 * kThickMT * kSubBytes;
     if (c.bits == 4) {
-      hipLaunchKernelGGL(gateup_kernel<4>, dim3(gu_grid), dim3(256), lds_ab, stream, a);
-      hipLaunchKernelGGL(down_kernel<4>, dim3(dn_grid), dim3(256), lds_ab, stream, a);
+      hipLaunchKernelGGL((gemm_grouped<4, false, 1>), grid(thin_max * nt_gu), dim3(256), lds_thin, stream, a);
+      if (thick_max > 0)
+        hipLaunchKernelGGL((gemm_grouped<4, false, kThickMT>), grid(thick_max * nt_gu), dim3(256),
+                           lds_thick, stream, a);
+      hipLaunchKernelGGL((gemm_grouped<4, true, 1>), grid(thin_max * nt_dn), dim3(256), lds_thin, stream, a);
+      if (thick_max > 0)
+        hipLaunchKernelGGL((gemm_grouped<4, true, kThickMT>), grid(thick_max * nt_dn), dim3(256),
+                           lds_thick, stream, a);
     } else {
-      hipLaunchKernelGGL(gateup_kernel<2>, dim3(gu_grid), dim3(256), lds_ab, stream, a);
-      hipLaunchKernelGGL(down_kernel<2>, dim3(dn_grid), dim3(256), lds_ab, stream, a);
+      hipLaunchKernelGGL((gemm_grouped<2, false, 1>), grid(thin_max * nt_gu), dim3(256), lds_thin, stream, a);
+      if (thick_max > 0)
+        hipLaunchKernelGGL((gemm_grouped<2, false, kThickMT>), grid(thick_max * nt_gu), dim3(256),
+                           lds_thick, stream, a);
+      hipLaunchKernelGGL((gemm_grouped<2, true, 1>), grid(thin_max * nt_dn), dim3(256), lds_thin, stream, a);
+      if (thick_max > 0)
+        hipLaunchKernelGGL((gemm_grouped<2, true, kThickMT>), grid(thick_max * nt_dn), dim3(256),
+                           lds_thick, stream, a);
     }
     const size_t nthreads = (size_t)n * (c.hidden / 4);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
