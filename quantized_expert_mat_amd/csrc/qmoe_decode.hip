@@ -52,6 +52,11 @@ constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an int
 constexpr int kMaxPass = kMaxK + kMaxShared;
 constexpr int kBatch = 4;              // items whose loads are issued before the first is reduced
 constexpr int kMaxLdsBytes = 160 * 1024;
+constexpr int kLdsLayers = 256;        // layer-table entries kept in LDS
+// The flash-moe layer shape as compile-time constants (hidden 4096, intermediate
+// 1024, 512 experts, top-4 + 1 shared, 256 workgroups): with these the compiler
+// folds every index computation and drops the guards the general shapes need.
+constexpr int kSpecH = 4096, kSpecI = 1024, kSpecE = 512, kSpecK = 4, kSpecS = 1, kSpecNwg = 256;
 
 enum Mode { MODE_LAYER = 0, MODE_ROUTE = 1, MODE_EXPERT = 2 };
 
@@ -85,16 +90,21 @@ struct DecodeArgs {
   int rpw;                       // phase C output rows per workgroup
   int npass;
   int pass_first[kMaxPass], pass_count[kMaxPass];
-  int pf;                        // 1: router / shared weights are prefetched into LDS tiles
-  int pf_down;                   // 1: down blocks are prefetched into LDS
-  int nbd;                       // down blocks per list entry in the down tile
-  int lds_xn, lds_xdig, lds_xsum, lds_hdig, lds_hsum, lds_acc, lds_xres, lds_tile_a, lds_tile_sh,
-      lds_tile_c;
+  int pre_router;                // router rows of a workgroup fit the register prefetch
+  int pre_shared;                // shared gate/up items of a workgroup fit it
+  int pre_down;                  // phase-C down slots of every wave fit it
+  int poll_sleep;                // pause between poll rounds, in units of 64 clocks
+  int lds_xn, lds_xdig, lds_xsum, lds_hdig, lds_hsum, lds_acc, lds_xres;
+  int lds_layers;  // LDS copy of the layer table (n_lds_layers entries)
+  int n_lds_layers;
+  int const_pass;  // 1: read the pass table from these arguments (compile-time constants)
   int lds_words;
 };
 
 // Small per-workgroup state kept in LDS across phases.
 struct Small {
+  int pass_first[kMaxPass], pass_count[kMaxPass];  // copies of the kernel arguments
+  int pass_lgn[kMaxPass];                          // log2(pass_count)
   float redf[kNW][kMaxPass + 2];
   int sel_idx[kMaxK];
   float sel_w[kMaxK];
@@ -118,9 +128,7 @@ struct Lds {
   float* acc;
   float* xres;       // this workgroup's rows of the (pre-norm) layer input
   float* hstage;     // phase C: h vectors (aliases xn and xdig, dead by then)
-  uint8_t* tile_a;   // router rows of this workgroup
-  uint8_t* tile_sh;  // shared-expert gate/up items of this workgroup
-  uint8_t* tile_c;   // down blocks of this workgroup, per expert list entry
+  unsigned lt;       // LDS byte address of the layer table copy
 };
 
 __device__ inline Lds lds_view(unsigned* raw, const DecodeArgs& a) {
@@ -134,10 +142,39 @@ __device__ inline Lds lds_view(unsigned* raw, const DecodeArgs& a) {
   s.acc = reinterpret_cast<float*>(raw + a.lds_acc);
   s.xres = reinterpret_cast<float*>(raw + a.lds_xres);
   s.hstage = reinterpret_cast<float*>(raw + a.lds_xn);
-  s.tile_a = reinterpret_cast<uint8_t*>(raw + a.lds_tile_a);
-  s.tile_sh = reinterpret_cast<uint8_t*>(raw + a.lds_tile_sh);
-  s.tile_c = reinterpret_cast<uint8_t*>(raw + a.lds_tile_c);
+  s.lt = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned*)(raw + a.lds_layers);
   return s;
+}
+
+// Layer l's weight pointers. Kept in LDS (copied at kernel start) where they fit:
+// reading them there waits only on the LDS counter, whereas a global load of the
+// table would make the compiler wait for every load issued before it, prefetches
+// included.
+__device__ inline LayerPtrs get_layer(const DecodeArgs& a, const Lds& s, int l) {
+  LayerPtrs p;
+  if (l < a.n_lds_layers) {
+    typedef __attribute__((address_space(3))) const unsigned long long lds_u64;
+    lds_u64* q = (lds_u64*)(uintptr_t)(s.lt + (unsigned)l * (unsigned)sizeof(LayerPtrs));
+    p.experts = reinterpret_cast<const uint8_t*>(q[0]);
+    p.shared = reinterpret_cast<const uint8_t*>(q[1]);
+    p.router = reinterpret_cast<const float*>(q[2]);
+    p.gamma = reinterpret_cast<const float*>(q[3]);
+  } else {
+    p = a.layers[l];
+  }
+  return p;
+}
+
+// Pass table entries: constants in the specialised kernel (pass 0 = the K routed
+// experts, pass 1 = the shared expert), else the LDS copy.
+__device__ inline int pass_first_of(const DecodeArgs& a, const Lds& s, int pi) {
+  return a.const_pass ? (pi == 0 ? 0 : kSpecK) : s.sm->pass_first[pi];
+}
+__device__ inline int pass_count_of(const DecodeArgs& a, const Lds& s, int pi) {
+  return a.const_pass ? (pi == 0 ? kSpecK : kSpecS) : s.sm->pass_count[pi];
+}
+__device__ inline int pass_lgn_of(const DecodeArgs& a, const Lds& s, int pi) {
+  return a.const_pass ? (pi == 0 ? log2i(kSpecK) : log2i(kSpecS)) : s.sm->pass_lgn[pi];
 }
 
 __device__ inline void split_range(int n, int parts, int p, int& b, int& e) {
@@ -160,6 +197,14 @@ __device__ inline int ld_coh(const int* p) {
 }
 // Wait until this wave's outstanding memory operations (stores included) are done.
 __device__ inline void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Issue-order point: memory operations are not moved across it by the compiler, so
+// prefetches stay where they are written (behind the loads they must not delay, and
+// ahead of the waits they should overlap). Emits no instruction.
+__device__ inline void issue_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 constexpr int kCachePolicySC1 = 16;           // device-coherent (bypasses non-coherent caches)
@@ -191,6 +236,13 @@ __device__ inline void xput(const Xv& x, int i, float v, unsigned epoch) {
 }
 
 __device__ __forceinline__ bool poll_abort(const DecodeArgs& a, unsigned long long t0, int lane0);
+
+// Pause between two polls of data that has not arrived: a workgroup that is done
+// early would otherwise re-read its inputs back to back and take memory bandwidth
+// from the workgroups still streaming weights.
+__device__ inline void poll_pause(const DecodeArgs& a) {
+  for (int i = 0; i < a.poll_sleep; ++i) __builtin_amdgcn_s_sleep(1);
+}
 
 // Wait until every pair of this workgroup's replica carries `epoch` and copy the
 // values into LDS (dst[i]). All threads take part; each polls its own chunks.
@@ -226,6 +278,7 @@ __device__ __forceinline__ bool xget(const DecodeArgs& a, const Xv& x, float* ds
         ok = false;
         break;
       }
+      poll_pause(a);
 #pragma unroll
       for (int k = 0; k < kPer; ++k)
         if (pending & (1u << k)) v[k] = ld_coh4(r, (base + (int)threadIdx.x + k * kThreads) * 16);
@@ -431,6 +484,21 @@ typedef __attribute__((address_space(3))) const unsigned lds_u32;
 
 __device__ inline uint4 to_uint4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
+// Loads through global-address-space pointers. Weight pointers come from a table in
+// memory, so the compiler cannot prove they are global and would emit flat loads,
+// which also count against the LDS wait counter: every later LDS wait would then
+// wait for them too, and a prefetch would stall the phase it is meant to overlap.
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u gl_v4u;
+typedef __attribute__((address_space(1))) const unsigned gl_u32;
+typedef __attribute__((address_space(1))) const v4f gl_v4f;
+__device__ inline uint4 ldg_u4(const void* p) { return to_uint4(*(gl_v4u*)(uintptr_t)p); }
+__device__ inline unsigned ldg_u32(const void* p) { return *(gl_u32*)(uintptr_t)p; }
+__device__ inline float4 ldg_f4(const void* p) {
+  const v4f v = *(gl_v4f*)(uintptr_t)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // blk points to global memory, or (in_lds) to an LDS copy of the block.
 template <int BITS>
 __device__ inline Slot ld_slot(const uint8_t* blk, int slot, bool in_lds) {
@@ -448,13 +516,13 @@ __device__ inline Slot ld_slot(const uint8_t* blk, int slot, bool in_lds) {
     }
     return s;
   }
-  s.c0 = reinterpret_cast<const uint4*>(blk)[slot];
+  s.c0 = ldg_u4(blk + slot * 16);
   if (BITS == 4) {
-    s.c1 = reinterpret_cast<const uint4*>(blk + 1024)[slot];
-    s.sb = reinterpret_cast<const unsigned*>(blk + 2048)[slot];
+    s.c1 = ldg_u4(blk + 1024 + slot * 16);
+    s.sb = ldg_u32(blk + 2048 + slot * 4);
   } else {
     s.c1 = make_uint4(0, 0, 0, 0);
-    s.sb = reinterpret_cast<const unsigned*>(blk + 1024)[slot];
+    s.sb = ldg_u32(blk + 1024 + slot * 4);
   }
   return s;
 }
@@ -495,19 +563,6 @@ __device__ inline float slot_dot(const Slot& s, const Dig& D) {
 
 __device__ inline float silu(float z) { return z / (1.f + expf(-z)); }
 
-// ------------------------------------------------------------ LDS prefetch
-// Copy `bytes` (multiple of 16) from global memory into LDS with the direct
-// global->LDS path, 1 KB per wave instruction, using waves [w0, kNW).
-__device__ inline void dma_to_lds(uint8_t* lds, const uint8_t* g, int bytes, int w0) {
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  if (w < w0) return;
-  for (int c = (w - w0) * 1024; c < bytes; c += (kNW - w0) * 1024) {
-    if (c + lane * 16 < bytes)
-      __builtin_amdgcn_global_load_lds(g + c + lane * 16,
-                                       (__attribute__((address_space(3))) void*)(lds + c), 16, 0, 0);
-  }
-}
-
 // ------------------------------------------------------------ abort / time-out
 // Every wait is bounded: after timeout_ticks a waiter raises the abort flag and the
 // device error, and every waiter that sees the flag gives up, so all workgroups
@@ -546,7 +601,7 @@ __device__ inline Xv xv_h(const DecodeArgs& a) {
 // rows this workgroup combines in phase C are kept for the residual.
 __device__ __forceinline__ bool prepare_x(const DecodeArgs& a, const Lds& s, int t, int l) {
   const int H = a.geo.H;
-  const float* gamma = a.mode == MODE_EXPERT ? nullptr : a.layers[l].gamma;
+  const float* gamma = a.mode == MODE_EXPERT ? nullptr : get_layer(a, s, l).gamma;
   const bool norm = a.mode != MODE_EXPERT && (a.flags & MOE_F_RMSNORM);
   bool ok = true;
   if (a.mode == MODE_LAYER && l > 0) {
@@ -612,33 +667,37 @@ __device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, 
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   if (i0 + w >= i1) {
+    issue_order();
     after_issue();
+    issue_order();
     return;
   }
   const Xv hxv = xv_h(a);
-  const int p = lane / g.Gh, grp = lane % g.Gh;
+  const int p = lane >> g.lGh, grp = lane & (g.Gh - 1);
   Dig D;
   load_dig(D, s.xdig, s.xsum, grp, s.sm->xs_x);
   bool first = true;
   for (int ib = i0 + w; ib < i1; ib += kBatch * kNW) {
     Slot G[kBatch], U[kBatch];
     int hv[kBatch], row[kBatch];
+    // loads are issued unconditionally (items past the range re-read the wave's
+    // first item and are not reduced): straight-line loads let the compiler wait
+    // for exactly the item it reduces next
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int i = ib + j * kNW;
-      hv[j] = -1;
-      row[j] = 0;
-      if (i < i1) {
-        const uint8_t *gb, *ub;
-        int row0;
-        src(i, gb, ub, hv[j], row0);
-        G[j] = ld_slot<BITS>(gb, lane, in_lds);
-        U[j] = ld_slot<BITS>(ub, lane, in_lds);
-        row[j] = row0 + p;
-      }
+      const uint8_t *gb, *ub;
+      int row0, hvec;
+      src(i < i1 ? i : i0 + w, gb, ub, hvec, row0);
+      G[j] = ld_slot<BITS>(gb, lane, in_lds);
+      U[j] = ld_slot<BITS>(ub, lane, in_lds);
+      hv[j] = i < i1 ? hvec : -1;
+      row[j] = row0 + p;
     }
     if (first) {
+      issue_order();
       after_issue();
+      issue_order();
       first = false;
     }
 #pragma unroll
@@ -652,13 +711,11 @@ __device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, 
 }
 
 // Router logits for rows [e0, e1) of this workgroup; row e - e0 on wave (e - e0) % kNW.
-__device__ __forceinline__ void router_rows(const DecodeArgs& a, const Lds& s, int t, int l, int e0, int e1,
-                            bool from_tile) {
+__device__ __forceinline__ void router_rows(const DecodeArgs& a, const Lds& s, int t, int l, int e0, int e1) {
   const int H = a.geo.H, E = a.E;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   if (e0 + w >= e1) return;
-  const float* W =
-      from_tile ? reinterpret_cast<const float*>(s.tile_a) : a.layers[l].router + (size_t)e0 * H;
+  const float* W = get_layer(a, s, l).router + (size_t)e0 * H;
   const int nq = H / 4;  // float4 columns
   constexpr int kMaxC = kMaxDim / 256;
   float4 xr[kMaxC];
@@ -673,7 +730,7 @@ __device__ __forceinline__ void router_rows(const DecodeArgs& a, const Lds& s, i
 #pragma unroll
     for (int c = 0; c < kMaxC; ++c) {
       const int q = lane + kWave * c;
-      wv[c] = q < nq ? row[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      wv[c] = q < nq ? ldg_f4(row + q) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float acc = 0.f;
 #pragma unroll
@@ -693,52 +750,161 @@ __device__ __forceinline__ void router_rows(const DecodeArgs& a, const Lds& s, i
   }
 }
 
-// Prefetch (into LDS) the router rows and shared gate/up items that phase A of
-// layer l will use, on waves [w0, kNW).
-__device__ __forceinline__ void prefetch_a(const DecodeArgs& a, const Lds& s, int l, int w0) {
+// ------------------------------------------------------------ register prefetch
+// Weights a phase needs are requested early, into the registers of the lanes that
+// will consume them, so their HBM latency overlaps an exchange wait instead of
+// following it: the next layer's router rows and shared gate/up slots right after
+// this layer's combine (they land while x is being exchanged), and the down slots
+// of phase C right after the routed gate/up loads of phase B (they land while h
+// is being exchanged). Plain loads keep the compiler's wait counts exact.
+constexpr int kRouterPre = 8;  // float4 of router rows per thread
+constexpr int kRowsPre = 4;    // router rows per workgroup on the prefetch path
+constexpr int kShPre = 1;      // shared gate/up items per wave
+constexpr int kDnPre = 5;      // down slots per lane
+
+struct StaticPre {
+  float4 r[kRouterPre];
+  Slot g[kShPre], u[kShPre];
+};
+
+struct DownPre {
+  Slot d[kDnPre];
+};
+
+// Router rows of this workgroup (float4 q = tid + kThreads*i of rows [e0, e1)) and
+// its shared gate/up items (item i0 + w + kNW*j on wave w) for layer l.
+template <int BITS>
+__device__ __forceinline__ void load_static(const DecodeArgs& a, const Lds& s, int l, StaticPre& sp) {
   const Geo& g = a.geo;
-  int e0, e1;
-  split_range(a.E, a.nwg, blockIdx.x, e0, e1);
-  dma_to_lds(s.tile_a, reinterpret_cast<const uint8_t*>(a.layers[l].router + (size_t)e0 * g.H),
-             (e1 - e0) * g.H * 4, w0);
-  if (a.S > 0) {
+  const LayerPtrs lp = get_layer(a, s, l);
+  if (a.pre_router) {
+    int e0, e1;
+    split_range(a.E, a.nwg, blockIdx.x, e0, e1);
+    const int nq = (e1 - e0) * (g.H / 4);
+    const float4* W = reinterpret_cast<const float4*>(lp.router + (size_t)e0 * g.H);
+#pragma unroll
+    for (int i = 0; i < kRouterPre; ++i) {
+      const int q = (int)threadIdx.x + kThreads * i;
+      sp.r[i] = ldg_f4(W + (q < nq ? q : 0));  // unconditional: exact wait counts
+    }
+  }
+  if (a.pre_shared) {
     int i0, i1;
     split_range(a.S * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
-    for (int i = i0; i < i1; ++i) {
-      const uint8_t* ex = a.layers[l].shared + (size_t)(i / g.nblk_gu) * g.expert_bytes +
-                          (size_t)(i % g.nblk_gu) * g.blk;
-      dma_to_lds(s.tile_sh + (size_t)(i - i0) * 2 * g.blk, ex, g.blk, w0);
-      dma_to_lds(s.tile_sh + (size_t)((i - i0) * 2 + 1) * g.blk, ex + g.off_up, g.blk, w0);
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const uint8_t* shared = lp.shared;
+#pragma unroll
+    for (int j = 0; j < kShPre; ++j) {
+      const int i0w = i0 + w + j * kNW;
+      const int i = i0w < i1 ? i0w : 0;  // unconditional: exact wait counts
+      const uint8_t* gb = shared + (size_t)(i >> g.lnb) * g.expert_bytes +
+                          (size_t)(i & (g.nblk_gu - 1)) * g.blk;
+      sp.g[j] = ld_slot<BITS>(gb, lane, false);
+      sp.u[j] = ld_slot<BITS>(gb + g.off_up, lane, false);
+    }
+  }
+}
+
+// Router logits of rows [e0, e1) from prefetched weights and x_n in LDS.
+__device__ __forceinline__ void router_from_regs(const DecodeArgs& a, const Lds& s, int t, int l,
+                                                 const StaticPre& sp) {
+  const int H = a.geo.H, h4 = H / 4;
+  int e0, e1;
+  split_range(a.E, a.nwg, blockIdx.x, e0, e1);
+  const int nr = e1 - e0;
+  float acc[kRowsPre];
+#pragma unroll
+  for (int j = 0; j < kRowsPre; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRouterPre; ++i) {
+    const int q = (int)threadIdx.x + kThreads * i;
+    if (q < nr * h4) {
+      const int row = q / h4;
+      const float4 xv = reinterpret_cast<const float4*>(s.xn)[q - row * h4];
+      float d = sp.r[i].x * xv.x;
+      d = fmaf(sp.r[i].y, xv.y, d);
+      d = fmaf(sp.r[i].z, xv.z, d);
+      d = fmaf(sp.r[i].w, xv.w, d);
+#pragma unroll
+      for (int j = 0; j < kRowsPre; ++j) acc[j] += row == j ? d : 0.f;
+    }
+  }
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+#pragma unroll
+  for (int j = 0; j < kRowsPre; ++j) {
+    if (j < nr) {
+      const float v = wave_sum(acc[j]);
+      if (lane == 0) s.sm->redf[w][j] = v;
+    }
+  }
+  __syncthreads();
+  const int j = (int)threadIdx.x / kRep, rep = (int)threadIdx.x % kRep;
+  if (j < nr) {
+    float v = 0.f;
+    for (int i = 0; i < kNW; ++i) v += s.sm->redf[i][j];
+    const int e = e0 + j;
+    const unsigned long long pv = ((unsigned long long)epoch_of(a, t, l) << 32) | __float_as_uint(v);
+    __hip_atomic_store(a.lx + (size_t)rep * a.e_pad + e, pv, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (rep == 0 && a.logits_out) a.logits_out[(size_t)t * a.E + e] = v;
+  }
+}
+
+// Shared gate/up + SwiGLU from prefetched slots (same items and outputs as the
+// direct path in phase A).
+template <int BITS>
+__device__ __forceinline__ void shared_from_regs(const DecodeArgs& a, const Lds& s, int t, int l,
+                                                 const StaticPre& sp) {
+  const Geo& g = a.geo;
+  int i0, i1;
+  split_range(a.S * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  if (i0 + w >= i1) return;
+  const Xv hxv = xv_h(a);
+  const int p = lane >> g.lGh, grp = lane & (g.Gh - 1);
+  Dig D;
+  load_dig(D, s.xdig, s.xsum, grp, s.sm->xs_x);
+  const unsigned epoch = epoch_of(a, t, l);
+#pragma unroll
+  for (int j = 0; j < kShPre; ++j) {
+    const int i = i0 + w + j * kNW;
+    if (i < i1) {
+      const float pg = seg_sum(slot_dot<BITS>(sp.g[j], D), g.Gh);
+      const float pu = seg_sum(slot_dot<BITS>(sp.u[j], D), g.Gh);
+      const int row = ((i & (g.nblk_gu - 1)) << g.lPh) + p;
+      if (grp == 0 && row < g.I) xput(hxv, (a.K + (i >> g.lnb)) * g.I + row, silu(pg) * pu, epoch);
     }
   }
 }
 
 template <int BITS>
-__device__ __forceinline__ bool phase_a(const DecodeArgs& a, const Lds& s, int t, int l, bool tiles) {
+__device__ __forceinline__ bool phase_a(const DecodeArgs& a, const Lds& s, int t, int l,
+                                        StaticPre& sp, bool preloaded) {
   const Geo& g = a.geo;
+  if (!preloaded) load_static<BITS>(a, s, l, sp);
   if (!prepare_x(a, s, t, l)) return false;
   SUBSTAMP(8);
   int e0, e1;
   split_range(a.E, a.nwg, blockIdx.x, e0, e1);
-  router_rows(a, s, t, l, e0, e1, tiles);
+  if (a.pre_router) router_from_regs(a, s, t, l, sp);
+  else router_rows(a, s, t, l, e0, e1);
   SUBSTAMP(9);
   if (a.mode == MODE_LAYER && a.S > 0) {
-    int i0, i1;
-    split_range(a.S * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
-    const uint8_t* shared = a.layers[l].shared;
-    auto src = [&](int i, const uint8_t*& gb, const uint8_t*& ub, int& hvec, int& row0) {
-      const int sh = i / g.nblk_gu, b = i % g.nblk_gu;
-      if (tiles) {
-        gb = s.tile_sh + (size_t)(i - i0) * 2 * g.blk;
-        ub = gb + g.blk;
-      } else {
+    if (a.pre_shared) {
+      shared_from_regs<BITS>(a, s, t, l, sp);
+    } else {
+      int i0, i1;
+      split_range(a.S * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
+      const uint8_t* shared = get_layer(a, s, l).shared;
+      auto src = [&](int i, const uint8_t*& gb, const uint8_t*& ub, int& hvec, int& row0) {
+        const int sh = i >> g.lnb, b = i & (g.nblk_gu - 1);
         gb = shared + (size_t)sh * g.expert_bytes + (size_t)b * g.blk;
         ub = gb + g.off_up;
-      }
-      hvec = a.K + sh;
-      row0 = b * g.Ph;
-    };
-    gateup_items<BITS>(a, s, i0, i1, tiles, epoch_of(a, t, l), src, [] {});
+        hvec = a.K + sh;
+        row0 = b << g.lPh;
+      };
+      gateup_items<BITS>(a, s, i0, i1, false, epoch_of(a, t, l), src, [] {});
+    }
   }
   return true;
 }
@@ -757,18 +923,29 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
   int bst[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) bst[j] = -1;
+  // the mask bytes and the previous token's set are read with independent loads
+  // issued together (one memory round trip, not one per slot)
   if (a.mode == MODE_LAYER && a.boost_mask && t > 0) {
     const uint8_t* m = a.boost_mask + ((size_t)t * a.L + l) * K;
     const int* ps = a.prev + ((size_t)((t - 1) & 1) * a.L + l) * kMaxK;
+    const __amdgpu_buffer_rsrc_t rp = coh_rsrc(ps, kMaxK * 4);
+    const v4u p0 = ld_coh4(rp, 0), p1 = ld_coh4(rp, 16);
+    unsigned mk[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) mk[j] = m[j < K ? j : 0];
+    const unsigned pv[kMaxK] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-      if (j < K && m[j]) bst[j] = ld_coh(ps + j);
+      if (j < K && mk[j]) bst[j] = (int)pv[j];
   } else if (a.boosted) {
     const int* b = a.boosted + (size_t)t * K;
+    int bv[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) bv[j] = b[j < K ? j : 0];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j < K) {
-        const int e = b[j];
+        const int e = bv[j];
         if (e >= 0 && e < E) bst[j] = e;
         else if ((e >= E || e < -1) && lane == 0) set_dev_err(a.err, DEV_BAD_INDEX);
       }
@@ -803,6 +980,7 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
           good &= (e >= E || ep == epoch) ? 1 : 0;
         }
       if (__all(good)) break;
+      poll_pause(a);
       if ((it & 31u) == 31u) {
         bool go = true;
         if (lane == 0) go = poll_abort(a, t0, 1);
@@ -901,31 +1079,98 @@ __device__ inline const uint8_t* list_expert(const DecodeArgs& a, const Lds& s, 
   }
   if (li < a.K) {
     wk = s.sm->sel_w[li];
-    return a.layers[l].experts + (size_t)s.sm->sel_idx[li] * g.expert_bytes;
+    return get_layer(a, s, l).experts + (size_t)s.sm->sel_idx[li] * g.expert_bytes;
   }
   wk = 1.f;
-  return a.layers[l].shared + (size_t)(li - a.K) * g.expert_bytes;
+  return get_layer(a, s, l).shared + (size_t)(li - a.K) * g.expert_bytes;
 }
 
-// Prefetch (into LDS) the down blocks phase C of this workgroup reads, for every
-// list entry, on waves [w0, kNW). Needs the selection in LDS.
-__device__ __forceinline__ void prefetch_c(const DecodeArgs& a, const Lds& s, int l, int w0) {
+// Job k (0-based) of this lane in phase C's down projection: the k-th (pass, chunk)
+// pair that wave w walks, in the order of the direct loop. A pass covers expert-list
+// entries [first, first + n); lane (p, kl, grp) handles row r0 + c*Pp + p, entry
+// first + kl and group grp of chunk c = w + kNW*m.
+struct DnJob {
+  bool on;     // this lane has a slot to read (its row lies inside the workgroup's)
+  int pass;    // -1: no job k on this wave
+  int li, row, slot;
+  const uint8_t* blk;
+  float wk;
+};
+
+__device__ __forceinline__ DnJob down_job(const DecodeArgs& a, const Lds& s, int l, int k) {
   const Geo& g = a.geo;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int r0 = blockIdx.x * a.rpw, r1 = min(g.H, r0 + a.rpw);
+  const int npass = a.mode == MODE_EXPERT ? 1 : a.npass;
+  DnJob j;
+  j.on = false;
+  j.pass = -1;
+  j.li = 0; j.row = 0; j.slot = 0; j.blk = nullptr; j.wk = 0.f;
+  // all divisors are powers of two: shifts and masks only
+  for (int pi = 0; pi < npass; ++pi) {
+    const int first = a.mode == MODE_EXPERT ? 0 : pass_first_of(a, s, pi);
+    const int lgn = a.mode == MODE_EXPERT ? 0 : pass_lgn_of(a, s, pi);
+    const int lseg = lgn + g.lGi, lPp = 6 - lseg;  // seg = n*Gi lanes, Pp = 64/seg rows
+    const int nchunk = r0 < r1 ? (r1 - r0 + (1 << lPp) - 1) >> lPp : 0;
+    const int cnt = w < nchunk ? (nchunk - w + kNW - 1) >> 2 : 0;
+    if (k < cnt) {
+      const int c = w + k * kNW;
+      const int grp = lane & (g.Gi - 1), kl = (lane >> g.lGi) & ((1 << lgn) - 1), p = lane >> lseg;
+      j.pass = pi;
+      j.li = first + kl;
+      j.row = r0 + (c << lPp) + p;
+      j.on = j.row < r1;
+      const uint8_t* ex = list_expert(a, s, l, j.li, j.wk);
+      j.blk = ex + g.off_down + (size_t)(j.row >> g.lPi) * g.blk;
+      j.slot = ((j.row & (g.Pi - 1)) << g.lGi) + grp;
+      return j;
+    }
+    k -= cnt;
+  }
+  return j;
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_down(const DecodeArgs& a, const Lds& s, int l, DownPre& dp) {
+  // unconditional loads (a lane without job k re-reads a valid slot it ignores), so
+  // the compiler's wait counts stay exact
+  const uint8_t* any = a.mode == MODE_EXPERT ? a.single_expert : get_layer(a, s, l).experts;
+#pragma unroll
+  for (int k = 0; k < kDnPre; ++k) {
+    const DnJob j = down_job(a, s, l, k);
+    dp.d[k] = ld_slot<BITS>(j.on ? j.blk : any, j.on ? j.slot : 0, false);
+  }
+}
+
+// Phase C's down projection from prefetched slots; partial sums per (pass, row) go
+// to s.acc exactly as in the direct loop.
+template <int BITS>
+__device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s, int l,
+                                               const DownPre& dp) {
+  const Geo& g = a.geo;
+  const int lane = threadIdx.x % kWave;
   const int r0 = blockIdx.x * a.rpw;
-  if (r0 >= g.H) return;
-  const int b0 = r0 / g.Pi;
-  const int nb = min(a.nbd, g.nblk_d - b0);
-  const int nlist = a.K + a.S;
-  for (int li = 0; li < nlist; ++li) {
-    float wk;
-    const uint8_t* ex = list_expert(a, s, l, li, wk);
-    dma_to_lds(s.tile_c + (size_t)li * a.nbd * g.blk, ex + g.off_down + (size_t)b0 * g.blk,
-               nb * g.blk, w0);
+  Dig D;
+  int dig_pass = -1;  // the h digits in D are those of this pass's entries
+#pragma unroll
+  for (int k = 0; k < kDnPre; ++k) {
+    const DnJob j = down_job(a, s, l, k);
+    if (j.pass < 0) continue;
+    const int n = a.mode == MODE_EXPERT ? 1 : pass_count_of(a, s, j.pass);
+    const int seg = n * g.Gi, grp = lane & (g.Gi - 1);
+    if (j.pass != dig_pass) {
+      load_dig(D, s.hdig, s.hsum, j.li * g.Gi + grp, s.sm->hxs[j.li]);
+      dig_pass = j.pass;
+    }
+    float part = j.on ? slot_dot<BITS>(dp.d[k], D) * j.wk : 0.f;
+    part = seg_sum(part, seg);
+    if (j.on && (lane % seg) == 0) s.acc[j.pass * a.rpw + (j.row - r0)] = part;
   }
 }
 
 template <int BITS>
-__device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t, int l, bool tiles) {
+__device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t, int l, DownPre& dp,
+                                        bool prefetch) {
   const Geo& g = a.geo;
   if (a.mode == MODE_EXPERT) {
     int i0, i1;
@@ -934,9 +1179,12 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
       gb = a.single_expert + (size_t)i * g.blk;
       ub = gb + g.off_up;
       hvec = 0;
-      row0 = i * g.Ph;
+      row0 = i << g.lPh;
     };
-    gateup_items<BITS>(a, s, i0, i1, false, epoch_of(a, t, l), src, [] {});
+    auto hook = [&] {
+      if (prefetch) load_down<BITS>(a, s, l, dp);
+    };
+    gateup_items<BITS>(a, s, i0, i1, false, epoch_of(a, t, l), src, hook);
     return true;
   }
   if (threadIdx.x == 0) s.sm->ok = 1;
@@ -948,27 +1196,29 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   if (a.trace_wg && t == 2 && threadIdx.x == 0)
     a.trace_wg[((size_t)l * a.nwg + blockIdx.x) * 4 + 1] = wall_clock64();
   if (a.mode != MODE_LAYER) return true;
-  const uint8_t* experts = a.layers[l].experts;
+  const uint8_t* experts = get_layer(a, s, l).experts;
   int i0, i1;
   split_range(a.K * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
   auto src = [&](int i, const uint8_t*& gb, const uint8_t*& ub, int& hvec, int& row0) {
-    const int k = i / g.nblk_gu, b = i % g.nblk_gu;
+    const int k = i >> g.lnb, b = i & (g.nblk_gu - 1);
     gb = experts + (size_t)s.sm->sel_idx[k] * g.expert_bytes + (size_t)b * g.blk;
     ub = gb + g.off_up;
     hvec = k;
-    row0 = b * g.Ph;
+    row0 = b << g.lPh;
   };
-  // the down blocks of phase C stream into LDS behind this wave's gate/up loads
+  // the down slots of phase C are requested right behind this wave's first gate/up
+  // loads, so they arrive while h is being exchanged
   auto hook = [&] {
-    if (tiles) prefetch_c(a, s, l, 0);
+    if (prefetch) load_down<BITS>(a, s, l, dp);
   };
   gateup_items<BITS>(a, s, i0, i1, false, epoch_of(a, t, l), src, hook);
   return true;
 }
 
 template <int BITS>
-__device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t, int l, bool tiles,
-                                        bool down_tile) {
+__device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t, int l,
+                                        bool pre_down, DownPre& dp, bool down_loaded,
+                                        StaticPre& sp, bool prefetch_static) {
   const Geo& g = a.geo;
   const int H = g.H, I = g.I;
   const bool expert_mode = a.mode == MODE_EXPERT;
@@ -976,19 +1226,14 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   const int rpw = a.rpw;
   const int r0 = blockIdx.x * rpw;
   const int r1 = min(H, r0 + rpw);
-  // h vectors of this layer (polled; in-order completion also retires the down-tile
-  // prefetch this wave issued in phase B)
+  // h vectors of this layer (polled; the down slots prefetched in phase B were
+  // requested before these polls, so they have landed when the polls complete)
   float* hs = s.hstage;
   {
     const Xv hv = xv_h(a);
     const Xv part{hv.base, nlist * I, hv.n_pad};
     const bool ok = xget(a, part, hs, epoch_of(a, t, l));
     if (!wg_all(s.sm, ok)) return false;
-  }
-  // the next layer's router rows and shared blocks stream into LDS meanwhile
-  if (tiles) {
-    const bool last = (l == a.L - 1);
-    if (!(last && t == a.T - 1)) prefetch_a(a, s, last ? 0 : l + 1, 0);
   }
   {
     float mx[kMaxPass];
@@ -1017,19 +1262,20 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   SUBSTAMP(11);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int npass = expert_mode ? 1 : a.npass;
-  const int b0 = r0 / g.Pi;
-  if (r0 < r1) {
+  if (pre_down) {
+    if (!down_loaded) load_down<BITS>(a, s, l, dp);
+    down_from_regs<BITS>(a, s, l, dp);
+  } else if (r0 < r1) {
     for (int pi = 0; pi < npass; ++pi) {
-      const int first = expert_mode ? 0 : a.pass_first[pi];
-      const int n = expert_mode ? 1 : a.pass_count[pi];
+      const int first = expert_mode ? 0 : pass_first_of(a, s, pi);
+      const int n = expert_mode ? 1 : pass_count_of(a, s, pi);
       const int seg = n * g.Gi;
       const int Pp = kWave / seg;
       const int grp = lane % g.Gi, kl = (lane / g.Gi) % n, p = lane / seg;
       const int li = first + kl;  // index in the expert list
       float wk;
       const uint8_t* ex = list_expert(a, s, l, li, wk);
-      const uint8_t* down = down_tile ? s.tile_c + (size_t)li * a.nbd * g.blk : ex + g.off_down;
-      const int bbase = down_tile ? b0 : 0;
+      const uint8_t* down = ex + g.off_down;
       const int nchunk = (r1 - r0 + Pp - 1) / Pp;
       if (w >= nchunk) continue;
       Dig D;
@@ -1043,7 +1289,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
           row[j] = r0 + c * Pp + p;
           if (c < nchunk && row[j] < r1) {
             const int b = row[j] / g.Pi, pd = row[j] % g.Pi;
-            S[j] = ld_slot<BITS>(down + (size_t)(b - bbase) * g.blk, pd * g.Gi + grp, down_tile);
+            S[j] = ld_slot<BITS>(down + (size_t)b * g.blk, pd * g.Gi + grp, false);
           }
         }
 #pragma unroll
@@ -1068,49 +1314,108 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
     if (expert_mode || l == a.L - 1) a.y[(size_t)t * H + rr] = v;
     else xput(xv_x(a), rr, v, epoch_of(a, t, l + 1));
   }
+  // the next layer's router rows and shared slots land while x is being exchanged
+  if (prefetch_static) {
+    issue_order();
+    load_static<BITS>(a, s, l == a.L - 1 ? 0 : l + 1, sp);
+    issue_order();
+  }
   return true;
 }
 
 // only_phase < 0: persistent (all tokens, all layers; phases wait on their inputs'
 // epochs). only_phase = 0/1/2: run that phase for token t_only, layer l_only.
+// The layer/stack chain in one persistent launch: every phase runs for every
+// (token, layer), so registers prefetched in one phase are handed to the next.
+// Used when the router rows and the down slots fit the register prefetch.
 template <int BITS>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int only_phase, int t_only,
-                                                          int l_only) {
-  extern __shared__ __align__(16) unsigned lds_raw[];
-  const Lds s = lds_view(lds_raw, a);
-  const bool persistent = only_phase < 0;
-  const bool pf = persistent && a.pf && a.mode == MODE_LAYER;
-  const bool pfd = pf && a.pf_down;
-  const int t0 = persistent ? 0 : t_only, t1 = persistent ? a.T : t_only + 1;
-  const int l0 = persistent ? 0 : l_only, l1 = persistent ? a.L : l_only + 1;
-  if (pf) prefetch_a(a, s, 0, 0);
-  unsigned long long* tr = nullptr;
-  for (int t = t0; t < t1; ++t) {
-    for (int l = l0; l < l1; ++l) {
-      if (a.trace && blockIdx.x == 0 && threadIdx.x == 0) tr = a.trace + ((size_t)t * a.L + l) * 16;
+__device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) {
+  StaticPre sp;
+  DownPre dp;
+  load_static<BITS>(a, s, 0, sp);
+  for (int t = 0; t < a.T; ++t) {
+    for (int l = 0; l < a.L; ++l) {
+      unsigned long long* tr =
+          (a.trace && blockIdx.x == 0 && threadIdx.x == 0) ? a.trace + ((size_t)t * a.L + l) * 16 : nullptr;
       if (threadIdx.x == 0) s.sm->tr = tr;
-#define QMOE_STAMP(i) \
-  if (tr) tr[i] = wall_clock64();
-      QMOE_STAMP(0);
+      if (tr) tr[0] = wall_clock64();
       unsigned long long* twg = (a.trace_wg && t == 2 && threadIdx.x == 0)
                                     ? a.trace_wg + ((size_t)l * a.nwg + blockIdx.x) * 4
                                     : nullptr;
+      if (!phase_a<BITS>(a, s, t, l, sp, true)) return;
+      if (tr) tr[1] = wall_clock64();
+      if (twg) twg[0] = wall_clock64();
+      if (!phase_b<BITS>(a, s, t, l, dp, true)) return;
+      if (tr) tr[3] = wall_clock64();
+      if (twg) twg[2] = wall_clock64();
+      const bool more = !(t == a.T - 1 && l == a.L - 1);
+      if (!phase_c<BITS>(a, s, t, l, true, dp, true, sp, more)) return;
+      if (tr) tr[5] = wall_clock64();
+      if (twg) twg[3] = wall_clock64();
+    }
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void specialise(DecodeArgs& a) {
+  a.geo = make_geo(kSpecH, kSpecI, BITS);
+  a.E = kSpecE;
+  a.K = kSpecK;
+  a.S = kSpecS;
+  a.mode = MODE_LAYER;
+  a.e_pad = kSpecE;
+  a.nwg = kSpecNwg;
+  a.rpw = kSpecH / kSpecNwg;
+  a.npass = 2;
+  a.pass_first[0] = 0; a.pass_count[0] = kSpecK;
+  a.pass_first[1] = kSpecK; a.pass_count[1] = kSpecS;
+  a.const_pass = 1;
+  a.pre_router = a.pre_shared = a.pre_down = 1;
+}
+
+// only_phase < 0: persistent (all tokens, all layers; phases wait on their inputs'
+// epochs). only_phase = 0/1/2: run that phase for token t_only, layer l_only.
+// SPEC: the specialised stack kernel (persistent, layer mode, flash-moe shape).
+template <int BITS, bool SPEC>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_raw, int only_phase,
+                                            int t_only, int l_only) {
+  const Lds s = lds_view(lds_raw, a);
+  const bool persistent = only_phase < 0;
+  // LDS copies of the pass table and of the layer table
+  if (!a.const_pass && (int)threadIdx.x < kMaxPass) {
+    s.sm->pass_first[threadIdx.x] = a.pass_first[threadIdx.x];
+    s.sm->pass_count[threadIdx.x] = a.pass_count[threadIdx.x];
+    s.sm->pass_lgn[threadIdx.x] = log2i(a.pass_count[threadIdx.x] > 0 ? a.pass_count[threadIdx.x] : 1);
+  }
+  {
+    const unsigned long long* src = reinterpret_cast<const unsigned long long*>(a.layers);
+    unsigned long long* dst = reinterpret_cast<unsigned long long*>(lds_raw + a.lds_layers);
+    for (int i = threadIdx.x; i < 4 * a.n_lds_layers; i += kThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+  if constexpr (SPEC) {
+    decode_chain<BITS>(a, s);
+    return;
+  }
+  if (persistent && a.mode == MODE_LAYER && a.pre_router && a.pre_down) {
+    decode_chain<BITS>(a, s);
+    return;
+  }
+  const int t0 = persistent ? 0 : t_only, t1 = persistent ? a.T : t_only + 1;
+  const int l0 = persistent ? 0 : l_only, l1 = persistent ? a.L : l_only + 1;
+  for (int t = t0; t < t1; ++t) {
+    for (int l = l0; l < l1; ++l) {
+      if (threadIdx.x == 0) s.sm->tr = nullptr;
+      StaticPre sp;
+      DownPre dp;
       bool have_x = false;
       if (a.mode != MODE_EXPERT && (persistent || only_phase == 0)) {
-        if (pf) {
-          wait_mem();  // this wave's router / shared prefetch has landed
-          __syncthreads();
-        }
-        if (!phase_a<BITS>(a, s, t, l, pf)) return;
+        if (!phase_a<BITS>(a, s, t, l, sp, false)) return;
         have_x = true;
-        QMOE_STAMP(1);
-        if (twg) twg[0] = wall_clock64();
       }
       if (persistent || only_phase == 1) {
         if (!have_x && a.mode != MODE_ROUTE && !prepare_x(a, s, t, l)) return;
-        if (!phase_b<BITS>(a, s, t, l, pfd)) return;
-        QMOE_STAMP(3);
-        if (twg) twg[2] = wall_clock64();
+        if (!phase_b<BITS>(a, s, t, l, dp, false)) return;
       }
       if (a.mode != MODE_ROUTE && (persistent || only_phase == 2)) {
         if (!persistent && a.mode == MODE_LAYER) {
@@ -1128,16 +1433,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, int only
           }
           __syncthreads();
         }
-        if (pfd) {
-          wait_mem();  // this wave's down-block prefetch has landed
-          __syncthreads();
-        }
-        if (!phase_c<BITS>(a, s, t, l, pf, pfd)) return;
-        QMOE_STAMP(5);
-        if (twg) twg[3] = wall_clock64();
+        if (!phase_c<BITS>(a, s, t, l, a.pre_down, dp, false, sp, false)) return;
       }
-#undef QMOE_STAMP
     }
+  }
+}
+
+template <int BITS, bool SPEC>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a_in, int only_phase, int t_only,
+                                                          int l_only) {
+  extern __shared__ __align__(16) unsigned lds_raw[];
+  if constexpr (SPEC) {
+    DecodeArgs a = a_in;
+    specialise<BITS>(a);
+    decode_body<BITS, true>(a, lds_raw, only_phase, t_only, l_only);
+  } else {
+    decode_body<BITS, false>(a_in, lds_raw, only_phase, t_only, l_only);
   }
 }
 
@@ -1156,10 +1467,13 @@ __global__ void zero_words(unsigned* sync, unsigned* err, unsigned long long* xc
 static int g_num_cu = -1;
 unsigned long long* g_trace = nullptr;     // set only by instrumented builds
 unsigned long long* g_trace_wg = nullptr;  // set only by instrumented builds
-int g_prefetch_mask = 0;  // LDS prefetch of router/shared tiles (bit 0) and down tiles (bit 1); off:
-                          // measured slower than direct loads (the DMA competes with the
-                          // latency-bound exchanges)
 static long long g_wall_khz = -1;
+// Register-prefetch paths in use when a shape allows them: router rows (bit 0),
+// shared gate/up slots (bit 1), down slots (bit 2); bit 3 allows the specialised
+// kernel. Instrumented builds change it to compare the paths; the results are
+// identical either way.
+int g_pre_mask = 15;  // bit 3: the specialised kernel
+int g_poll_sleep = 0;
 
 static hipError_t device_info() {
   if (g_num_cu > 0) return hipSuccess;
@@ -1211,6 +1525,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.sync = reinterpret_cast<unsigned*>(ws + r.wl.sync);
   a.err = reinterpret_cast<unsigned*>(ws + r.wl.err);
   a.timeout_ticks = (unsigned long long)g_wall_khz * 2000ull;  // 2 seconds per barrier wait
+  a.poll_sleep = g_poll_sleep;
   a.trace = g_trace;
   a.trace_wg = g_trace_wg;
 
@@ -1272,25 +1587,30 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.lds_hsum = words; words = up4(words + 2 * nlist * Gi);
   a.lds_acc = words; words = up4(words + kMaxPass * rpw);
   a.lds_xres = words; words = up4(words + rpw);
-  // tiles: router rows and shared gate/up items of this workgroup; down blocks
-  const int rows_pw = (a.E + nwg - 1) / nwg;
-  const int sh_pw = (a.S * a.geo.nblk_gu + nwg - 1) / nwg;
-  const int router_words = rows_pw * c.hidden;
-  const int sh_words = sh_pw * 2 * a.geo.blk / 4;
-  // down tile: the blocks covering rows [r0, r0 + rpw) (one extra for a straddle)
-  a.nbd = (rpw + a.geo.Pi - 1) / a.geo.Pi + (rpw % a.geo.Pi ? 1 : 0);
-  const int down_words = nlist * a.nbd * a.geo.blk / 4;
-  const bool want_pf = r.mode == MODE_LAYER && !r.phased;
-  const int with_pf = words + router_words + sh_words + down_words + 12;
-  a.pf = want_pf && (size_t)with_pf * 4 <= (size_t)kMaxLdsBytes;
-  a.pf_down = a.pf && (g_prefetch_mask & 2);
-  if (!(g_prefetch_mask & 1)) a.pf = 0;
-  if (!a.pf && a.pf_down) a.pf = 0, a.pf_down = 0;
-  a.lds_tile_a = a.lds_tile_sh = a.lds_tile_c = words;
-  if (a.pf) {
-    words = up4(words + router_words);
-    a.lds_tile_sh = words; words = up4(words + sh_words);
-    a.lds_tile_c = words; words = up4(words + down_words);
+  a.n_lds_layers = (r.mode == MODE_EXPERT || !r.layers_dev) ? 0 : std::min(r.L, kLdsLayers);
+  a.lds_layers = (words + 1) & ~1;  // 8-byte aligned
+  words = up4(a.lds_layers + a.n_lds_layers * (int)(sizeof(LayerPtrs) / 4));
+  // register prefetch eligibility (see load_static / load_down)
+  {
+    const int rows_pw = (a.E + nwg - 1) / nwg;
+    a.pre_router = rows_pw <= kRowsPre && rows_pw * (c.hidden / 4) <= kThreads * kRouterPre;
+    const int sh_pw = (a.S * a.geo.nblk_gu + nwg - 1) / nwg;
+    a.pre_shared = r.mode == MODE_LAYER && a.S > 0 && sh_pw <= kNW * kShPre;
+    // every wave's number of down jobs, for the largest row range a workgroup gets
+    int worst = 0;
+    for (int w = 0; w < kNW; ++w) {
+      int jobs = 0;
+      for (int pi = 0; pi < np; ++pi) {
+        const int seg = a.pass_count[pi] * Gi, Pp = kWave / seg;
+        const int nchunk = (rpw + Pp - 1) / Pp;
+        jobs += w < nchunk ? (nchunk - w + kNW - 1) / kNW : 0;
+      }
+      worst = std::max(worst, jobs);
+    }
+    a.pre_down = worst <= kDnPre;
+    a.pre_router = a.pre_router && (g_pre_mask & 1);
+    a.pre_shared = a.pre_shared && (g_pre_mask & 2);
+    a.pre_down = a.pre_down && (g_pre_mask & 4);
   }
   a.lds_words = words;
   const size_t lds = (size_t)words * 4;
@@ -1299,13 +1619,19 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
     return hipErrorInvalidValue;
   }
 
-  auto kern = c.bits == 4 ? decode_kernel<4> : decode_kernel<2>;
-  static bool attr_set[2] = {false, false};
-  if (lds > 64 * 1024 && !attr_set[c.bits == 4]) {
+  // the specialised kernel when the call is exactly the flash-moe stack shape
+  const bool spec = r.mode == MODE_LAYER && !r.phased && c.hidden == kSpecH && c.inter == kSpecI &&
+                    a.E == kSpecE && a.K == kSpecK && a.S == kSpecS && nwg == kSpecNwg &&
+                    a.pre_router && a.pre_shared && a.pre_down && (g_pre_mask & 8);
+  auto kern = c.bits == 4 ? (spec ? decode_kernel<4, true> : decode_kernel<4, false>)
+                          : (spec ? decode_kernel<2, true> : decode_kernel<2, false>);
+  static bool attr_set[4] = {false, false, false, false};
+  const int ki = (c.bits == 4 ? 2 : 0) + (spec ? 1 : 0);
+  if (lds > 64 * 1024 && !attr_set[ki]) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
     if (e != hipSuccess) return e;
-    attr_set[c.bits == 4] = true;
+    attr_set[ki] = true;
   }
   // every exchange slot of this call starts at epoch 0
   const size_t nx = (size_t)(r.wl.prev - r.wl.xbuf) / sizeof(unsigned long long);

@@ -50,20 +50,22 @@ struct Geo {
   size_t off_up;     // byte offset of the up matrix inside an expert
   size_t off_down;   // byte offset of the down matrix
   size_t expert_bytes;
+  // log2 of Gh, Ph, Gi, Pi and nblk_gu (all powers of two for the supported shapes)
+  int lGh, lPh, lGi, lPi, lnb;
 };
 
-__host__ __device__ inline int log2i(int v) {
+__host__ __device__ constexpr int log2i(int v) {
   int r = 0;
   while ((1 << r) < v) ++r;
   return r;
 }
 
-__host__ __device__ inline bool pow2_dim_ok(int v) {
+__host__ __device__ constexpr bool pow2_dim_ok(int v) {
   return v >= 64 && v <= kMaxDim && (v & (v - 1)) == 0;
 }
 
-__host__ __device__ inline Geo make_geo(int H, int I, int bits) {
-  Geo g;
+__host__ __device__ constexpr Geo make_geo(int H, int I, int bits) {
+  Geo g{};
   g.H = H; g.I = I; g.bits = bits;
   g.Gh = H / kGroup; g.Ph = kWave / g.Gh;
   g.Gi = I / kGroup; g.Pi = kWave / g.Gi;
@@ -73,6 +75,8 @@ __host__ __device__ inline Geo make_geo(int H, int I, int bits) {
   g.off_up = (size_t)g.nblk_gu * g.blk;
   g.off_down = 2 * g.off_up;
   g.expert_bytes = g.off_down + (size_t)g.nblk_d * g.blk;
+  g.lGh = log2i(g.Gh); g.lPh = log2i(g.Ph); g.lGi = log2i(g.Gi); g.lPi = log2i(g.Pi);
+  g.lnb = log2i(g.nblk_gu);
   return g;
 }
 
