@@ -152,7 +152,9 @@ __device__ inline Lds lds_view(unsigned* raw, const DecodeArgs& a) {
 // included.
 __device__ inline LayerPtrs get_layer(const DecodeArgs& a, const Lds& s, int l) {
   LayerPtrs p;
-  if (l < a.n_lds_layers) {
+  // the specialised kernel runs only when the whole table is in LDS: no global
+  // path to merge with (a merge would make the compiler wait for all loads)
+  if (a.const_pass || l < a.n_lds_layers) {
     typedef __attribute__((address_space(3))) const unsigned long long lds_u64;
     lds_u64* q = (lds_u64*)(uintptr_t)(s.lt + (unsigned)l * (unsigned)sizeof(LayerPtrs));
     p.experts = reinterpret_cast<const uint8_t*>(q[0]);
@@ -1622,7 +1624,8 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   // the specialised kernel when the call is exactly the flash-moe stack shape
   const bool spec = r.mode == MODE_LAYER && !r.phased && c.hidden == kSpecH && c.inter == kSpecI &&
                     a.E == kSpecE && a.K == kSpecK && a.S == kSpecS && nwg == kSpecNwg &&
-                    a.pre_router && a.pre_shared && a.pre_down && (g_pre_mask & 8);
+                    a.pre_router && a.pre_shared && a.pre_down && a.n_lds_layers == r.L &&
+                    (g_pre_mask & 8);
   auto kern = c.bits == 4 ? (spec ? decode_kernel<4, true> : decode_kernel<4, false>)
                           : (spec ? decode_kernel<2, true> : decode_kernel<2, false>);
   static bool attr_set[4] = {false, false, false, false};
