@@ -88,6 +88,7 @@ struct DecodeArgs {
   unsigned long long* trace_wg;  // optional [L][nwg][4] stamps of every workgroup at token 2
   int nwg;
   int rpw;                       // phase C output rows per workgroup
+  int exact_rows;                // nwg * rpw == H: every workgroup owns exactly rpw rows
   int npass;
   int pass_first[kMaxPass], pass_count[kMaxPass];
   int pre_router;                // router rows of a workgroup fit the register prefetch
@@ -113,10 +114,16 @@ struct Small {
   float hsc[kMaxPass];
   float hxs[kMaxPass];
   unsigned long long* tr;  // trace row (workgroup 0, thread 0 only)
+  // Stamps are kept here and written out once per layer, after the layer's last
+  // loads are issued: a store in the middle of a phase would be waited for by the
+  // next wait on a load (the counter is in issue order), and so distort the phase.
+  unsigned long long trl[16];
+  unsigned long long twl[4];
 };
 
+typedef __attribute__((address_space(1))) unsigned long long gl_u64;
 #define SUBSTAMP(i) \
-  if (threadIdx.x == 0 && s.sm->tr) s.sm->tr[i] = wall_clock64();
+  if (threadIdx.x == 0 && s.sm->tr) s.sm->trl[i] = wall_clock64();
 
 struct Lds {
   Small* sm;
@@ -200,6 +207,20 @@ __device__ inline int ld_coh(const int* p) {
 // Wait until this wave's outstanding memory operations (stores included) are done.
 __device__ inline void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// A copy of v that the compiler cannot prove equal to v. Values formed from it are
+// recomputed where they are used instead of being hoisted out of the layer loop
+// and kept live, for the whole loop, in registers that the prefetches need.
+template <typename T>
+__device__ inline T launder_s(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+template <typename T>
+__device__ inline T launder_v(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Issue-order point: memory operations are not moved across it by the compiler, so
 // prefetches stay where they are written (behind the loads they must not delay, and
 // ahead of the waits they should overlap). Emits no instruction.
@@ -231,10 +252,12 @@ struct Xv {
 
 __device__ inline void xput(const Xv& x, int i, float v, unsigned epoch) {
   const unsigned long long pv = ((unsigned long long)epoch << 32) | __float_as_uint(v);
+  // global address space: a store through a generic pointer would be a flat store
+  __attribute__((address_space(1))) unsigned long long* base =
+      (__attribute__((address_space(1))) unsigned long long*)(uintptr_t)launder_s(x.base);
 #pragma unroll
   for (int r = 0; r < kRep; ++r)
-    __hip_atomic_store(x.base + (size_t)r * x.n_pad + i, pv, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(base + (size_t)r * x.n_pad + i, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ bool poll_abort(const DecodeArgs& a, unsigned long long t0, int lane0);
@@ -247,10 +270,12 @@ __device__ inline void poll_pause(const DecodeArgs& a) {
 }
 
 // Wait until every pair of this workgroup's replica carries `epoch` and copy the
-// values into LDS (dst[i]). All threads take part; each polls its own chunks.
+// values into LDS (dst[i]). All threads take part; each polls its own chunks,
+// kPer 16-byte chunks per thread in flight at once (a vector of up to
+// 2*kPer*kThreads values is awaited in one round trip).
 // Returns false if the kernel is aborting.
+template <int kPer = 8>
 __device__ __forceinline__ bool xget(const DecodeArgs& a, const Xv& x, float* dst, unsigned epoch) {
-  constexpr int kPer = 8;
   const unsigned long long* src = x.base + (size_t)(blockIdx.x % kRep) * x.n_pad;
   const __amdgpu_buffer_rsrc_t r = coh_rsrc(src, x.n_pad * 8);
   const int nch = (x.n + 1) / 2;  // only the n produced values are awaited
@@ -621,7 +646,7 @@ __device__ __forceinline__ bool prepare_x(const DecodeArgs& a, const Lds& s, int
     float4 v = *reinterpret_cast<float4*>(s.xn + i);
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     if (gamma) {
-      const float4 gm = *reinterpret_cast<const float4*>(gamma + i);
+      const float4 gm = ldg_f4(gamma + i);
       v.x *= gm.x; v.y *= gm.y; v.z *= gm.z; v.w *= gm.w;
       *reinterpret_cast<float4*>(s.xn + i) = v;
     }
@@ -1102,7 +1127,7 @@ struct DnJob {
 __device__ __forceinline__ DnJob down_job(const DecodeArgs& a, const Lds& s, int l, int k) {
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const int r0 = blockIdx.x * a.rpw, r1 = min(g.H, r0 + a.rpw);
+  const int r0 = blockIdx.x * a.rpw, r1 = a.exact_rows ? r0 + a.rpw : min(g.H, r0 + a.rpw);
   const int npass = a.mode == MODE_EXPERT ? 1 : a.npass;
   DnJob j;
   j.on = false;
@@ -1170,7 +1195,61 @@ __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s
   }
 }
 
+// Phase B of the specialised kernel (hidden 4096, inter 1024, K 4, 256 workgroups):
+// a workgroup owns kNW*kBatch consecutive gate/up rows of one routed expert, so
+// each wave has exactly one batch. Every address (gate/up rows and the phase-C down
+// slots) is formed from LDS first; then all loads go out in one straight run, with
+// no branch or LDS read between them that would make the compiler wait for the
+// loads already issued.
+static_assert(kSpecK * kSpecI / kSpecNwg == kNW * kBatch, "one batch per wave");
+static_assert(kSpecI % (kNW * kBatch) == 0, "a workgroup's rows lie in one expert");
 template <int BITS>
+__device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds& s, int t, int l,
+                                                 DownPre& dp) {
+  const Geo& g = a.geo;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int i0 = blockIdx.x * (kNW * kBatch);
+  const int k = i0 >> g.lnb;  // the routed expert (list entry) of every row here
+  const uint8_t* ex = get_layer(a, s, l).experts + (size_t)s.sm->sel_idx[k] * g.expert_bytes;
+  const uint8_t* gb[kBatch];
+  int row[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int b = (i0 + w + j * kNW) & (g.nblk_gu - 1);
+    gb[j] = ex + (size_t)b * g.blk;
+    row[j] = b;  // one row per block in this shape
+  }
+  const uint8_t* db[kDnPre];
+  int ds[kDnPre];
+#pragma unroll
+  for (int q = 0; q < kDnPre; ++q) {
+    const DnJob j = down_job(a, s, l, q);
+    db[q] = j.on ? j.blk : ex;
+    ds[q] = j.on ? j.slot : 0;
+  }
+  Dig D;
+  load_dig(D, s.xdig, s.xsum, lane, s.sm->xs_x);
+  Slot G[kBatch], U[kBatch];
+  issue_order();
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    G[j] = ld_slot<BITS>(gb[j], lane, false);
+    U[j] = ld_slot<BITS>(gb[j] + g.off_up, lane, false);
+  }
+#pragma unroll
+  for (int q = 0; q < kDnPre; ++q) dp.d[q] = ld_slot<BITS>(db[q], ds[q], false);
+  issue_order();
+  const Xv hxv = xv_h(a);
+  const unsigned epoch = epoch_of(a, t, l);
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const float pg = seg_sum(slot_dot<BITS>(G[j], D), kWave);
+    const float pu = seg_sum(slot_dot<BITS>(U[j], D), kWave);
+    if (lane == 0) xput(hxv, k * g.I + row[j], silu(pg) * pu, epoch);
+  }
+}
+
+template <int BITS, bool SPEC = false>
 __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t, int l, DownPre& dp,
                                         bool prefetch) {
   const Geo& g = a.geo;
@@ -1195,9 +1274,12 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   __syncthreads();
   if (!s.sm->ok) return false;
   SUBSTAMP(10);
-  if (a.trace_wg && t == 2 && threadIdx.x == 0)
-    a.trace_wg[((size_t)l * a.nwg + blockIdx.x) * 4 + 1] = wall_clock64();
+  if (a.trace_wg && t == 2 && threadIdx.x == 0) s.sm->twl[1] = wall_clock64();
   if (a.mode != MODE_LAYER) return true;
+  if constexpr (SPEC) {
+    gateup_down_spec<BITS>(a, s, t, l, dp);
+    return true;
+  }
   const uint8_t* experts = get_layer(a, s, l).experts;
   int i0, i1;
   split_range(a.K * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
@@ -1217,7 +1299,10 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   return true;
 }
 
-template <int BITS>
+// chunks per thread that poll the whole h exchange of the specialised shape at once
+constexpr int kSpecHPer = (kSpecK + kSpecS) * kSpecI / 2 / kThreads;
+
+template <int BITS, bool SPEC = false>
 __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t, int l,
                                         bool pre_down, DownPre& dp, bool down_loaded,
                                         StaticPre& sp, bool prefetch_static) {
@@ -1227,17 +1312,22 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   const int nlist = expert_mode ? 1 : a.K + a.S;
   const int rpw = a.rpw;
   const int r0 = blockIdx.x * rpw;
-  const int r1 = min(H, r0 + rpw);
+  const int r1 = a.exact_rows ? r0 + rpw : min(H, r0 + rpw);
   // h vectors of this layer (polled; the down slots prefetched in phase B were
   // requested before these polls, so they have landed when the polls complete)
   float* hs = s.hstage;
   {
-    const Xv hv = xv_h(a);
-    const Xv part{hv.base, nlist * I, hv.n_pad};
-    const bool ok = xget(a, part, hs, epoch_of(a, t, l));
-    if (!wg_all(s.sm, ok)) return false;
-  }
-  {
+    {
+      const Xv hv = xv_h(a);
+      const Xv part{hv.base, nlist * I, hv.n_pad};
+      bool ok;
+      if constexpr (SPEC)
+        ok = xget<kSpecHPer>(a, part, hs, epoch_of(a, t, l));
+      else
+        ok = xget(a, part, hs, epoch_of(a, t, l));
+      if (!wg_all(s.sm, ok)) return false;
+    }
+    SUBSTAMP(13);
     float mx[kMaxPass];
     for (int j = 0; j < nlist; ++j) {
       mx[j] = 0.f;
@@ -1330,7 +1420,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
 // The layer/stack chain in one persistent launch: every phase runs for every
 // (token, layer), so registers prefetched in one phase are handed to the next.
 // Used when the router rows and the down slots fit the register prefetch.
-template <int BITS>
+template <int BITS, bool SPEC>
 __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) {
   StaticPre sp;
   DownPre dp;
@@ -1340,20 +1430,26 @@ __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) 
       unsigned long long* tr =
           (a.trace && blockIdx.x == 0 && threadIdx.x == 0) ? a.trace + ((size_t)t * a.L + l) * 16 : nullptr;
       if (threadIdx.x == 0) s.sm->tr = tr;
-      if (tr) tr[0] = wall_clock64();
+      if (tr) s.sm->trl[0] = wall_clock64();
       unsigned long long* twg = (a.trace_wg && t == 2 && threadIdx.x == 0)
                                     ? a.trace_wg + ((size_t)l * a.nwg + blockIdx.x) * 4
                                     : nullptr;
       if (!phase_a<BITS>(a, s, t, l, sp, true)) return;
-      if (tr) tr[1] = wall_clock64();
-      if (twg) twg[0] = wall_clock64();
-      if (!phase_b<BITS>(a, s, t, l, dp, true)) return;
-      if (tr) tr[3] = wall_clock64();
-      if (twg) twg[2] = wall_clock64();
+      if (tr) s.sm->trl[1] = wall_clock64();
+      if (twg) s.sm->twl[0] = wall_clock64();
+      if (!phase_b<BITS, SPEC>(a, s, t, l, dp, true)) return;
+      if (tr) s.sm->trl[3] = wall_clock64();
+      if (twg) s.sm->twl[2] = wall_clock64();
       const bool more = !(t == a.T - 1 && l == a.L - 1);
-      if (!phase_c<BITS>(a, s, t, l, true, dp, true, sp, more)) return;
-      if (tr) tr[5] = wall_clock64();
-      if (twg) twg[3] = wall_clock64();
+      if (!phase_c<BITS, SPEC>(a, s, t, l, true, dp, true, sp, more)) return;
+      if (tr) {
+        s.sm->trl[5] = wall_clock64();
+        for (int i = 0; i < 16; ++i) ((gl_u64*)(uintptr_t)tr)[i] = s.sm->trl[i];
+      }
+      if (twg) {
+        s.sm->twl[3] = wall_clock64();
+        for (int i = 0; i < 4; ++i) ((gl_u64*)(uintptr_t)twg)[i] = s.sm->twl[i];
+      }
     }
   }
 }
@@ -1368,6 +1464,7 @@ __device__ __forceinline__ void specialise(DecodeArgs& a) {
   a.e_pad = kSpecE;
   a.nwg = kSpecNwg;
   a.rpw = kSpecH / kSpecNwg;
+  a.exact_rows = 1;
   a.npass = 2;
   a.pass_first[0] = 0; a.pass_count[0] = kSpecK;
   a.pass_first[1] = kSpecK; a.pass_count[1] = kSpecS;
@@ -1390,17 +1487,18 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
     s.sm->pass_lgn[threadIdx.x] = log2i(a.pass_count[threadIdx.x] > 0 ? a.pass_count[threadIdx.x] : 1);
   }
   {
-    const unsigned long long* src = reinterpret_cast<const unsigned long long*>(a.layers);
+    const __attribute__((address_space(1))) unsigned long long* src =
+        (const __attribute__((address_space(1))) unsigned long long*)(uintptr_t)a.layers;
     unsigned long long* dst = reinterpret_cast<unsigned long long*>(lds_raw + a.lds_layers);
     for (int i = threadIdx.x; i < 4 * a.n_lds_layers; i += kThreads) dst[i] = src[i];
   }
   __syncthreads();
   if constexpr (SPEC) {
-    decode_chain<BITS>(a, s);
+    decode_chain<BITS, true>(a, s);
     return;
   }
   if (persistent && a.mode == MODE_LAYER && a.pre_router && a.pre_down) {
-    decode_chain<BITS>(a, s);
+    decode_chain<BITS, false>(a, s);
     return;
   }
   const int t0 = persistent ? 0 : t_only, t1 = persistent ? a.T : t_only + 1;
@@ -1572,6 +1670,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
     return hipErrorInvalidValue;
   }
   a.rpw = rpw;
+  a.exact_rows = (long long)rpw * nwg == c.hidden;
   a.nwg = nwg;
   const int nlist = r.mode == MODE_EXPERT ? 1 : c.top_k + c.n_shared;
 
