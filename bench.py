@@ -9,7 +9,15 @@ token's routed experts repeating the previous token's (temporal tier).
 Prints one JSON line. `value` is decode tokens/s; `roofline` prices the decode
 kernel's algorithmic bytes (weights touched per token, the per-token figure
 below) against MI355X's 8 TB/s HBM; `cpu_baseline` is the CPU oracle timed on
-a bounded sample (token 0 through the first few layers) and scaled to tokens/s.
+a bounded sample (the first tokens through all layers) and scaled to tokens/s.
+
+Two helper modes feed the `traffic` figure (HBM bytes per launch measured by the
+FETCH_SIZE / WRITE_SIZE counters, calibrated against a plain copy):
+  --copy-calibration   three 1 GiB device-to-device copies (run under rocprofv3 --pmc)
+  --traffic-record F W CF CW
+                       turn four rocprofv3 counter CSVs (decode FETCH_SIZE, decode
+                       WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE) into the record
+                       profiles/decode_stack60_traffic.json that later runs report
 """
 import argparse
 import json
@@ -34,6 +42,60 @@ def per_token_bytes(w):
     from tests.helpers import config_for
     eb = q.moe_packed_expert_bytes(config_for(w))
     return w.n_layers * ((w.top_k + w.n_shared) * eb + 4 * w.n_experts * w.hidden)
+
+
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack60_traffic.json")
+
+
+def copy_calibration():
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}), flush=True)
+
+
+def _counter_rows(path, counter):
+    import csv
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    if not rows:
+        raise SystemExit(f"{path}: no {counter} rows")
+    return rows
+
+
+def traffic_record(f_csv, w_csv, cf_csv, cw_csv, config_name, layers, tokens):
+    """Per-launch HBM bytes of the decode kernel: its FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch) scaled by what the same counters read for a copy of known size."""
+    from quantized_expert_mat_amd import build as qb
+
+    def avg(path, counter, pred):
+        v = [float(r["Counter_Value"]) for r in _counter_rows(path, counter) if pred(r)]
+        if not v:
+            raise SystemExit(f"{path}: no matching {counter} dispatch")
+        return sum(v) / len(v), len(v)
+
+    is_dec = lambda r: "decode_kernel" in r["Kernel_Name"]
+    is_copy = lambda r: "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= (1 << 16)
+    fetch, nf = avg(f_csv, "FETCH_SIZE", is_dec)
+    write, nw = avg(w_csv, "WRITE_SIZE", is_dec)
+    cfetch, ncf = avg(cf_csv, "FETCH_SIZE", is_copy)
+    cwrite, ncw = avg(cw_csv, "WRITE_SIZE", is_copy)
+    kib = COPY_BYTES / 1024
+    ff, fw = kib / cfetch, kib / cwrite
+    rec = {
+        "config": config_name, "layers": layers, "tokens": tokens, "source_hash": qb.source_hash(),
+        "decode_fetch_kib": fetch, "decode_write_kib": write, "decode_dispatches": [nf, nw],
+        "copy_fetch_kib": cfetch, "copy_write_kib": cwrite, "copy_dispatches": [ncf, ncw],
+        "fetch_scale": ff, "write_scale": fw,
+        "bytes_per_launch": (fetch * ff + write * fw) * 1024,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec), flush=True)
 
 
 def cpu_baseline_and_parity(w, x0_host, y_gpu, idx_gpu, n_tokens):
@@ -201,7 +263,15 @@ def main():
     ap.add_argument("--phased", action="store_true")
     ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
                     help="decode: the 60-layer stack (default); prefill: 1155 tokens through one layer")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
+    if args.traffic_record:
+        import workload as wl
+        w = wl.CONFIGS[args.config]
+        return traffic_record(*args.traffic_record, w.name, args.layers or w.n_layers, args.tokens or w.n_tokens)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the decode stack fits one MI355X's HBM and this build has "
               f"no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -291,12 +361,13 @@ def main():
         log(f"cpu oracle: {dt:.1f} s for {n} tokens x {L} layers -> {cpu['value']:.4f} tok/s")
 
     traffic = None
-    tf = os.path.join(ROOT, "profiles", "decode_stack60_traffic.json")
+    tf = TRAFFIC_FILE
     if os.path.exists(tf):
         try:
             rec = json.load(open(tf))
             from quantized_expert_mat_amd import build as qb
-            if rec.get("source_hash") == qb.source_hash() and rec.get("config") == w.name:
+            if (rec.get("source_hash") == qb.source_hash() and rec.get("config") == w.name
+                    and rec.get("layers") == L):
                 traffic = rec["bytes_per_launch"] * (T / rec.get("tokens", T))
         except Exception:
             traffic = None
