@@ -80,11 +80,12 @@ struct DecodeArgs {
   unsigned long long* hx;        // [kRep][(K+S)*I] expert intermediates
   int e_pad;                     // E rounded up to even
   int* sel;                      // [2*kMaxK]
-  int* prev;                     // [2][L][kMaxK]
+  unsigned long long* prev;      // [2][L][kMaxK] (expert, epoch) pairs: the sorted set of the
+                                 // token before, per layer (temporal tier)
   unsigned* sync;                // [0] abort flag
   unsigned* err;
   unsigned long long timeout_ticks;
-  unsigned long long* trace;     // optional [T][L][16] wall-clock stamps from workgroup 0
+  unsigned long long* trace;     // optional [T][L][16] wall-clock stamps from the last workgroup
   unsigned long long* trace_wg;  // optional [L][nwg][4] stamps of every workgroup at token 2
   int nwg;
   int rpw;                       // phase C output rows per workgroup
@@ -326,15 +327,29 @@ __device__ inline float dpp_f(float v) {
 }
 constexpr int kQuad1032 = 0xB1, kQuad2301 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
 
+__device__ inline float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ inline unsigned long long readlane_u64(unsigned long long v, int l) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)v, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // Sum over aligned segments of `width` lanes (power of two); every lane of a
-// segment receives the segment's total.
+// segment receives the segment's total. Within a 16-lane row the steps are DPP
+// moves; across rows the four row totals are read out with readlane (a lane
+// shuffle would be an LDS permute, a round trip of LDS latency per step).
 __device__ inline float seg_sum(float v, int width) {
   if (width >= 2) v += dpp_f<kQuad1032>(v);
   if (width >= 4) v += dpp_f<kQuad2301>(v);
   if (width >= 8) v += dpp_f<kRowHalfMirror>(v);
   if (width >= 16) v += dpp_f<kRowMirror>(v);
-  if (width >= 32) v += __shfl_xor(v, 16);
-  if (width >= 64) v += __shfl_xor(v, 32);
+  if (width >= 32) {
+    const float r0 = readlane_f(v, 0), r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
+    if (width >= 64) v = (r0 + r1) + (r2 + r3);
+    else v = (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+  }
   return v;
 }
 __device__ inline int seg_sum8_i(int v) {
@@ -348,12 +363,12 @@ __device__ inline float seg_max(float v, int width) {
   if (width >= 4) v = fmaxf(v, dpp_f<kQuad2301>(v));
   if (width >= 8) v = fmaxf(v, dpp_f<kRowHalfMirror>(v));
   if (width >= 16) v = fmaxf(v, dpp_f<kRowMirror>(v));
-  if (width >= 32) v = fmaxf(v, __shfl_xor(v, 16));
-  if (width >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  if (width >= 32) {
+    const float r0 = readlane_f(v, 0), r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
+    if (width >= 64) v = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    else v = (threadIdx.x & 32) ? fmaxf(r2, r3) : fmaxf(r0, r1);
+  }
   return v;
-}
-__device__ inline float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 // Whole-wave sum, returned uniform (one lane of each 16-lane row read out).
 __device__ inline float wave_sum(float v) {
@@ -373,10 +388,10 @@ __device__ inline unsigned long long wave_max_u64(unsigned long long k) {
   k = dpp_max_step<kQuad2301>(k);
   k = dpp_max_step<kRowHalfMirror>(k);
   k = dpp_max_step<kRowMirror>(k);
-  unsigned long long o = __shfl_xor(k, 16);
-  k = o > k ? o : k;
-  o = __shfl_xor(k, 32);
-  return o > k ? o : k;
+  const unsigned long long r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16);
+  const unsigned long long r2 = readlane_u64(k, 32), r3 = readlane_u64(k, 48);
+  const unsigned long long a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
 }
 
 // Power-of-two scale that maps |v| <= m into (-2^22, 2^22).
@@ -639,6 +654,7 @@ __device__ __forceinline__ bool prepare_x(const DecodeArgs& a, const Lds& s, int
       *reinterpret_cast<float4*>(s.xn + i) = *reinterpret_cast<const float4*>(x + i);
   }
   if (!wg_all(s.sm, ok)) return false;
+  SUBSTAMP(14);
   const int r0 = blockIdx.x * a.rpw;
   if ((int)threadIdx.x < a.rpw && r0 + (int)threadIdx.x < H) s.xres[threadIdx.x] = s.xn[r0 + threadIdx.x];
   float ss = 0.f, mx = 0.f;
@@ -942,7 +958,9 @@ __device__ inline unsigned ord_f32(float f) {
 }
 
 // Top-K with the temporal tier, then softmax over the selected logits. Runs on
-// wave 0; the result is left in LDS (sel_idx, sel_w).
+// wave 0 (kCh chunks of 4 logits per lane); the result is left in LDS (sel_idx,
+// sel_w).
+template <int kCh>
 __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, int t, int l) {
   if (threadIdx.x >= kWave) return;
   const int E = a.E, K = a.K, lane = threadIdx.x;
@@ -950,20 +968,19 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
   int bst[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) bst[j] = -1;
-  // the mask bytes and the previous token's set are read with independent loads
-  // issued together (one memory round trip, not one per slot)
-  if (a.mode == MODE_LAYER && a.boost_mask && t > 0) {
+  // The mask bytes and the previous token's set (epoch-tagged pairs written by
+  // workgroup 0 a whole token earlier, so the first read normally finds them) are
+  // requested together with the logits and checked after the logits poll.
+  const bool tier_prev = a.mode == MODE_LAYER && a.boost_mask && t > 0;
+  unsigned mk[kMaxK];
+  v4u pp[kMaxK / 2];
+  const __amdgpu_buffer_rsrc_t rp = coh_rsrc(a.prev + ((size_t)((t + 1) & 1) * a.L + l) * kMaxK, kMaxK * 8);
+  if (tier_prev) {
     const uint8_t* m = a.boost_mask + ((size_t)t * a.L + l) * K;
-    const int* ps = a.prev + ((size_t)((t - 1) & 1) * a.L + l) * kMaxK;
-    const __amdgpu_buffer_rsrc_t rp = coh_rsrc(ps, kMaxK * 4);
-    const v4u p0 = ld_coh4(rp, 0), p1 = ld_coh4(rp, 16);
-    unsigned mk[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) mk[j] = m[j < K ? j : 0];
-    const unsigned pv[kMaxK] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < K && mk[j]) bst[j] = (int)pv[j];
+    for (int q = 0; q < kMaxK / 2; ++q) pp[q] = ld_coh4(rp, 16 * q);
   } else if (a.boosted) {
     const int* b = a.boosted + (size_t)t * K;
     int bv[kMaxK];
@@ -980,7 +997,6 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
   }
   const bool by_bias = (a.flags & MOE_F_SELECT_BY_BIAS) != 0;
   const float* sb = a.sel_bias ? a.sel_bias + (size_t)t * E : nullptr;
-  constexpr int kCh = kMaxE / (4 * kWave);  // groups of 4 logits per lane
   constexpr int kPer = 4 * kCh;
   unsigned long long key[kPer];
   float lgv[kPer];
@@ -1011,10 +1027,37 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
       if ((it & 31u) == 31u) {
         bool go = true;
         if (lane == 0) go = poll_abort(a, t0, 1);
-        if (!__shfl(go ? 1 : 0, 0)) {
+        if (!__builtin_amdgcn_readlane(go ? 1 : 0, 0)) {
           s.sm->ok = 0;
           return;
         }
+      }
+    }
+    SUBSTAMP(15);
+    if (tier_prev) {
+      const unsigned pep = epoch_of(a, t - 1, l);
+      const unsigned long long t1 = wall_clock64();
+      for (unsigned it = 0;; ++it) {
+        bool good = true;
+#pragma unroll
+        for (int q = 0; q < kMaxK / 2; ++q)
+          good = good && (2 * q >= K || pp[q].y == pep) && (2 * q + 1 >= K || pp[q].w == pep);
+        if (good) break;
+        if ((it & 31u) == 31u) {
+          bool go = true;
+          if (lane == 0) go = poll_abort(a, t1, 1);
+          if (!__builtin_amdgcn_readlane(go ? 1 : 0, 0)) {
+            s.sm->ok = 0;
+            return;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kMaxK / 2; ++q) pp[q] = ld_coh4(rp, 16 * q);
+      }
+#pragma unroll
+      for (int q = 0; q < kMaxK / 2; ++q) {
+        if (2 * q < K && mk[2 * q]) bst[2 * q] = (int)pp[q].x;
+        if (2 * q + 1 < K && mk[2 * q + 1]) bst[2 * q + 1] = (int)pp[q].z;
       }
     }
 #pragma unroll
@@ -1055,7 +1098,7 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
 #pragma unroll
     for (int r = 0; r < kPer; ++r)
       if (key[r] == wbest) key[r] = 0;
-    const float lw = __shfl(bl, (e / 4) % kWave);  // the owner lane holds the winner's logit
+    const float lw = readlane_f(bl, (e / 4) % kWave);  // the owner lane holds the winner's logit
     if (lane == k) {
       my_idx = e;
       my_lg = lw;
@@ -1086,13 +1129,13 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
       // rank of my_idx among the selected set = its position in sorted order
       int rank = 0;
       for (int j = 0; j < K; ++j) {
-        const int other = __shfl(my_idx, j);
+        const int other = __builtin_amdgcn_readlane(my_idx, j);
         rank += (j != lane && other < my_idx) ? 1 : 0;
       }
-      int* ps = a.prev + ((size_t)(t & 1) * a.L + l) * kMaxK;
-      if (mine) st_coh(ps + rank, my_idx);
+      unsigned long long* ps = a.prev + ((size_t)(t & 1) * a.L + l) * kMaxK;
+      const unsigned long long pv = ((unsigned long long)epoch_of(a, t, l) << 32) | (unsigned)my_idx;
+      if (mine) __hip_atomic_store(ps + rank, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    wait_mem();  // published before any later exchange write of this workgroup
   }
 }
 
@@ -1270,7 +1313,10 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   }
   if (threadIdx.x == 0) s.sm->ok = 1;
   __syncthreads();
-  select_topk(a, s, t, l);
+  if constexpr (SPEC)
+    select_topk<(kSpecE + 4 * kWave - 1) / (4 * kWave)>(a, s, t, l);
+  else
+    select_topk<kMaxE / (4 * kWave)>(a, s, t, l);
   __syncthreads();
   if (!s.sm->ok) return false;
   SUBSTAMP(10);
@@ -1428,7 +1474,8 @@ __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) 
   for (int t = 0; t < a.T; ++t) {
     for (int l = 0; l < a.L; ++l) {
       unsigned long long* tr =
-          (a.trace && blockIdx.x == 0 && threadIdx.x == 0) ? a.trace + ((size_t)t * a.L + l) * 16 : nullptr;
+          (a.trace && blockIdx.x == a.nwg - 1 && threadIdx.x == 0) ? a.trace + ((size_t)t * a.L + l) * 16
+                                                                    : nullptr;
       if (threadIdx.x == 0) s.sm->tr = tr;
       if (tr) s.sm->trl[0] = wall_clock64();
       unsigned long long* twg = (a.trace_wg && t == 2 && threadIdx.x == 0)
@@ -1621,7 +1668,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.hx = reinterpret_cast<unsigned long long*>(ws + r.wl.hbuf);
   a.e_pad = (a.E + 1) & ~1;
   a.sel = reinterpret_cast<int*>(ws + r.wl.sel);
-  a.prev = reinterpret_cast<int*>(ws + r.wl.prev);
+  a.prev = reinterpret_cast<unsigned long long*>(ws + r.wl.prev);
   a.sync = reinterpret_cast<unsigned*>(ws + r.wl.sync);
   a.err = reinterpret_cast<unsigned*>(ws + r.wl.err);
   a.timeout_ticks = (unsigned long long)g_wall_khz * 2000ull;  // 2 seconds per barrier wait
@@ -1736,7 +1783,8 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
     attr_set[ki] = true;
   }
   // every exchange slot of this call starts at epoch 0
-  const size_t nx = (size_t)(r.wl.prev - r.wl.xbuf) / sizeof(unsigned long long);
+  // every exchange slot, the selection words and the epoch-tagged previous sets
+  const size_t nx = (size_t)(r.wl.layers - r.wl.xbuf) / sizeof(unsigned long long);
   hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, stream, a.sync, a.err, a.xx, nx);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -107,7 +107,7 @@ inline WsLayout ws_layout(const moe_config& c, int T, int L) {
   w.logits = o; o = align256(o + kRep * sizeof(uint64_t) * c.n_experts);
   w.hbuf = o; o = align256(o + kRep * sizeof(uint64_t) * (size_t)(kMaxK + kMaxShared) * c.inter);
   w.sel = o; o = align256(o + 2 * sizeof(int) * kMaxK);
-  w.prev = o; o = align256(o + sizeof(int) * 2 * (size_t)(L > 0 ? L : 1) * kMaxK);
+  w.prev = o; o = align256(o + sizeof(uint64_t) * 2 * (size_t)(L > 0 ? L : 1) * kMaxK);
   w.layers = o; o = align256(o + sizeof(LayerPtrs) * (size_t)(L > 0 ? L : 1));
   w.total = o;
   return w;
