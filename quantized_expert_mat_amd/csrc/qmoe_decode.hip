@@ -33,8 +33,10 @@
 // fma(nibble, scale*x, bias*x) ("Kernel dequant tối ưu FMA"). Carried one step
 // further, a 64-group contributes scale*sum(q*x) + bias*sum(x); sum(x) per group
 // is computed once per vector, so the inner loop is just sum(q*x). That inner
-// loop runs on the integer dot-product unit: x is scaled by a power of two to a
-// 23-bit integer and split into six signed base-16 digits, the codes are stored
+// loop runs on the integer dot-product unit: each 64-group of x is scaled by its
+// own power of two to 23-bit integers, split into six signed base-16 digits (the
+// group's scale comes from the group alone, so encoding needs no vector-wide
+// reduction first), the codes are stored
 // as signed nibbles (q - 8), and v_dot8_i32_i4 forms eight 4-bit products per
 // instruction with exact int32 accumulation. One weight element then costs about
 // one VALU operation instead of two and a half for convert + FMA, which keeps the
@@ -111,9 +113,6 @@ struct Small {
   int sel_idx[kMaxK];
   float sel_w[kMaxK];
   int ok;
-  float xs_x;
-  float hsc[kMaxPass];
-  float hxs[kMaxPass];
   unsigned long long* tr;  // trace row (workgroup 0, thread 0 only)
   // Stamps are kept here and written out once per layer, after the layer's last
   // loads are issued: a store in the middle of a phase would be waited for by the
@@ -231,6 +230,24 @@ __device__ inline void issue_order() {
 }
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+__device__ inline uint4 to_uint4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+// Loads through global-address-space pointers. Weight pointers come from a table in
+// memory, so the compiler cannot prove they are global and would emit flat loads,
+// which also count against the LDS wait counter: every later LDS wait would then
+// wait for them too, and a prefetch would stall the phase it is meant to overlap.
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u gl_v4u;
+typedef __attribute__((address_space(1))) const unsigned gl_u32;
+typedef __attribute__((address_space(1))) const v4f gl_v4f;
+__device__ inline uint4 ldg_u4(const void* p) { return to_uint4(*(gl_v4u*)(uintptr_t)p); }
+__device__ inline unsigned ldg_u32(const void* p) { return *(gl_u32*)(uintptr_t)p; }
+__device__ inline float4 ldg_f4(const void* p) {
+  const v4f v = *(gl_v4f*)(uintptr_t)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 constexpr int kCachePolicySC1 = 16;           // device-coherent (bypasses non-coherent caches)
 constexpr int kBufferRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
@@ -450,34 +467,61 @@ __device__ inline int encode_chunk(const float v[8], float sc, unsigned out[6]) 
   return isum;
 }
 
-// Encode nvec vectors of length n (multiple of 64) held in LDS at src + j*n, with
-// per-vector scales sc[j]. Digits for (vector j, group g) go to
-// dig[(j*G + g)*kDigitStride + dw*6 + d]; sums to sum[2*(j*G+g)] = 8*sum(ints),
-// sum[2*(j*G+g)+1] = float sum of the values. Whole workgroup participates.
-__device__ __forceinline__ void encode_vectors(const float* src, int nvec, int n, const float* sc, unsigned* dig,
-                               float* sum) {
+// Encode nvec vectors of length n (multiple of 64) held in LDS at src + j*n, each
+// value first multiplied by gamma[i] (if given) and then by mul, the product
+// written back when NORM_BACK. Every group of 64
+// values gets its own power-of-two scale, from the group's largest magnitude found
+// across the 8 lanes that hold the group, so no vector-wide maximum (and no
+// barrier) precedes the encoding. Digits for (vector j, group g) go to
+// dig[(j*G + g)*kDigitStride + dw*6 + d]; sum[4*(j*G + g) + {0, 1, 2}] = 8*sum(ints),
+// float sum of the values, 1/scale. Whole workgroup participates.
+template <bool NORM_BACK>
+__device__ __forceinline__ void encode_vectors(float* src, int nvec, int n, float mul, const float* gamma,
+                                               unsigned* dig, float* sum) {
   const int G = n / kGroup;
   const int chunks_per_vec = n / 8;
   const int total = nvec * chunks_per_vec;
   // total is a multiple of 8 and kThreads a multiple of 64: the 8 chunks of a group
-  // always sit in 8 consecutive lanes (one DPP half-row) of one wave.
+  // always sit in 8 consecutive lanes (one DPP half-row) of one wave, all active or
+  // all inactive.
   for (int base = 0; base < total; base += kThreads) {
     const int c = base + (int)threadIdx.x;
-    int isum = 0;
-    float fsum = 0.f;
     const bool active = c < total;
-    int j = 0, cc = 0;
-    if (active) {
-      j = c / chunks_per_vec;
-      cc = c % chunks_per_vec;
-      const float4* p = reinterpret_cast<const float4*>(src + (size_t)j * n + (size_t)cc * 8);
-      const float4 v0 = p[0], v1 = p[1];
-      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      unsigned o[6];
-      isum = encode_chunk(v, sc[j], o);
+    const int j = active ? c / chunks_per_vec : 0, cc = active ? c % chunks_per_vec : 0;
+    float v[8];
+    {
+      float4* p = reinterpret_cast<float4*>(src + (size_t)j * n + (size_t)cc * 8);
+      float4 v0 = active ? p[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 v1 = active ? p[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (NORM_BACK && gamma) {
+        const float4 g0 = ldg_f4(gamma + (size_t)cc * 8), g1 = ldg_f4(gamma + (size_t)cc * 8 + 4);
+        v0.x *= g0.x; v0.y *= g0.y; v0.z *= g0.z; v0.w *= g0.w;
+        v1.x *= g1.x; v1.y *= g1.y; v1.z *= g1.z; v1.w *= g1.w;
+      }
+      if (NORM_BACK) {
+        v0.x *= mul; v0.y *= mul; v0.z *= mul; v0.w *= mul;
+        v1.x *= mul; v1.y *= mul; v1.z *= mul; v1.w *= mul;
+        if (active) {
+          p[0] = v0;
+          p[1] = v1;
+        }
+      }
+      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+      v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    }
+    float m = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) fsum += v[i];
-      const int g = cc / 8, dw = cc % 8;
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = seg_max(m, 8);
+    float sc, xs;
+    digit_scale(m, &sc, &xs);
+    unsigned o[6];
+    int isum = encode_chunk(v, sc, o);
+    float fsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fsum += v[i];
+    const int g = cc / 8, dw = cc % 8;
+    if (active) {
       uint2* dst = reinterpret_cast<uint2*>(dig + (size_t)(j * G + g) * kDigitStride + dw * 6);
       dst[0] = make_uint2(o[0], o[1]);
       dst[1] = make_uint2(o[2], o[3]);
@@ -485,11 +529,8 @@ __device__ __forceinline__ void encode_vectors(const float* src, int nvec, int n
     }
     isum = seg_sum8_i(isum);  // |sum of 64 ints| <= 2^28: exact in int32
     fsum = seg_sum(fsum, 8);
-    if (active && (cc % 8) == 0) {
-      const int g = cc / 8;
-      sum[2 * (j * G + g)] = 8.f * (float)isum;
-      sum[2 * (j * G + g) + 1] = fsum;
-    }
+    if (active && dw == 0)
+      *reinterpret_cast<float4*>(sum + 4 * (j * G + g)) = make_float4(8.f * (float)isum, fsum, xs, 0.f);
   }
 }
 
@@ -499,7 +540,7 @@ struct Dig {
   float X8, Xf, xs;
 };
 
-__device__ inline void load_dig(Dig& D, const unsigned* dig, const float* sum, int idx, float xs) {
+__device__ inline void load_dig(Dig& D, const unsigned* dig, const float* sum, int idx) {
   const uint4* p = reinterpret_cast<const uint4*>(dig + (size_t)idx * kDigitStride);
 #pragma unroll
   for (int i = 0; i < 12; ++i) {
@@ -509,9 +550,10 @@ __device__ inline void load_dig(Dig& D, const unsigned* dig, const float* sum, i
     D.d[4 * i + 2] = v.z;
     D.d[4 * i + 3] = v.w;
   }
-  D.X8 = sum[2 * idx];
-  D.Xf = sum[2 * idx + 1];
-  D.xs = xs;
+  const float4 sm = *reinterpret_cast<const float4*>(sum + 4 * idx);
+  D.X8 = sm.x;
+  D.Xf = sm.y;
+  D.xs = sm.z;
 }
 
 struct Slot {
@@ -524,22 +566,6 @@ typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 typedef __attribute__((address_space(3))) const v4u lds_v4u;
 typedef __attribute__((address_space(3))) const unsigned lds_u32;
 
-__device__ inline uint4 to_uint4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
-
-// Loads through global-address-space pointers. Weight pointers come from a table in
-// memory, so the compiler cannot prove they are global and would emit flat loads,
-// which also count against the LDS wait counter: every later LDS wait would then
-// wait for them too, and a prefetch would stall the phase it is meant to overlap.
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const v4u gl_v4u;
-typedef __attribute__((address_space(1))) const unsigned gl_u32;
-typedef __attribute__((address_space(1))) const v4f gl_v4f;
-__device__ inline uint4 ldg_u4(const void* p) { return to_uint4(*(gl_v4u*)(uintptr_t)p); }
-__device__ inline unsigned ldg_u32(const void* p) { return *(gl_u32*)(uintptr_t)p; }
-__device__ inline float4 ldg_f4(const void* p) {
-  const v4f v = *(gl_v4f*)(uintptr_t)p;
-  return make_float4(v.x, v.y, v.z, v.w);
-}
 
 // blk points to global memory, or (in_lds) to an LDS copy of the block.
 template <int BITS>
@@ -657,44 +683,28 @@ __device__ __forceinline__ bool prepare_x(const DecodeArgs& a, const Lds& s, int
   SUBSTAMP(14);
   const int r0 = blockIdx.x * a.rpw;
   if ((int)threadIdx.x < a.rpw && r0 + (int)threadIdx.x < H) s.xres[threadIdx.x] = s.xn[r0 + threadIdx.x];
-  float ss = 0.f, mx = 0.f;
-  for (int i = threadIdx.x * 4; i < H; i += kThreads * 4) {
-    float4 v = *reinterpret_cast<float4*>(s.xn + i);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    if (gamma) {
-      const float4 gm = ldg_f4(gamma + i);
-      v.x *= gm.x; v.y *= gm.y; v.z *= gm.z; v.w *= gm.w;
-      *reinterpret_cast<float4*>(s.xn + i) = v;
-    }
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-  }
-  ss = wave_sum(ss);
-  mx = wave_max(mx);
-  const int w = threadIdx.x / kWave;
-  if ((threadIdx.x % kWave) == 0) {
-    s.sm->redf[w][0] = ss;
-    s.sm->redf[w][1] = mx;
-  }
-  __syncthreads();
-  ss = 0.f;
-  mx = 0.f;
-  for (int i = 0; i < kNW; ++i) {
-    ss += s.sm->redf[i][0];
-    mx = fmaxf(mx, s.sm->redf[i][1]);
-  }
-  const float rinv = norm ? 1.f / sqrtf(ss / (float)H + a.eps) : 1.f;
+  float ss = 0.f;
   if (norm) {
     for (int i = threadIdx.x * 4; i < H; i += kThreads * 4) {
-      float4 v = *reinterpret_cast<float4*>(s.xn + i);
-      v.x *= rinv; v.y *= rinv; v.z *= rinv; v.w *= rinv;
-      *reinterpret_cast<float4*>(s.xn + i) = v;
+      const float4 v = *reinterpret_cast<const float4*>(s.xn + i);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
+    ss = wave_sum(ss);
+    if ((threadIdx.x % kWave) == 0) s.sm->redf[threadIdx.x / kWave][0] = ss;
   }
-  float sc, xs;
-  digit_scale(mx * rinv, &sc, &xs);
   __syncthreads();
-  encode_vectors(s.xn, 1, H, &sc, s.xdig, s.xsum);
-  if (threadIdx.x == 0) s.sm->xs_x = xs;
+  float rinv = 1.f;
+  if (norm) {
+    ss = 0.f;
+    for (int i = 0; i < kNW; ++i) ss += s.sm->redf[i][0];
+    rinv = 1.f / sqrtf(ss / (float)H + a.eps);
+  }
+  // x_n = (x * gamma) * rinv in place (the router reads it), then its digits; the
+  // raw rows were copied to xres before the barrier above
+  if (norm || gamma)
+    encode_vectors<true>(s.xn, 1, H, rinv, gamma, s.xdig, s.xsum);
+  else
+    encode_vectors<false>(s.xn, 1, H, 1.f, nullptr, s.xdig, s.xsum);
   __syncthreads();
   return true;
 }
@@ -718,7 +728,7 @@ __device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, 
   const Xv hxv = xv_h(a);
   const int p = lane >> g.lGh, grp = lane & (g.Gh - 1);
   Dig D;
-  load_dig(D, s.xdig, s.xsum, grp, s.sm->xs_x);
+  load_dig(D, s.xdig, s.xsum, grp);
   bool first = true;
   for (int ib = i0 + w; ib < i1; ib += kBatch * kNW) {
     Slot G[kBatch], U[kBatch];
@@ -906,7 +916,7 @@ __device__ __forceinline__ void shared_from_regs(const DecodeArgs& a, const Lds&
   const Xv hxv = xv_h(a);
   const int p = lane >> g.lGh, grp = lane & (g.Gh - 1);
   Dig D;
-  load_dig(D, s.xdig, s.xsum, grp, s.sm->xs_x);
+  load_dig(D, s.xdig, s.xsum, grp);
   const unsigned epoch = epoch_of(a, t, l);
 #pragma unroll
   for (int j = 0; j < kShPre; ++j) {
@@ -1229,7 +1239,7 @@ __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s
     const int n = a.mode == MODE_EXPERT ? 1 : pass_count_of(a, s, j.pass);
     const int seg = n * g.Gi, grp = lane & (g.Gi - 1);
     if (j.pass != dig_pass) {
-      load_dig(D, s.hdig, s.hsum, j.li * g.Gi + grp, s.sm->hxs[j.li]);
+      load_dig(D, s.hdig, s.hsum, j.li * g.Gi + grp);
       dig_pass = j.pass;
     }
     float part = j.on ? slot_dot<BITS>(dp.d[k], D) * j.wk : 0.f;
@@ -1271,7 +1281,7 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
     ds[q] = j.on ? j.slot : 0;
   }
   Dig D;
-  load_dig(D, s.xdig, s.xsum, lane, s.sm->xs_x);
+  load_dig(D, s.xdig, s.xsum, lane);
   Slot G[kBatch], U[kBatch];
   issue_order();
 #pragma unroll
@@ -1374,27 +1384,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
       if (!wg_all(s.sm, ok)) return false;
     }
     SUBSTAMP(13);
-    float mx[kMaxPass];
-    for (int j = 0; j < nlist; ++j) {
-      mx[j] = 0.f;
-      for (int i = threadIdx.x * 4; i < I; i += kThreads * 4) {
-        const float4 v = *reinterpret_cast<const float4*>(hs + (size_t)j * I + i);
-        mx[j] = fmaxf(mx[j], fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-      }
-    }
-    const int w = threadIdx.x / kWave;
-    for (int j = 0; j < nlist; ++j) {
-      const float m = wave_max(mx[j]);
-      if ((threadIdx.x % kWave) == 0) s.sm->redf[w][j] = m;
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < nlist) {
-      float m = 0.f;
-      for (int i = 0; i < kNW; ++i) m = fmaxf(m, s.sm->redf[i][threadIdx.x]);
-      digit_scale(m, &s.sm->hsc[threadIdx.x], &s.sm->hxs[threadIdx.x]);
-    }
-    __syncthreads();
-    encode_vectors(hs, nlist, I, s.sm->hsc, s.hdig, s.hsum);
+    encode_vectors<false>(hs, nlist, I, 1.f, nullptr, s.hdig, s.hsum);
     __syncthreads();
   }
   SUBSTAMP(11);
@@ -1417,7 +1407,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
       const int nchunk = (r1 - r0 + Pp - 1) / Pp;
       if (w >= nchunk) continue;
       Dig D;
-      load_dig(D, s.hdig, s.hsum, li * g.Gi + grp, s.sm->hxs[li]);
+      load_dig(D, s.hdig, s.hsum, li * g.Gi + grp);
       for (int c0 = w; c0 < nchunk; c0 += kBatch * kNW) {
         Slot S[kBatch];
         int row[kBatch];
@@ -1729,10 +1719,10 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   const int xregion = words;
   a.lds_xn = words; words = up4(words + c.hidden);
   a.lds_xdig = words; words = up4(words + a.geo.Gh * kDigitStride);
-  a.lds_xsum = words; words = up4(words + 2 * a.geo.Gh);
+  a.lds_xsum = words; words = up4(words + 4 * a.geo.Gh);
   words = std::max(words, up4(xregion + hstage_words));
   a.lds_hdig = words; words = up4(words + nlist * Gi * kDigitStride);
-  a.lds_hsum = words; words = up4(words + 2 * nlist * Gi);
+  a.lds_hsum = words; words = up4(words + 4 * nlist * Gi);
   a.lds_acc = words; words = up4(words + kMaxPass * rpw);
   a.lds_xres = words; words = up4(words + rpw);
   a.n_lds_layers = (r.mode == MODE_EXPERT || !r.layers_dev) ? 0 : std::min(r.L, kLdsLayers);
