@@ -1192,7 +1192,7 @@ __device__ __forceinline__ DnJob down_job(const DecodeArgs& a, const Lds& s, int
     const int lgn = a.mode == MODE_EXPERT ? 0 : pass_lgn_of(a, s, pi);
     const int lseg = lgn + g.lGi, lPp = 6 - lseg;  // seg = n*Gi lanes, Pp = 64/seg rows
     const int nchunk = r0 < r1 ? (r1 - r0 + (1 << lPp) - 1) >> lPp : 0;
-    const int cnt = w < nchunk ? (nchunk - w + kNW - 1) >> 2 : 0;
+    const int cnt = w < nchunk ? (int)((unsigned)(nchunk - w + kNW - 1) / kNW) : 0;
     if (k < cnt) {
       const int c = w + k * kNW;
       const int grp = lane & (g.Gi - 1), kl = (lane >> g.lGi) & ((1 << lgn) - 1), p = lane >> lseg;
