@@ -34,8 +34,9 @@ def _mv(W, x):
     return [math.fsum(w * v for w, v in zip(row, x)) for row in W]
 
 
-def layer(x, router_rows, experts, shared, K, rmsnorm=True, residual=True, eps=1e-6):
-    """experts/shared: lists of (codes[3], scales[3], biases[3]) as nested lists."""
+def layer(x, router_rows, experts, shared, K, rmsnorm=True, residual=True, eps=1e-6, shared_gate=None):
+    """experts/shared: lists of (codes[3], scales[3], biases[3]) as nested lists.
+    shared_gate: one row per shared expert (its output scaled by 1/(1+e^-(row.x_n))) or None."""
     H = len(x)
     if rmsnorm:
         r = math.sqrt(math.fsum(v * v for v in x) / H + eps)
@@ -61,6 +62,10 @@ def layer(x, router_rows, experts, shared, K, rmsnorm=True, residual=True, eps=1
 
     outs = [run(experts[i]) for i in idx]
     sh = [run(s) for s in shared]
+    if shared_gate is not None:
+        for j, row in enumerate(shared_gate):
+            c = 1.0 / (1.0 + math.exp(-math.fsum(g * v for g, v in zip(row, xn))))
+            sh[j] = [c * v for v in sh[j]]
     y = []
     for i in range(H):
         terms = ([x[i]] if residual else []) + [w[k] * outs[k][i] for k in range(K)] + [o[i] for o in sh]

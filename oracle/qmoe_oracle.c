@@ -167,14 +167,15 @@ void orc_expert(int H, int I,
   free(g); free(u); free(h);
 }
 
-/* Combine: y = (residual ? x : 0) + sum_k w[k] * o[k] + sum_s o_shared[s].
+/* Combine: y = (residual ? x : 0) + sum_k w[k] * o[k] + sum_s c[s] * o_shared[s],
+ * with c[s] the shared-expert gate factor (c == NULL: every factor is 1).
  * o: [n_routed][H] then [n_shared][H], contiguous. */
 void orc_combine(int H, int n_routed, int n_shared, const double* x, int residual,
-                 const double* w, const double* o, double* y) {
+                 const double* w, const double* o, const double* c, double* y) {
   for (int i = 0; i < H; ++i) {
     double acc = residual ? x[i] : 0.0;
     for (int k = 0; k < n_routed; ++k) acc += w[k] * o[(size_t)k * H + i];
-    for (int s = 0; s < n_shared; ++s) acc += o[(size_t)(n_routed + s) * H + i];
+    for (int s = 0; s < n_shared; ++s) acc += (c ? c[s] : 1.0) * o[(size_t)(n_routed + s) * H + i];
     y[i] = acc;
   }
 }

@@ -14,7 +14,9 @@ Shaders", "Deferred GPU Expert Compute"):
    softmax over all logits and renormalisation over the selected K.
 4. Each selected expert and the shared expert: dequant mat-vec for gate and up,
    SwiGLU (silu on gate), dequant mat-vec for down.
-5. Weighted combine plus the shared expert plus the residual.
+5. Weighted combine plus the shared expert plus the residual. Optionally each
+   shared expert is scaled by a gate, sigmoid(g_s . x_n) (the "gate" of the page's
+   combine kernel, read as the shared-expert gate of this model family).
 
 Prefill (one layer, T tokens) adds the bf16 rounding points of a bf16 GEMM:
 x_b = bf16(x); x_n = RMSNorm(x_b); router from the unrounded x_n; expert input
@@ -72,7 +74,7 @@ def lib():
         L.orc_matvec.argtypes = [ctypes.c_int, ctypes.c_int, _U8, _U16, _U16, _D, ctypes.c_int, _D]
         L.orc_expert.argtypes = [ctypes.c_int, ctypes.c_int] + [_U8, _U16, _U16] * 3 + \
             [_D, ctypes.c_int, _D, _D]
-        L.orc_combine.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _D, ctypes.c_int, _D, _D, _D]
+        L.orc_combine.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _D, ctypes.c_int, _D, _D, _D, _D]
         _lib = L
     return _lib
 
@@ -158,7 +160,24 @@ def expert(canon, x, bf16_points=False, return_h=False):
     return (o, h) if return_h else o
 
 
-def combine(x, w, o_routed, o_shared, residual=True):
+def sigmoid(z):
+    """Logistic function in fp64 (the form that cannot overflow)."""
+    if z >= 0:
+        return 1.0 / (1.0 + math.exp(-z))
+    e = math.exp(z)
+    return e / (1.0 + e)
+
+
+def shared_gates(G, xn):
+    """Shared-expert gate factors sigmoid(G[s] . x_n), one per shared expert. The page
+    ("Flash-MoE", section "Metal Compute Shaders") lists a gate in its combine
+    kernel without defining it; the reading here is the shared-expert gate of this
+    model family: a float32 vector per shared expert, the dot product accumulated
+    like the router's (fp64, index order)."""
+    return np.array([sigmoid(float(z)) for z in router(np.asarray(G, dtype=np.float32), xn)])
+
+
+def combine(x, w, o_routed, o_shared, residual=True, gates=None):
     x = _c(x, np.float64)
     H = x.size
     o = _c(np.concatenate([np.reshape(o_routed, (-1, H)), np.reshape(o_shared, (-1, H))]), np.float64)
@@ -166,7 +185,9 @@ def combine(x, w, o_routed, o_shared, residual=True):
     y = np.empty(H, dtype=np.float64)
     n_r = np.reshape(o_routed, (-1, H)).shape[0]
     n_s = np.reshape(o_shared, (-1, H)).shape[0]
-    lib().orc_combine(H, n_r, n_s, _p(x, _D), int(residual), _p(w, _D), _p(o, _D), _p(y, _D))
+    c = None if gates is None else _c(gates, np.float64)
+    lib().orc_combine(H, n_r, n_s, _p(x, _D), int(residual), _p(w, _D), _p(o, _D),
+                      None if c is None else _p(c, _D), _p(y, _D))
     return y
 
 
@@ -176,11 +197,12 @@ class LayerResult:
 
 
 def layer_decode(x, router_W, get_expert, shared, K, rmsnorm_on=True, residual=True, gamma=None,
-                 eps=1e-6, boosted=(), sel=None, by_sel=False, force_idx=None):
+                 eps=1e-6, boosted=(), sel=None, by_sel=False, force_idx=None, shared_gate=None):
     """One decode layer for one token.
 
     get_expert(e) -> canonical expert e; shared: list of canonical shared experts.
     force_idx: a selected set to use instead of the oracle's own (near-tie follow).
+    shared_gate: [S][H] float32 or None (shared experts added with weight 1).
     """
     x = np.asarray(x, dtype=np.float64)
     xn = rmsnorm(x, gamma, eps) if rmsnorm_on else x.copy()
@@ -191,12 +213,13 @@ def layer_decode(x, router_W, get_expert, shared, K, rmsnorm_on=True, residual=T
         w = weights_for(logits, idx)
     o_r = np.stack([expert(get_expert(int(e)), xn) for e in idx])
     o_s = np.stack([expert(c, xn) for c in shared]) if shared else np.zeros((0, x.size))
-    y = combine(x, w, o_r, o_s, residual)
+    gates = shared_gates(shared_gate, xn) if (shared_gate is not None and shared) else None
+    y = combine(x, w, o_r, o_s, residual, gates=gates)
     return LayerResult(y, idx, w, gap, logits, xn)
 
 
 def prefill_token(x, router_W, get_expert, shared, K, sel, gamma=None, eps=1e-6, by_sel=True,
-                  boosted=(), rmsnorm_on=True, residual=True, force_idx=None):
+                  boosted=(), rmsnorm_on=True, residual=True, force_idx=None, shared_gate=None):
     """One token of the batched prefill with the bf16 rounding points (the input,
     the expert input, every dequantised weight and the SwiGLU output are rounded
     to bf16; the router sees the unrounded normalised input). Selection uses
@@ -213,7 +236,9 @@ def prefill_token(x, router_W, get_expert, shared, K, sel, gamma=None, eps=1e-6,
     a = round_bf16(xn)
     o_r = np.stack([expert(get_expert(int(e)), a, bf16_points=True) for e in idx])
     o_s = np.stack([expert(c, a, bf16_points=True) for c in shared]) if shared else np.zeros((0, xb.size))
-    y = combine(xb, w, o_r, o_s, residual=residual)
+    # the gate sees the unrounded x_n, as the router does
+    gates = shared_gates(shared_gate, xn) if (shared_gate is not None and shared) else None
+    y = combine(xb, w, o_r, o_s, residual=residual, gates=gates)
     return LayerResult(y, idx, w, gap, logits, xn)
 
 
@@ -221,7 +246,7 @@ NEAR_TIE = 1e-5
 
 
 def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=None,
-                 rmsnorm_on=True, residual=True, eps=1e-6, follow=None, tokens=None):
+                 rmsnorm_on=True, residual=True, eps=1e-6, follow=None, tokens=None, shared_gate_of=None):
     """Decode stack: for each token t in order, for each layer l, x <- layer(x).
     Attention is the identity between MoE blocks.
 
@@ -245,14 +270,16 @@ def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=N
             if boost is not None and t > 0 and prev is not None:
                 ps = np.sort(prev[l])
                 boosted = tuple(int(ps[j]) for j in range(K) if boost[t][l][j])
+            sg = None if shared_gate_of is None else shared_gate_of(l)
             r = layer_decode(x, router_of(l), lambda e, l=l: expert_of(l, e), shared_of(l), K,
-                             rmsnorm_on=rmsnorm_on, residual=residual, eps=eps, boosted=boosted)
+                             rmsnorm_on=rmsnorm_on, residual=residual, eps=eps, boosted=boosted,
+                             shared_gate=sg)
             if follow is not None:
                 f = follow(t, l, r.idx, r.gap)
                 if f is not None and set(int(v) for v in f) != set(int(v) for v in r.idx):
                     r = layer_decode(x, router_of(l), lambda e, l=l: expert_of(l, e), shared_of(l), K,
                                      rmsnorm_on=rmsnorm_on, residual=residual, eps=eps,
-                                     boosted=boosted, force_idx=f)
+                                     boosted=boosted, force_idx=f, shared_gate=sg)
             sets[t, l] = np.sort(r.idx)
             gaps[t, l] = r.gap
             x = r.y

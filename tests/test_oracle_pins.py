@@ -204,6 +204,67 @@ def test_layer_matches_pure_python_brute_force(rms, res):
     np.testing.assert_allclose(r.y, yb, rtol=0, atol=1e-12 * scale)
 
 
+def test_layer_with_shared_gate_matches_pure_python_brute_force():
+    rng = np.random.default_rng(15)
+    H, I, E, K = 64, 64, 8, 2
+    experts = [rand_canon(rng, H, I, s_sigma=0.1, b_sigma=0.05) for _ in range(E)]
+    shared = [rand_canon(rng, H, I, s_sigma=0.1, b_sigma=0.05)]
+    W = rng.normal(0, 0.3, (E, H)).astype(np.float32)
+    G = rng.normal(0, 0.3, (1, H)).astype(np.float32)
+    x = rng.normal(size=H)
+
+    def tolist(c):
+        return ([m.tolist() for m in c[0]], [m.tolist() for m in c[1]], [m.tolist() for m in c[2]])
+
+    yb, ib, wb = brute.layer(list(x), [list(map(float, r)) for r in W], [tolist(e) for e in experts],
+                             [tolist(s) for s in shared], K, shared_gate=[list(map(float, r)) for r in G])
+    r = ref.layer_decode(x, W, lambda e: experts[e], shared, K, shared_gate=G)
+    assert list(r.idx) == ib
+    scale = max(abs(v) for v in yb)
+    np.testing.assert_allclose(r.y, yb, rtol=0, atol=1e-12 * scale)
+
+
+def _gate_layers(seed):
+    rng = np.random.default_rng(seed)
+    H, I, E, K = 128, 64, 8, 2
+    experts = [rand_canon(rng, H, I) for _ in range(E)]
+    shared = [rand_canon(rng, H, I, s_sigma=0.05)]
+    W = rng.normal(0, 0.02, (E, H)).astype(np.float32)
+    x = rng.normal(size=H)
+    full = ref.layer_decode(x, W, lambda e: experts[e], shared, K)
+    # the same routed part without the shared expert: combine of the same selection
+    o_r = np.stack([ref.expert(experts[int(e)], full.xn) for e in full.idx])
+    none = ref.combine(x, full.w, o_r, np.zeros((0, H)))
+    return x, W, experts, shared, K, full, none
+
+
+def test_shared_gate_zero_vector_halves_the_shared_expert():
+    x, W, experts, shared, K, full, none = _gate_layers(16)
+    g = ref.layer_decode(x, W, lambda e: experts[e], shared, K, shared_gate=np.zeros((1, x.size), np.float32))
+    # sigmoid(0) = 1/2 exactly: the gated output is the midpoint of "shared weight 1"
+    # and "no shared expert" (the combine is linear in the shared weight)
+    np.testing.assert_allclose(g.y, 0.5 * (full.y + none), rtol=0, atol=1e-13 * np.abs(full.y).max())
+    assert list(g.idx) == list(full.idx)
+
+
+@pytest.mark.parametrize("k,m", [(3, 2.0), (77, -1.5), (0, 40.0)])
+def test_shared_gate_one_hot_row_closed_form(k, m):
+    x, W, experts, shared, K, full, none = _gate_layers(17)
+    G = np.zeros((1, x.size), np.float32)
+    G[0, k] = m
+    g = ref.layer_decode(x, W, lambda e: experts[e], shared, K, shared_gate=G)
+    c = 1.0 / (1.0 + math.exp(-m * full.xn[k]))   # the textbook logistic of one product
+    expect = none + c * (full.y - none)
+    np.testing.assert_allclose(g.y, expect, rtol=0, atol=1e-12 * np.abs(full.y).max())
+
+
+def test_shared_gate_saturates_to_no_shared_expert():
+    x, W, experts, shared, K, full, none = _gate_layers(18)
+    G = (-1000.0 * np.sign(full.xn)).astype(np.float32)[None, :]   # G . x_n = -1000 sum|x_n|
+    g = ref.layer_decode(x, W, lambda e: experts[e], shared, K, shared_gate=G)
+    np.testing.assert_array_equal(g.y, none)
+
+
 def test_zero_experts_stack_is_identity():
     rng = np.random.default_rng(11)
     H, I, E, K, L = 128, 64, 16, 4, 5
