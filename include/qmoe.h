@@ -74,6 +74,13 @@ typedef struct {
   const void* shared;    /* n_shared packed experts (NULL if n_shared == 0) */
   const float* router_w; /* [n_experts][hidden] float32, row-major */
   const float* gamma;    /* [hidden] RMSNorm weight, or NULL for all ones */
+  /* [n_shared][hidden] float32 shared-expert gate, or NULL. When given, shared
+   * expert s enters the combine scaled by sigmoid(shared_gate[s] . x_n) instead of
+   * with weight 1 (x_n: the normalised layer input the router sees). The page
+   * ("Flash-MoE", section "Metal Compute Shaders") lists a gate in its combine
+   * kernel without defining it; this is the shared-expert gate of that model
+   * family. 16-byte aligned. Decode (any T) and prefill both honour it. */
+  const float* shared_gate;
 } moe_layer_weights;
 
 /* Bytes of one packed expert (gate, up, down). 0 if the config is invalid.

@@ -43,7 +43,8 @@ class Config(ctypes.Structure):
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [("experts", ctypes.c_void_p), ("shared", ctypes.c_void_p),
-                ("router_w", ctypes.c_void_p), ("gamma", ctypes.c_void_p)]
+                ("router_w", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("shared_gate", ctypes.c_void_p)]
 
 
 _lib = None
@@ -126,9 +127,10 @@ def moe_expert_forward(cfg, packed_expert, T, x, y, ws, stream=None):
                                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def layer_weights(experts, shared, router_w, gamma=None):
+def layer_weights(experts, shared, router_w, gamma=None, shared_gate=None):
     return LayerWeights(experts.data_ptr(), shared.data_ptr() if shared is not None else None,
-                        router_w.data_ptr(), gamma.data_ptr() if gamma is not None else None)
+                        router_w.data_ptr(), gamma.data_ptr() if gamma is not None else None,
+                        shared_gate.data_ptr() if shared_gate is not None else None)
 
 
 def moe_layer_forward(cfg, layer, T, x, y, ws, sel_bias=None, boosted=None, idx_out=None, w_out=None,

@@ -85,12 +85,14 @@ moe_status upload_layers(const moe_config& c, int L, const moe_layer_weights* la
       REQUIRE(w.experts && w.router_w, MOE_ERR_ARG, "layer %d: experts/router_w is NULL", l0 + i);
       REQUIRE(c.n_shared == 0 || w.shared, MOE_ERR_ARG, "layer %d: shared is NULL", l0 + i);
       REQUIRE(aligned(w.experts, 256) && aligned(w.router_w, 256) &&
-                  (!w.shared || aligned(w.shared, 256)) && (!w.gamma || aligned(w.gamma, 16)),
+                  (!w.shared || aligned(w.shared, 256)) && (!w.gamma || aligned(w.gamma, 16)) &&
+                  (!w.shared_gate || aligned(w.shared_gate, 16)),
               MOE_ERR_ALIGN, "layer %d: weight pointers must be 256-byte aligned", l0 + i);
       tmp[i].experts = static_cast<const uint8_t*>(w.experts);
       tmp[i].shared = static_cast<const uint8_t*>(w.shared);
       tmp[i].router = w.router_w;
       tmp[i].gamma = w.gamma;
+      tmp[i].sgate = c.n_shared > 0 ? w.shared_gate : nullptr;
     }
     hipError_t e = hipMemcpyAsync(dev + l0, tmp, sizeof(LayerPtrs) * n, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "uploading the layer table");
@@ -166,7 +168,7 @@ moe_status moe_route(const moe_config* cfg, int32_t T, const float* x, const flo
   hipStream_t st = (hipStream_t)stream;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   const WsLayout wl = ws_layout(*cfg, T, 1);
-  moe_layer_weights lw = {router_w, nullptr, router_w, gamma};  // experts unused when routing
+  moe_layer_weights lw = {router_w, nullptr, router_w, gamma, nullptr};  // experts unused when routing
   moe_config c1 = *cfg;
   c1.n_shared = 0;
   s = upload_layers(c1, 1, &lw, w8, wl, st);
@@ -237,8 +239,9 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_layer_weights* lay
     REQUIRE(cfg->n_shared == 0 || layer->shared, MOE_ERR_ARG, "shared is NULL");
     REQUIRE(aligned(layer->experts, 256) && aligned(layer->router_w, 256) &&
                 (!layer->shared || aligned(layer->shared, 256)) &&
-                (!layer->gamma || aligned(layer->gamma, 16)),
-            MOE_ERR_ALIGN, "weight pointers must be 256-byte aligned (gamma 16-byte)");
+                (!layer->gamma || aligned(layer->gamma, 16)) &&
+                (!layer->shared_gate || aligned(layer->shared_gate, 16)),
+            MOE_ERR_ALIGN, "weight pointers must be 256-byte aligned (gamma, shared_gate 16-byte)");
     std::string msg;
     s = prefill_forward(*cfg, layer, T, x, y, sel_bias, boosted, idx_out, w_out, w8, ws_bytes, st,
                         &msg);
@@ -263,6 +266,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_layer_weights* lay
   r.ws = w8;
   r.wl = wl;
   r.phased = (cfg->flags & MOE_F_PHASED) != 0;
+  r.any_sgate = cfg->n_shared > 0 && layer->shared_gate != nullptr;
   return run_decode(r, st);
 }
 
@@ -299,6 +303,8 @@ moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_layer_we
   r.ws = w8;
   r.wl = wl;
   r.phased = (cfg->flags & MOE_F_PHASED) != 0;
+  r.any_sgate = false;
+  for (int l = 0; l < L; ++l) r.any_sgate = r.any_sgate || (cfg->n_shared > 0 && layers[l].shared_gate);
   return run_decode(r, st);
 }
 

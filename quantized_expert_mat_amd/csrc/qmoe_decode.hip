@@ -91,6 +91,7 @@ struct DecodeArgs {
   unsigned long long* trace_wg;  // optional [L][nwg][4] stamps of every workgroup at token 2
   int nwg;
   int rpw;                       // phase C output rows per workgroup
+  int any_sgate;                 // some layer has a shared-expert gate
   int exact_rows;                // nwg * rpw == H: every workgroup owns exactly rpw rows
   int npass;
   int pass_first[kMaxPass], pass_count[kMaxPass];
@@ -113,6 +114,8 @@ struct Small {
   int sel_idx[kMaxK];
   float sel_w[kMaxK];
   int ok;
+  float sgc[kMaxShared];       // shared-expert gate factors of the current layer
+  float sgp[kNW][kMaxShared];  // their per-wave partial dot products
   unsigned long long* tr;  // trace row (workgroup 0, thread 0 only)
   // Stamps are kept here and written out once per layer, after the layer's last
   // loads are issued: a store in the middle of a phase would be waited for by the
@@ -168,6 +171,7 @@ __device__ inline LayerPtrs get_layer(const DecodeArgs& a, const Lds& s, int l) 
     p.shared = reinterpret_cast<const uint8_t*>(q[1]);
     p.router = reinterpret_cast<const float*>(q[2]);
     p.gamma = reinterpret_cast<const float*>(q[3]);
+    p.sgate = reinterpret_cast<const float*>(q[4]);
   } else {
     p = a.layers[l];
   }
@@ -930,6 +934,42 @@ __device__ __forceinline__ void shared_from_regs(const DecodeArgs& a, const Lds&
   }
 }
 
+// Shared-expert gate factors c_s = sigmoid(g_s . x_n) of layer l into LDS (x_n in
+// LDS); workgroup 0 also publishes them for a following phase launch. Layers
+// without a gate keep weight 1 (list_expert reads the factor only when some layer
+// has a gate).
+__device__ __forceinline__ void shared_gate_factors(const DecodeArgs& a, const Lds& s, int l) {
+  const int S = a.S, H = a.geo.H;
+  const float* G = a.any_sgate ? get_layer(a, s, l).sgate : nullptr;
+  if (G) {
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    for (int sh = 0; sh < S; ++sh) {
+      float part = 0.f;
+      for (int i = threadIdx.x * 4; i < H; i += kThreads * 4) {
+        const float4 gv = ldg_f4(G + (size_t)sh * H + i);
+        const float4 xv = *reinterpret_cast<const float4*>(s.xn + i);
+        part = fmaf(gv.x, xv.x, part);
+        part = fmaf(gv.y, xv.y, part);
+        part = fmaf(gv.z, xv.z, part);
+        part = fmaf(gv.w, xv.w, part);
+      }
+      part = wave_sum(part);
+      if (lane == 0) s.sm->sgp[w][sh] = part;
+    }
+    __syncthreads();
+  }
+  if ((int)threadIdx.x < S) {
+    float c = 1.f;
+    if (G) {
+      float z = 0.f;
+      for (int i = 0; i < kNW; ++i) z += s.sm->sgp[i][threadIdx.x];
+      c = 1.f / (1.f + expf(-z));
+    }
+    s.sm->sgc[threadIdx.x] = c;
+    if (blockIdx.x == 0) st_coh(a.sel + 2 * kMaxK + threadIdx.x, __float_as_int(c));
+  }
+}
+
 template <int BITS>
 __device__ __forceinline__ bool phase_a(const DecodeArgs& a, const Lds& s, int t, int l,
                                         StaticPre& sp, bool preloaded) {
@@ -941,6 +981,7 @@ __device__ __forceinline__ bool phase_a(const DecodeArgs& a, const Lds& s, int t
   split_range(a.E, a.nwg, blockIdx.x, e0, e1);
   if (a.pre_router) router_from_regs(a, s, t, l, sp);
   else router_rows(a, s, t, l, e0, e1);
+  if (a.any_sgate && a.mode == MODE_LAYER) shared_gate_factors(a, s, l);
   SUBSTAMP(9);
   if (a.mode == MODE_LAYER && a.S > 0) {
     if (a.pre_shared) {
@@ -1161,7 +1202,7 @@ __device__ inline const uint8_t* list_expert(const DecodeArgs& a, const Lds& s, 
     wk = s.sm->sel_w[li];
     return get_layer(a, s, l).experts + (size_t)s.sm->sel_idx[li] * g.expert_bytes;
   }
-  wk = 1.f;
+  wk = a.any_sgate ? s.sm->sgc[li - a.K] : 1.f;
   return get_layer(a, s, l).shared + (size_t)(li - a.K) * g.expert_bytes;
 }
 
@@ -1506,6 +1547,7 @@ __device__ __forceinline__ void specialise(DecodeArgs& a) {
   a.pass_first[0] = 0; a.pass_count[0] = kSpecK;
   a.pass_first[1] = kSpecK; a.pass_count[1] = kSpecS;
   a.const_pass = 1;
+  a.any_sgate = 0;
   a.pre_router = a.pre_shared = a.pre_down = 1;
 }
 
@@ -1527,7 +1569,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
     const __attribute__((address_space(1))) unsigned long long* src =
         (const __attribute__((address_space(1))) unsigned long long*)(uintptr_t)a.layers;
     unsigned long long* dst = reinterpret_cast<unsigned long long*>(lds_raw + a.lds_layers);
-    for (int i = threadIdx.x; i < 4 * a.n_lds_layers; i += kThreads) dst[i] = src[i];
+    for (int i = threadIdx.x; i < (int)(sizeof(LayerPtrs) / 8) * a.n_lds_layers; i += kThreads) dst[i] = src[i];
   }
   __syncthreads();
   if constexpr (SPEC) {
@@ -1568,6 +1610,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
             s.sm->sel_idx[threadIdx.x] = ld_coh(a.sel + threadIdx.x);
             s.sm->sel_w[threadIdx.x] = __int_as_float(ld_coh(a.sel + kMaxK + threadIdx.x));
           }
+          if ((int)threadIdx.x < a.S)
+            s.sm->sgc[threadIdx.x] = __int_as_float(ld_coh(a.sel + 2 * kMaxK + threadIdx.x));
           __syncthreads();
         }
         if (!phase_c<BITS>(a, s, t, l, a.pre_down, dp, false, sp, false)) return;
@@ -1707,6 +1751,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
     return hipErrorInvalidValue;
   }
   a.rpw = rpw;
+  a.any_sgate = r.any_sgate ? 1 : 0;
   a.exact_rows = (long long)rpw * nwg == c.hidden;
   a.nwg = nwg;
   const int nlist = r.mode == MODE_EXPERT ? 1 : c.top_k + c.n_shared;
@@ -1761,7 +1806,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   const bool spec = r.mode == MODE_LAYER && !r.phased && c.hidden == kSpecH && c.inter == kSpecI &&
                     a.E == kSpecE && a.K == kSpecK && a.S == kSpecS && nwg == kSpecNwg &&
                     a.pre_router && a.pre_shared && a.pre_down && a.n_lds_layers == r.L &&
-                    (g_pre_mask & 8);
+                    !r.any_sgate && (g_pre_mask & 8);
   auto kern = c.bits == 4 ? (spec ? decode_kernel<4, true> : decode_kernel<4, false>)
                           : (spec ? decode_kernel<2, true> : decode_kernel<2, false>);
   static bool attr_set[4] = {false, false, false, false};

@@ -86,6 +86,7 @@ struct LayerPtrs {
   const uint8_t* shared;
   const float* router;
   const float* gamma;
+  const float* sgate;  // [n_shared][H] shared-expert gate or NULL
 };
 
 // Workspace layout (byte offsets from the workspace base; all 256-B aligned).
@@ -106,7 +107,8 @@ inline WsLayout ws_layout(const moe_config& c, int T, int L) {
   w.xbuf = o; o = align256(o + kRep * sizeof(uint64_t) * c.hidden);
   w.logits = o; o = align256(o + kRep * sizeof(uint64_t) * c.n_experts);
   w.hbuf = o; o = align256(o + kRep * sizeof(uint64_t) * (size_t)(kMaxK + kMaxShared) * c.inter);
-  w.sel = o; o = align256(o + 2 * sizeof(int) * kMaxK);
+  // selection words: [kMaxK] indices, [kMaxK] weights, [kMaxShared] shared-gate factors
+  w.sel = o; o = align256(o + sizeof(int) * (2 * kMaxK + kMaxShared));
   w.prev = o; o = align256(o + sizeof(uint64_t) * 2 * (size_t)(L > 0 ? L : 1) * kMaxK);
   w.layers = o; o = align256(o + sizeof(LayerPtrs) * (size_t)(L > 0 ? L : 1));
   w.total = o;
@@ -131,6 +133,7 @@ struct DecodeRequest {
   uint8_t* ws;
   WsLayout wl;
   bool phased;
+  bool any_sgate;  // some layer has a shared-expert gate
 };
 
 hipError_t launch_pack(const Geo& geo, int n, const uint8_t* codes, const uint16_t* scales,

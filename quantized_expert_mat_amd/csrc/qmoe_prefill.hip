@@ -56,7 +56,7 @@ constexpr int kPairBits = 14;      // pair index bits in a sort key
 // ---------------------------------------------------------------------------
 struct PLayout {
   int Tc, rows, max_tiles;
-  size_t err, a, xn, logits, idx, wts, pos, rowtok, thin, thick, hbuf, obuf, total;
+  size_t err, a, xn, logits, idx, wts, pos, rowtok, thin, thick, hbuf, obuf, sgc, total;
 };
 
 PLayout p_layout(const moe_config& c, int T) {
@@ -79,6 +79,7 @@ PLayout p_layout(const moe_config& c, int T) {
   p.thick = o; o = align256(o + 16 * (size_t)(p.max_tiles + 1));
   p.hbuf = o; o = align256(o + (size_t)p.rows * c.inter * 2);
   p.obuf = o; o = align256(o + (size_t)p.rows * c.hidden * 4);
+  p.sgc = o; o = align256(o + (size_t)p.Tc * kMaxShared * 4);
   p.total = o;
   return p;
 }
@@ -98,6 +99,7 @@ struct PArgs {
   float* w_out;           // [n][K] or null
   const uint8_t* experts;
   const uint8_t* shared;
+  const float* sgate;     // [S][H] shared-expert gate or null
   unsigned* err;
   uint16_t* a;            // [Tc][H] bf16 expert input
   float* xn;              // [Tc][H] normalised input (router operand)
@@ -110,6 +112,7 @@ struct PArgs {
   int4* thick;            // m-tiles of 17..64 rows, same format
   uint16_t* hbuf;         // [rows][I] bf16 SwiGLU output
   float* obuf;            // [rows][H] float32 expert outputs
+  float* sgc;             // [Tc][kMaxShared] shared-expert gate factors (with sgate)
 };
 
 __device__ inline float bf16_round(float v) {
@@ -142,12 +145,15 @@ __device__ inline unsigned ord_f32(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: x_b = bf16(x); x_n = RMSNorm(x_b) (or x_b); A = bf16(x_n).
+// prep: x_b = bf16(x); x_n = RMSNorm(x_b) (or x_b); A = bf16(x_n); with a
+// shared-expert gate also c_s = sigmoid(g_s . x_n) from the unrounded x_n.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prep_kernel(PArgs a) {
   const int t = blockIdx.x;
   const float* xr = a.x + (size_t)t * a.H;
   __shared__ float red[4];
+  __shared__ float gred[kMaxShared][4];
+  float gz[kMaxShared] = {};
   float ss = 0.f;
   for (int k = threadIdx.x * 4; k < a.H; k += 1024) {
     const float4 v = *reinterpret_cast<const float4*>(xr + k);
@@ -174,6 +180,26 @@ __global__ __launch_bounds__(256) void prep_kernel(PArgs a) {
     *reinterpret_cast<float4*>(a.xn + (size_t)t * a.H + k) = make_float4(n0, n1, n2, n3);
     *reinterpret_cast<uint2*>(a.a + (size_t)t * a.H + k) =
         make_uint2(pack_bf16(n0, n1), pack_bf16(n2, n3));
+    if (a.sgate) {
+      for (int sh = 0; sh < a.S; ++sh) {
+        const float4 g = *reinterpret_cast<const float4*>(a.sgate + (size_t)sh * a.H + k);
+        gz[sh] = fmaf(g.x, n0, gz[sh]);
+        gz[sh] = fmaf(g.y, n1, gz[sh]);
+        gz[sh] = fmaf(g.z, n2, gz[sh]);
+        gz[sh] = fmaf(g.w, n3, gz[sh]);
+      }
+    }
+  }
+  if (a.sgate) {
+    for (int sh = 0; sh < a.S; ++sh) {
+      const float v = wave_sum_f(gz[sh]);
+      if ((threadIdx.x & 63) == 0) gred[sh][threadIdx.x >> 6] = v;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < a.S) {
+      const float z = gred[threadIdx.x][0] + gred[threadIdx.x][1] + gred[threadIdx.x][2] + gred[threadIdx.x][3];
+      a.sgc[(size_t)t * kMaxShared + threadIdx.x] = 1.f / (1.f + expf(-z));
+    }
   }
 }
 
@@ -684,7 +710,8 @@ __global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// combine: y[t] = x_b[t] (residual) + sum_k w[t][k] o[pos[t][k]] + sum_s o_s[t].
+// combine: y[t] = x_b[t] (residual) + sum_k w[t][k] o[pos[t][k]] + sum_s c_s o_s[t]
+// (c_s = 1 without a shared-expert gate).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(PArgs a) {
   const int h4 = a.H / 4;
@@ -707,7 +734,13 @@ __global__ __launch_bounds__(256) void combine_kernel(PArgs a) {
   for (int s = 0; s < a.S; ++s) {
     const float4 o =
         *reinterpret_cast<const float4*>(a.obuf + (np + (size_t)s * a.n + t) * a.H + k);
-    acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+    if (a.sgate) {
+      const float c = a.sgc[(size_t)t * kMaxShared + s];
+      acc.x = fmaf(c, o.x, acc.x); acc.y = fmaf(c, o.y, acc.y);
+      acc.z = fmaf(c, o.z, acc.z); acc.w = fmaf(c, o.w, acc.w);
+    } else {
+      acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+    }
   }
   *reinterpret_cast<float4*>(a.y + (size_t)t * a.H + k) = acc;
 }
@@ -747,6 +780,7 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
   a.gamma = lw->gamma;
   a.experts = static_cast<const uint8_t*>(lw->experts);
   a.shared = static_cast<const uint8_t*>(lw->shared);
+  a.sgate = c.n_shared > 0 ? lw->shared_gate : nullptr;
   a.err = reinterpret_cast<unsigned*>(ws + pl.err);
   a.a = reinterpret_cast<uint16_t*>(ws + pl.a);
   a.xn = reinterpret_cast<float*>(ws + pl.xn);
@@ -759,6 +793,7 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
   a.thick = reinterpret_cast<int4*>(ws + pl.thick);
   a.hbuf = reinterpret_cast<uint16_t*>(ws + pl.hbuf);
   a.obuf = reinterpret_cast<float*>(ws + pl.obuf);
+  a.sgc = reinterpret_cast<float*>(ws + pl.sgc);
 
   static bool attr_done = false;
   const size_t group_lds_max = sizeof(unsigned) * (kSortMax + 2 * kMaxE + 1024);

@@ -18,9 +18,12 @@ def config_for(w: wl.WorkloadConfig, extra_flags=0):
 class DeviceLayer:
     """One layer of packed experts, shared experts and router weights on the GPU."""
 
-    def __init__(self, w: wl.WorkloadConfig, layer: int, device="cuda", chunk=32, ws=None):
+    def __init__(self, w: wl.WorkloadConfig, layer: int, device="cuda", chunk=32, ws=None, gated=False):
         import torch
         self.w, self.layer = w, layer
+        self.sgate = None
+        if gated and w.n_shared:
+            self.sgate = torch.from_numpy(wl.shared_gate_weights(w.seed, layer, w.n_shared, w.hidden)).to(device)
         self.cfg = config_for(w)
         spec = w.expert_spec()
         nb = q.moe_packed_expert_bytes(self.cfg)
@@ -58,7 +61,8 @@ class DeviceLayer:
         q.moe_device_status(ws)
 
     def weights(self):
-        return q.layer_weights(self.experts, self.shared if self.w.n_shared else None, self.router)
+        return q.layer_weights(self.experts, self.shared if self.w.n_shared else None, self.router,
+                               shared_gate=self.sgate)
 
 
 class HostLayer:
@@ -79,6 +83,9 @@ class HostLayer:
 
     def shared(self):
         return [self.expert(self.w.n_experts + s) for s in range(self.w.n_shared)]
+
+    def shared_gate(self):
+        return wl.shared_gate_weights(self.w.seed, self.layer, self.w.n_shared, self.w.hidden)
 
 
 class DeviceCanonicalLayer:

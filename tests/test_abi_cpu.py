@@ -79,6 +79,10 @@ def test_null_misaligned_and_small_workspace_rejected():
     cfg_sel = cfg.with_flags(q.MOE_F_SELECT_BY_BIAS)
     assert L.moe_layer_forward(ctypes.byref(cfg_sel), ctypes.byref(lw), 1, p, p, None, None, None, None, p,
                                big, None) == q.MOE_ERR_ARG
+    # a shared-expert gate must be 16-byte aligned
+    lw_gate = q.LayerWeights(1 << 20, 1 << 20, 1 << 20, None, (1 << 20) + 4)
+    assert L.moe_layer_forward(ctypes.byref(cfg), ctypes.byref(lw_gate), 1, p, p, None, None, None, None,
+                               p, big, None) == q.MOE_ERR_ALIGN
     arr = (q.LayerWeights * 1)(lw)
     assert L.moe_stack_decode(ctypes.byref(cfg_sel), 1, arr, 1, p, None, p, None, None, p, big,
                               None) == q.MOE_ERR_ARG

@@ -29,10 +29,10 @@ import numpy as np
 
 __all__ = [
     "GOLDEN", "KEY0", "KIND_CODES", "KIND_SCALE", "KIND_BIAS", "KIND_ROUTER",
-    "KIND_X", "KIND_BOOST", "KIND_GUMBEL", "KIND_RANK",
+    "KIND_X", "KIND_BOOST", "KIND_GUMBEL", "KIND_RANK", "KIND_SGATE",
     "mix64", "stream_key", "words", "codes", "normals", "f32_from_normals",
     "bf16_bits_from_f32", "bf16_bits_to_f32", "bf16_from_normals",
-    "ExpertSpec", "expert_canonical", "router_weights", "tokens_x",
+    "ExpertSpec", "expert_canonical", "router_weights", "shared_gate_weights", "tokens_x",
     "boost_mask", "zipf_gumbel_scores", "WorkloadConfig", "CONFIGS",
 ]
 
@@ -44,6 +44,7 @@ _C2 = np.uint64(0x94D049BB133111EB)
 
 KIND_CODES, KIND_SCALE, KIND_BIAS, KIND_ROUTER = 1, 2, 3, 4
 KIND_X, KIND_BOOST, KIND_GUMBEL, KIND_RANK = 5, 6, 7, 8
+KIND_SGATE = 9
 
 
 def mix64(z):
@@ -148,6 +149,12 @@ def expert_canonical(spec: ExpertSpec, seed: int, layer: int, expert: int):
 def router_weights(seed, layer, n_experts, hidden, sigma=0.02):
     n = normals(stream_key(seed, KIND_ROUTER, layer, 0, 0), n_experts * hidden)
     return f32_from_normals(n, sigma).reshape(n_experts, hidden)
+
+
+def shared_gate_weights(seed, layer, n_shared, hidden, sigma=0.02):
+    """Shared-expert gate vectors [n_shared][hidden] float32 ~ N(0, sigma)."""
+    n = normals(stream_key(seed, KIND_SGATE, layer, 0, 0), n_shared * hidden)
+    return f32_from_normals(n, sigma).reshape(n_shared, hidden)
 
 
 def tokens_x(seed, n_tokens, hidden, first_token=0):
