@@ -26,7 +26,7 @@
  *  - Two calls may run concurrently only on different streams with disjoint
  *    workspaces and outputs.
  *  - Supported shapes: hidden and inter are 64 * 2^k (64 .. 4096); group 64;
- *    bits 4 or 2; 1 <= top_k <= 8, top_k <= n_experts <= 1024; n_shared 0..2.
+ *    bits 4 or 2; 1 <= top_k <= 16, top_k <= n_experts <= 1024; n_shared 0..2.
  */
 #ifndef QMOE_H
 #define QMOE_H

@@ -1031,7 +1031,8 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) mk[j] = m[j < K ? j : 0];
 #pragma unroll
-    for (int q = 0; q < kMaxK / 2; ++q) pp[q] = ld_coh4(rp, 16 * q);
+    for (int q = 0; q < kMaxK / 2; ++q)
+      if (2 * q < K) pp[q] = ld_coh4(rp, 16 * q);
   } else if (a.boosted) {
     const int* b = a.boosted + (size_t)t * K;
     int bv[kMaxK];
@@ -1103,7 +1104,8 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
           }
         }
 #pragma unroll
-        for (int q = 0; q < kMaxK / 2; ++q) pp[q] = ld_coh4(rp, 16 * q);
+        for (int q = 0; q < kMaxK / 2; ++q)
+          if (2 * q < K) pp[q] = ld_coh4(rp, 16 * q);
       }
 #pragma unroll
       for (int q = 0; q < kMaxK / 2; ++q) {
@@ -1124,7 +1126,7 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
         if (sb) sc = by_bias ? sb[min(e, E - 1)] : lg + sb[min(e, E - 1)];
         unsigned tier = 0;
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) tier |= (bst[j] == e) ? 1u : 0u;
+        for (int j = 0; j < kMaxK; ++j) tier |= (j < K && bst[j] == e) ? 1u : 0u;
         key[r4] = e < E ? ((unsigned long long)(tier + 1u) << 42) |
                               ((unsigned long long)ord_f32(sc) << 10) |
                               (unsigned long long)(kMaxE - 1 - e)

@@ -11,7 +11,7 @@ namespace qmoe {
 
 constexpr int kWave = 64;
 constexpr int kGroup = 64;
-constexpr int kMaxK = 8;
+constexpr int kMaxK = 16;  // routed experts per token (the model's native top-k is 10)
 constexpr int kMaxE = 1024;
 constexpr int kMaxShared = 2;
 constexpr int kMaxDim = 4096;

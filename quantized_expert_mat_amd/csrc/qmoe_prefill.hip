@@ -48,8 +48,10 @@ constexpr int kChunkT = 2048;      // tokens per pass (bounds the workspace)
 constexpr int kBM = 64;            // rows (token-expert pairs) per thick m-tile
 constexpr int kGuCols = 64;        // intermediate columns per gate/up workgroup
 constexpr int kDnCols = 128;       // output columns per down workgroup
-constexpr int kSortMax = 16384;    // pairs per pass (kChunkT * kMaxK)
+constexpr int kSortMax = 16384;    // routed (token, expert) pairs per pass
 constexpr int kPairBits = 14;      // pair index bits in a sort key
+static_assert((1 << kPairBits) >= kSortMax && (long long)kMaxE << kPairBits <= (1ll << 32),
+              "sort keys hold an expert and a pair index");
 
 // ---------------------------------------------------------------------------
 // Workspace layout of one prefill pass
@@ -61,7 +63,9 @@ struct PLayout {
 
 PLayout p_layout(const moe_config& c, int T) {
   PLayout p;
-  p.Tc = T < 1 ? 1 : (T < kChunkT ? T : kChunkT);
+  // tokens per pass: at most kChunkT, and at most kSortMax routed pairs
+  const int tmax = std::min(kChunkT, kSortMax / std::max(1, c.top_k));
+  p.Tc = T < 1 ? 1 : (T < tmax ? T : tmax);
   const int TK = p.Tc * c.top_k;
   p.rows = TK + c.n_shared * p.Tc;
   const int nz = c.n_experts < TK ? c.n_experts : TK;

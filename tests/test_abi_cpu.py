@@ -45,7 +45,7 @@ def test_workspace_bytes_positive_and_monotone():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(bits=3), q.MOE_ERR_UNSUPPORTED), (dict(hidden=1000), q.MOE_ERR_UNSUPPORTED),
-    (dict(hidden=8192), q.MOE_ERR_UNSUPPORTED), (dict(top_k=9), q.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=8192), q.MOE_ERR_UNSUPPORTED), (dict(top_k=17), q.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=2, top_k=4), q.MOE_ERR_SHAPE), (dict(n_experts=2000), q.MOE_ERR_SHAPE),
     (dict(n_shared=3), q.MOE_ERR_UNSUPPORTED), (dict(group=32), q.MOE_ERR_UNSUPPORTED),
     (dict(flags=1 << 10), q.MOE_ERR_ARG), (dict(flags=q.MOE_F_RMSNORM, eps=0.0), q.MOE_ERR_ARG),

@@ -270,3 +270,63 @@ def test_zero_tokens_is_a_no_op():
     q.moe_stack_decode(cfg, [dl.weights()], 0, x, y, ws)
     torch.cuda.synchronize()
     assert float(y.max()) == 7.0
+
+
+# ------------------------------------------------------------------ top-k above 8
+
+def test_layer_forward_top10():
+    """The model's native top-10 (routed experts per token up to 16)."""
+    w = small(top_k=10, n_experts=40)
+    cfg = config_for(w)
+    dl, hl = DeviceLayer(w, 0), HostLayer(w, 0)
+    T = 3
+    x = xs(w, T)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    idx = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
+    ws = ws_for(cfg, T)
+    q.moe_layer_forward(cfg, dl.weights(), T, xd, y, ws, idx_out=idx, w_out=wts)
+    q.moe_device_status(ws)
+    yh, ih, wh = y.cpu().numpy(), idx.cpu().numpy(), wts.cpu().numpy()
+    for t in range(T):
+        r = ref.layer_decode(x[t], hl.router, hl.expert, hl.shared(), w.top_k)
+        if not same_set(r.idx, ih[t]):
+            assert r.gap < NEAR_TIE, f"token {t}: sets differ, gap {r.gap}"
+            r = ref.layer_decode(x[t], hl.router, hl.expert, hl.shared(), w.top_k, force_idx=ih[t])
+        assert abs(float(wh[t].sum()) - 1.0) < 1e-5
+        parity(yh[t], r.y, f"top-10 token {t}")
+
+
+def test_stack_decode_top10_with_tier():
+    w = small(hidden=512, inter=128, n_experts=32, top_k=10, n_layers=3, n_tokens=4, temporal_p=0.27)
+    L, T, K = w.n_layers, w.n_tokens, w.top_k
+    cfg = config_for(w)
+    dls = [DeviceLayer(w, l) for l in range(L)]
+    hls = [HostLayer(w, l) for l in range(L)]
+    x = xs(w, T)
+    mask = wl.boost_mask(w.seed + 5, T, L, K, 0.5)
+    y = torch.empty((T, w.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, L, K), dtype=torch.int32, device="cuda")
+    ws = ws_for(cfg, T, L)
+    q.moe_stack_decode(cfg, [d.weights() for d in dls], T, torch.from_numpy(x).cuda(), y, ws,
+                       boost_mask=torch.from_numpy(mask).cuda(), idx_trace=idx)
+    q.moe_device_status(ws)
+    ih = idx.cpu().numpy()
+
+    def follow(t, l, oi, gap):
+        if same_set(oi, ih[t, l]):
+            return None
+        assert gap < NEAR_TIE, f"t={t} l={l}: sets differ, gap {gap}"
+        return ih[t, l]
+
+    ys, sets, _ = ref.stack_decode(x, L, lambda l: hls[l].router, lambda l, e: hls[l].expert(e),
+                                   lambda l: hls[l].shared(), K, boost=mask, follow=follow)
+    for t in range(T):
+        parity(y.cpu().numpy()[t], ys[t], f"top-10 stack token {t}")
+    for t in range(1, T):
+        for l in range(L):
+            prev = sorted(ih[t - 1, l])
+            for j in range(K):
+                if mask[t, l, j]:
+                    assert prev[j] in ih[t, l]

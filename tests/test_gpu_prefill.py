@@ -168,3 +168,15 @@ def test_prefill_full_size_sampled():
     assert counts.max() > 128  # the hottest expert spans several m-tiles
     tokens = [0, 1, 577, T - 1] + [int(t) for t in np.nonzero((ih == hot).any(axis=1))[0][[0, -1]]]
     check_tokens(w, cl, x, yh, ih, wh, sel, tokens, what="prefill1155")
+
+
+@pytest.mark.parametrize("T", [37, 1700])
+def test_prefill_top10(T):
+    """Top-10 routing; at 1700 tokens the pass holds at most 16384 routed pairs, so two passes."""
+    w = small(top_k=10, n_experts=32, hidden=256, inter=128)
+    dl, hl = DeviceLayer(w, 0), HostLayer(w, 0)
+    x = wl.tokens_x(w.seed + 1000, T, w.hidden)
+    sel, _ = wl.zipf_gumbel_scores(w.seed + 3, T, w.n_experts, 1.1)
+    yh, ih, wh = run_prefill(w, dl, x, sel)
+    toks = range(T) if T <= 64 else list(range(0, T, 97)) + [1637, 1638, 1639, T - 1]
+    check_tokens(w, hl, x, yh, ih, wh, sel, toks, what=f"top-10 T={T}")
