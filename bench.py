@@ -35,13 +35,14 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def per_token_bytes(w):
+def per_token_bytes(w, gated=False):
     """Algorithmic bytes one token reads: per layer, the packed bytes of the K routed
-    and S shared experts plus the float32 router."""
+    and S shared experts plus the float32 router (and the float32 shared-expert gate)."""
     import quantized_expert_mat_amd as q
     from tests.helpers import config_for
     eb = q.moe_packed_expert_bytes(config_for(w))
-    return w.n_layers * ((w.top_k + w.n_shared) * eb + 4 * w.n_experts * w.hidden)
+    gate = 4 * w.n_shared * w.hidden if gated else 0
+    return w.n_layers * ((w.top_k + w.n_shared) * eb + 4 * w.n_experts * w.hidden + gate)
 
 
 COPY_BYTES = 1 << 30
@@ -98,7 +99,7 @@ def traffic_record(f_csv, w_csv, cf_csv, cw_csv, config_name, layers, tokens):
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline_and_parity(w, x0_host, y_gpu, idx_gpu, n_tokens):
+def cpu_baseline_and_parity(w, x0_host, y_gpu, idx_gpu, n_tokens, gated=False):
     """Replay tokens 0..n_tokens-1 through every layer with the CPU oracle (the
     weights it touches regenerated on the side; generation time excluded) and
     compare with the GPU's outputs of the same tokens."""
@@ -118,9 +119,10 @@ def cpu_baseline_and_parity(w, x0_host, y_gpu, idx_gpu, n_tokens):
         return idx_gpu[t, l]
 
     t0 = time.perf_counter()
+    sg = (lambda l: wl.shared_gate_weights(w.seed, l, w.n_shared, w.hidden)) if gated else None
     ys, sets, _ = ref.stack_decode(x0_host[:n_tokens], w.n_layers, lambda l: hls[l].router,
                                    lambda l, e: hls[l].expert(e), lambda l: hls[l].shared(), w.top_k,
-                                   boost=boost[:n_tokens], follow=follow)
+                                   boost=boost[:n_tokens], follow=follow, shared_gate_of=sg)
     dt = time.perf_counter() - t0 - sum(h.gen_seconds for h in hls)
     worst = (0.0, 0.0)
     for t in range(n_tokens):
@@ -261,6 +263,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--phased", action="store_true")
+    ap.add_argument("--shared-gate", action="store_true",
+                    help="give every layer a shared-expert gate (sigmoid(g . x_n) scales the shared expert)")
     ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
                     help="decode: the 60-layer stack (default); prefill: 1155 tokens through one layer")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -305,7 +309,7 @@ def main():
     ws = torch.empty(q.moe_workspace_bytes(cfg, T, L), dtype=torch.uint8, device=dev)
     dls = []
     for l in range(L):
-        dls.append(DeviceLayer(w, l, chunk=8, ws=ws))
+        dls.append(DeviceLayer(w, l, chunk=8, ws=ws, gated=args.shared_gate))
         if l % 10 == 9 or l == L - 1:
             log(f"layer {l + 1}/{L} generated and packed ({time.perf_counter() - t_setup:.1f} s)")
     layers = [d.weights() for d in dls]
@@ -341,7 +345,7 @@ def main():
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     tok_s = T * args.steps / elapsed
-    ptb = per_token_bytes(w)
+    ptb = per_token_bytes(w, gated=args.shared_gate)
     achieved = ptb * T / avg_launch_s / 1e9
     log(f"{tok_s:.1f} tok/s, {elapsed / args.steps * 1e3:.2f} ms/step, launch avg {avg_launch_s * 1e3:.3f} ms, "
         f"{achieved:.0f} GB/s")
@@ -354,7 +358,7 @@ def main():
     par = None
     if not args.no_cpu:
         n = min(args.cpu_tokens, T)
-        dt, par = cpu_baseline_and_parity(w, x0.cpu().numpy(), y.cpu().numpy(), ih, n)
+        dt, par = cpu_baseline_and_parity(w, x0.cpu().numpy(), y.cpu().numpy(), ih, n, gated=args.shared_gate)
         cpu = {"value": round(n / dt, 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
                "sample": f"tokens 0-{n - 1} through all {L} layers (temporal tier replayed), "
                          f"{dt:.1f} s of single-threaded fp64 oracle arithmetic"}
@@ -367,7 +371,7 @@ def main():
             rec = json.load(open(tf))
             from quantized_expert_mat_amd import build as qb
             if (rec.get("source_hash") == qb.source_hash() and rec.get("config") == w.name
-                    and rec.get("layers") == L):
+                    and rec.get("layers") == L and not args.shared_gate):
                 traffic = rec["bytes_per_launch"] * (T / rec.get("tokens", T))
         except Exception:
             traffic = None
@@ -389,7 +393,8 @@ def main():
         "config": {"workload": w.name, "layers": L, "tokens_per_step": T, "hidden": H, "inter": w.inter,
                    "experts": w.n_experts, "top_k": K, "shared": w.n_shared, "bits": w.bits,
                    "temporal_repeat_target": w.temporal_p, "temporal_repeat_realised": round(float(rep), 4),
-                   "bytes_per_token": ptb, "mode": "phased" if args.phased else "persistent"},
+                   "bytes_per_token": ptb, "mode": "phased" if args.phased else "persistent",
+                   "shared_gate": bool(args.shared_gate)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,

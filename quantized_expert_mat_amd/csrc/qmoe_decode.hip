@@ -819,9 +819,12 @@ constexpr int kRowsPre = 4;    // router rows per workgroup on the prefetch path
 constexpr int kShPre = 1;      // shared gate/up items per wave
 constexpr int kDnPre = 5;      // down slots per lane
 
+constexpr int kGatePre = kSpecH / (4 * kThreads);  // float4 of the shared-expert gate per thread
+
 struct StaticPre {
   float4 r[kRouterPre];
   Slot g[kShPre], u[kShPre];
+  float4 sg[kGatePre];  // specialised kernel with a gate: this thread's share of g_0
 };
 
 struct DownPre {
@@ -830,10 +833,18 @@ struct DownPre {
 
 // Router rows of this workgroup (float4 q = tid + kThreads*i of rows [e0, e1)) and
 // its shared gate/up items (item i0 + w + kNW*j on wave w) for layer l.
-template <int BITS>
+template <int BITS, bool SPEC = false>
 __device__ __forceinline__ void load_static(const DecodeArgs& a, const Lds& s, int l, StaticPre& sp) {
   const Geo& g = a.geo;
   const LayerPtrs lp = get_layer(a, s, l);
+  if constexpr (SPEC) {
+    if (a.any_sgate) {
+      // the gate vector (a layer without one re-reads router row 0, not used)
+      const float* G = lp.sgate ? lp.sgate : lp.router;
+#pragma unroll
+      for (int i = 0; i < kGatePre; ++i) sp.sg[i] = ldg_f4(G + ((int)threadIdx.x + kThreads * i) * 4);
+    }
+  }
   if (a.pre_router) {
     int e0, e1;
     split_range(a.E, a.nwg, blockIdx.x, e0, e1);
@@ -970,7 +981,7 @@ __device__ __forceinline__ void shared_gate_factors(const DecodeArgs& a, const L
   }
 }
 
-template <int BITS>
+template <int BITS, bool SPEC = false>
 __device__ __forceinline__ bool phase_a(const DecodeArgs& a, const Lds& s, int t, int l,
                                         StaticPre& sp, bool preloaded) {
   const Geo& g = a.geo;
@@ -979,9 +990,34 @@ __device__ __forceinline__ bool phase_a(const DecodeArgs& a, const Lds& s, int t
   SUBSTAMP(8);
   int e0, e1;
   split_range(a.E, a.nwg, blockIdx.x, e0, e1);
+  if constexpr (SPEC) {
+    if (a.any_sgate) {
+      // the specialised kernel's gate: the dot product from the prefetched vector;
+      // the router's barrier below publishes the per-wave partials
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < kGatePre; ++i) {
+        const float4 xv = reinterpret_cast<const float4*>(s.xn)[(int)threadIdx.x + kThreads * i];
+        part = fmaf(sp.sg[i].x, xv.x, part);
+        part = fmaf(sp.sg[i].y, xv.y, part);
+        part = fmaf(sp.sg[i].z, xv.z, part);
+        part = fmaf(sp.sg[i].w, xv.w, part);
+      }
+      part = wave_sum(part);
+      if ((threadIdx.x % kWave) == 0) s.sm->sgp[threadIdx.x / kWave][0] = part;
+    }
+  }
   if (a.pre_router) router_from_regs(a, s, t, l, sp);
   else router_rows(a, s, t, l, e0, e1);
-  if (a.any_sgate && a.mode == MODE_LAYER) shared_gate_factors(a, s, l);
+  if constexpr (SPEC) {
+    if (a.any_sgate && threadIdx.x == 0) {
+      float z = 0.f;
+      for (int i = 0; i < kNW; ++i) z += s.sm->sgp[i][0];
+      s.sm->sgc[0] = get_layer(a, s, l).sgate ? 1.f / (1.f + expf(-z)) : 1.f;
+    }
+  } else if (a.any_sgate && a.mode == MODE_LAYER) {
+    shared_gate_factors(a, s, l);
+  }
   SUBSTAMP(9);
   if (a.mode == MODE_LAYER && a.S > 0) {
     if (a.pre_shared) {
@@ -1488,7 +1524,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   // the next layer's router rows and shared slots land while x is being exchanged
   if (prefetch_static) {
     issue_order();
-    load_static<BITS>(a, s, l == a.L - 1 ? 0 : l + 1, sp);
+    load_static<BITS, SPEC>(a, s, l == a.L - 1 ? 0 : l + 1, sp);
     issue_order();
   }
   return true;
@@ -1503,7 +1539,7 @@ template <int BITS, bool SPEC>
 __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) {
   StaticPre sp;
   DownPre dp;
-  load_static<BITS>(a, s, 0, sp);
+  load_static<BITS, SPEC>(a, s, 0, sp);
   for (int t = 0; t < a.T; ++t) {
     for (int l = 0; l < a.L; ++l) {
       unsigned long long* tr =
@@ -1514,7 +1550,7 @@ __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) 
       unsigned long long* twg = (a.trace_wg && t == 2 && threadIdx.x == 0)
                                     ? a.trace_wg + ((size_t)l * a.nwg + blockIdx.x) * 4
                                     : nullptr;
-      if (!phase_a<BITS>(a, s, t, l, sp, true)) return;
+      if (!phase_a<BITS, SPEC>(a, s, t, l, sp, true)) return;
       if (tr) s.sm->trl[1] = wall_clock64();
       if (twg) s.sm->twl[0] = wall_clock64();
       if (!phase_b<BITS, SPEC>(a, s, t, l, dp, true)) return;
@@ -1535,7 +1571,7 @@ __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) 
 }
 
 template <int BITS>
-__device__ __forceinline__ void specialise(DecodeArgs& a) {
+__device__ __forceinline__ void specialise(DecodeArgs& a, bool gate) {
   a.geo = make_geo(kSpecH, kSpecI, BITS);
   a.E = kSpecE;
   a.K = kSpecK;
@@ -1549,7 +1585,7 @@ __device__ __forceinline__ void specialise(DecodeArgs& a) {
   a.pass_first[0] = 0; a.pass_count[0] = kSpecK;
   a.pass_first[1] = kSpecK; a.pass_count[1] = kSpecS;
   a.const_pass = 1;
-  a.any_sgate = 0;
+  a.any_sgate = gate;
   a.pre_router = a.pre_shared = a.pre_down = 1;
 }
 
@@ -1622,13 +1658,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
   }
 }
 
-template <int BITS, bool SPEC>
+// GATE (specialised kernel only): some layer has a shared-expert gate.
+template <int BITS, bool SPEC, bool GATE = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a_in, int only_phase, int t_only,
                                                           int l_only) {
   extern __shared__ __align__(16) unsigned lds_raw[];
   if constexpr (SPEC) {
     DecodeArgs a = a_in;
-    specialise<BITS>(a);
+    specialise<BITS>(a, GATE);
     decode_body<BITS, true>(a, lds_raw, only_phase, t_only, l_only);
   } else {
     decode_body<BITS, false>(a_in, lds_raw, only_phase, t_only, l_only);
@@ -1808,11 +1845,15 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   const bool spec = r.mode == MODE_LAYER && !r.phased && c.hidden == kSpecH && c.inter == kSpecI &&
                     a.E == kSpecE && a.K == kSpecK && a.S == kSpecS && nwg == kSpecNwg &&
                     a.pre_router && a.pre_shared && a.pre_down && a.n_lds_layers == r.L &&
-                    !r.any_sgate && (g_pre_mask & 8);
-  auto kern = c.bits == 4 ? (spec ? decode_kernel<4, true> : decode_kernel<4, false>)
-                          : (spec ? decode_kernel<2, true> : decode_kernel<2, false>);
-  static bool attr_set[4] = {false, false, false, false};
-  const int ki = (c.bits == 4 ? 2 : 0) + (spec ? 1 : 0);
+                    (g_pre_mask & 8);
+  const bool gate = spec && r.any_sgate;
+  auto kern = c.bits == 4
+                  ? (spec ? (gate ? decode_kernel<4, true, true> : decode_kernel<4, true, false>)
+                          : decode_kernel<4, false>)
+                  : (spec ? (gate ? decode_kernel<2, true, true> : decode_kernel<2, true, false>)
+                          : decode_kernel<2, false>);
+  static bool attr_set[6] = {false, false, false, false, false, false};
+  const int ki = (c.bits == 4 ? 3 : 0) + (spec ? (gate ? 2 : 1) : 0);
   if (lds > 64 * 1024 && !attr_set[ki]) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
