@@ -15,7 +15,11 @@
  *    (vi.news.hada.io), section "Kernel dequant tối ưu FMA" (the
  *    (nibble*scale+bias)*x product) and section "Metal Compute Shaders" (4-bit
  *    and 2-bit dequant mat-vec).  The oracle uses the naive form: it never
- *    applies the FMA or group-factored rewrites.
+ *    applies the FMA or group-factored rewrites.  Codes are plain integers, so
+ *    the same function serves 2-, 3- and 4-bit experts; 3-bit experts stand in
+ *    for the 3-bit ones of "Autoresearch impulsa a Qwen3.5-397B a 20.34 tok/s en
+ *    M5 Max mediante transmision SSD" (openclawradar.com), section
+ *    "Optimizaciones Efectivas".
  *  - RMS normalisation, SwiGLU, and the MoE combine with residual: same page,
  *    section "Metal Compute Shaders" and section "Deferred GPU Expert Compute"
  *    (combine + norm + residual feed the next layer).

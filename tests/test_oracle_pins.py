@@ -43,6 +43,24 @@ def test_expert_bytes_closed_form_matches_page():
     assert per_expert == 7_077_888
     assert per_expert / 2 ** 20 == g["expert_mib_4bit"]["value"]
     assert 3 * H * I * 2 // 8 + 3 * H * I // 64 * 4 == 3_932_160  # 2-bit
+    q3 = 3 * H * I * 3 // 8 + 3 * H * I // 64 * 4  # 3-bit
+    assert q3 == 5_505_024
+    # a 3-bit group-affine expert is about as much smaller than a 4-bit one as the
+    # page's 3-bit experts are (within one percentage point)
+    assert abs((1 - q3 / per_expert) - g["q3_size_reduction"]["value"]) < 0.01
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_generator_codes_are_bit_slices_of_the_word_stream(bits):
+    # element k is bits [b*(k % per), +b) of word k // per, per = 64 // b
+    key = wl.stream_key(3, wl.KIND_CODES, 1, 2, 0)
+    n = 3 * (64 // bits) + 5
+    got = wl.codes(key, n, bits)
+    words = [int(v) for v in wl.words(key, 0, n)]
+    per = 64 // bits
+    want = [(words[k // per] >> (bits * (k % per))) % (1 << bits) for k in range(n)]
+    assert got.tolist() == want
+    assert got.max() < (1 << bits)
 
 
 def test_fma_rewrite_identity_exact():

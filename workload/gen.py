@@ -9,7 +9,7 @@ Definition (implemented identically, bit for bit, in ``gen_device.hip``):
   ``k = KEY0; for f in fields: k = mix64(k ^ (f + GOLDEN))``.
 * Word ``i`` of a stream is ``mix64(key + (i + 1) * GOLDEN)`` (mod 2**64), i.e.
   the i-th output of a SplitMix64 generator whose state starts at ``key``.
-* ``b``-bit codes (b in {2, 4}): element ``k`` of a matrix (row-major index) is
+* ``b``-bit codes (b in {2, 3, 4}): element ``k`` of a matrix (row-major index) is
   bits ``[b*(k % (64//b)), +b)`` of word ``k // (64//b)``.
 * Approximate standard normals (Irwin-Hall with 12 terms, a textbook
   approximation whose variance is exactly 1 up to discretisation): element
@@ -33,7 +33,7 @@ __all__ = [
     "mix64", "stream_key", "words", "codes", "normals", "f32_from_normals",
     "bf16_bits_from_f32", "bf16_bits_to_f32", "bf16_from_normals",
     "ExpertSpec", "expert_canonical", "router_weights", "shared_gate_weights", "tokens_x",
-    "boost_mask", "zipf_gumbel_scores", "WorkloadConfig", "CONFIGS",
+    "boost_mask", "zipf_gumbel_scores", "WorkloadConfig", "CONFIGS", "STACK60_3BIT",
 ]
 
 M64 = (1 << 64) - 1
@@ -222,3 +222,9 @@ CONFIGS = [
                    n_tokens=256, temporal_p=0.27),
     WorkloadConfig("prefill1155", 4096, 1024, 512, n_tokens=1155, zipf=1.1),
 ]
+
+# The 60-layer decode stack with 3-bit experts: a synthetic group-affine stand-in
+# for the 3-bit experts of the autoresearch page ("Optimizaciones Efectivas"),
+# which it finds about 23% smaller than 4-bit ones.
+STACK60_3BIT = WorkloadConfig("stack60-3bit", 4096, 1024, 512, bits=3, sigma_scale=0.04, n_layers=60,
+                              n_tokens=256, temporal_p=0.27)
