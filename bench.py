@@ -258,6 +258,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=2, help="2: 4-bit stack, 3: 2-bit stack")
+    ap.add_argument("--bits", type=int, choices=[3], default=None,
+                    help="3: the 60-layer stack with 3-bit experts (instead of --config)")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--cpu-tokens", type=int, default=4)
@@ -274,7 +276,7 @@ def main():
         return copy_calibration()
     if args.traffic_record:
         import workload as wl
-        w = wl.CONFIGS[args.config]
+        w = wl.STACK60_3BIT if args.bits == 3 else wl.CONFIGS[args.config]
         return traffic_record(*args.traffic_record, w.name, args.layers or w.n_layers, args.tokens or w.n_tokens)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the decode stack fits one MI355X's HBM and this build has "
@@ -294,7 +296,7 @@ def main():
     from workload import device as wdev
     from tests.helpers import DeviceLayer, config_for
 
-    w = wl.CONFIGS[args.config]
+    w = wl.STACK60_3BIT if args.bits == 3 else wl.CONFIGS[args.config]
     if args.layers or args.tokens:
         w = w.replace(n_layers=args.layers or w.n_layers, n_tokens=args.tokens or w.n_tokens)
     L, T, K, H = w.n_layers, w.n_tokens, w.top_k, w.hidden
@@ -377,8 +379,7 @@ def main():
             traffic = None
 
     out = {
-        "metric": "decode tok/s, 60-layer 4-bit MoE stack; effective HBM GB/s vs peak"
-                  if w.bits == 4 else "decode tok/s, 60-layer 2-bit MoE stack; effective HBM GB/s vs peak",
+        "metric": f"decode tok/s, 60-layer {w.bits}-bit MoE stack; effective HBM GB/s vs peak",
         "value": round(tok_s, 2),
         "unit": "tok/s",
         "n_gpus": 1,

@@ -6,7 +6,7 @@
  * token and one layer ("Flash-MoE - Chạy mô hình 397 tỷ tham số trên laptop",
  * vi.news.hada.io): a router picks K of E experts per token, an always-on shared
  * expert runs beside them, each expert is a SwiGLU FFN whose weights are 4-bit
- * (or 2-bit) codes with one (scale, bias) pair per 64-element group, and the
+ * (or 3- or 2-bit) codes with one (scale, bias) pair per 64-element group, and the
  * outputs are combined with the routing weights and added to the residual
  * (sections "Kiến trúc mô hình", "Kernel dequant tối ưu FMA", "Metal Compute
  * Shaders", "Deferred GPU Expert Compute").
@@ -26,7 +26,7 @@
  *  - Two calls may run concurrently only on different streams with disjoint
  *    workspaces and outputs.
  *  - Supported shapes: hidden and inter are 64 * 2^k (64 .. 4096); group 64;
- *    bits 4 or 2; 1 <= top_k <= 16, top_k <= n_experts <= 1024; n_shared 0..2.
+ *    bits 4, 3 or 2; 1 <= top_k <= 16, top_k <= n_experts <= 1024; n_shared 0..2.
  */
 #ifndef QMOE_H
 #define QMOE_H
@@ -62,7 +62,10 @@ typedef struct {
   int32_t n_experts; /* E: routed experts per layer */
   int32_t top_k;     /* K: routed experts per token */
   int32_t n_shared;  /* S: always-on shared experts, added with weight 1 */
-  int32_t bits;      /* code width: 4 or 2 */
+  int32_t bits;      /* code width: 4, 3 or 2 (3: a group-affine stand-in for the
+                        3-bit experts of "Autoresearch impulsa a Qwen3.5-397B a 20.34
+                        tok/s en M5 Max mediante transmision SSD", openclawradar.com,
+                        section "Optimizaciones Efectivas") */
   int32_t group;     /* quantization group along the input dimension: 64 */
   int32_t flags;     /* MOE_F_* */
   float eps;         /* RMSNorm epsilon (inside the square root) */
@@ -86,7 +89,8 @@ typedef struct {
 /* Bytes of one packed expert (gate, up, down). 0 if the config is invalid.
  * With H=4096, I=1024, 4-bit codes and bf16 (scale, bias) per 64-group this is
  * 7,077,888 B = 6.75 MiB, the per-expert size the flash-moe page gives in its
- * "SSD Expert Streaming" section. */
+ * "SSD Expert Streaming" section; 3-bit codes give 5,505,024 B (22% less) and
+ * 2-bit codes 3,932,160 B. */
 size_t moe_packed_expert_bytes(const moe_config* cfg);
 
 /* Workspace bytes that suffice for any call below with at most n_tokens tokens

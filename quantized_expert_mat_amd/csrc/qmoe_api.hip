@@ -47,7 +47,7 @@ moe_status check_config(const moe_config* c) {
   if (!pow2_dim_ok(c->inter))
     return fail(MOE_ERR_UNSUPPORTED, "inter=%d: must be 64*2^k, 64..4096", c->inter);
   if (c->group != 64) return fail(MOE_ERR_UNSUPPORTED, "group=%d: only 64", c->group);
-  if (c->bits != 4 && c->bits != 2) return fail(MOE_ERR_UNSUPPORTED, "bits=%d: only 4 or 2", c->bits);
+  if (c->bits < 2 || c->bits > 4) return fail(MOE_ERR_UNSUPPORTED, "bits=%d: only 2, 3 or 4", c->bits);
   if (c->top_k < 1 || c->top_k > kMaxK)
     return fail(MOE_ERR_UNSUPPORTED, "top_k=%d: must be 1..%d", c->top_k, kMaxK);
   if (c->n_experts < c->top_k || c->n_experts > kMaxE)

@@ -234,6 +234,7 @@ __device__ inline void issue_order() {
 }
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ inline uint4 to_uint4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
@@ -245,7 +246,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const v4u gl_v4u;
 typedef __attribute__((address_space(1))) const unsigned gl_u32;
 typedef __attribute__((address_space(1))) const v4f gl_v4f;
+typedef __attribute__((address_space(1))) const v2u gl_v2u;
 __device__ inline uint4 ldg_u4(const void* p) { return to_uint4(*(gl_v4u*)(uintptr_t)p); }
+__device__ inline uint2 ldg_u2(const void* p) {
+  const v2u v = *(gl_v2u*)(uintptr_t)p;
+  return make_uint2(v.x, v.y);
+}
 __device__ inline unsigned ldg_u32(const void* p) { return *(gl_u32*)(uintptr_t)p; }
 __device__ inline float4 ldg_f4(const void* p) {
   const v4f v = *(gl_v4f*)(uintptr_t)p;
@@ -560,6 +566,7 @@ __device__ inline void load_dig(Dig& D, const unsigned* dig, const float* sum, i
   D.xs = sm.z;
 }
 
+// Codes of one slot: 4-bit c0 and c1; 3-bit c0 and c1.x, c1.y; 2-bit c0.
 struct Slot {
   uint4 c0, c1;
   unsigned sb;
@@ -568,6 +575,7 @@ struct Slot {
 typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 
 typedef __attribute__((address_space(3))) const v4u lds_v4u;
+typedef __attribute__((address_space(3))) const v2u lds_v2u;
 typedef __attribute__((address_space(3))) const unsigned lds_u32;
 
 
@@ -581,21 +589,25 @@ __device__ inline Slot ld_slot(const uint8_t* blk, int slot, bool in_lds) {
     s.c0 = to_uint4(c[slot]);
     if (BITS == 4) {
       s.c1 = to_uint4(c[64 + slot]);
-      s.sb = ((lds_u32*)(uintptr_t)(off + 2048))[slot];
+    } else if (BITS == 3) {
+      const v2u h = ((lds_v2u*)(uintptr_t)(off + kPlane1Offset))[slot];
+      s.c1 = make_uint4(h.x, h.y, 0, 0);
     } else {
       s.c1 = make_uint4(0, 0, 0, 0);
-      s.sb = ((lds_u32*)(uintptr_t)(off + 1024))[slot];
     }
+    s.sb = ((lds_u32*)(uintptr_t)(off + sb_offset(BITS)))[slot];
     return s;
   }
   s.c0 = ldg_u4(blk + slot * 16);
   if (BITS == 4) {
-    s.c1 = ldg_u4(blk + 1024 + slot * 16);
-    s.sb = ldg_u32(blk + 2048 + slot * 4);
+    s.c1 = ldg_u4(blk + kPlane1Offset + slot * 16);
+  } else if (BITS == 3) {
+    const uint2 h = ldg_u2(blk + kPlane1Offset + slot * 8);
+    s.c1 = make_uint4(h.x, h.y, 0, 0);
   } else {
     s.c1 = make_uint4(0, 0, 0, 0);
-    s.sb = ldg_u32(blk + 1024 + slot * 4);
   }
+  s.sb = ldg_u32(blk + sb_offset(BITS) + slot * 4);
   return s;
 }
 
@@ -606,6 +618,16 @@ __device__ inline float slot_dot(const Slot& s, const Dig& D) {
   if (BITS == 4) {
     cw[0] = s.c0.x; cw[1] = s.c0.y; cw[2] = s.c0.z; cw[3] = s.c0.w;
     cw[4] = s.c1.x; cw[5] = s.c1.y; cw[6] = s.c1.z; cw[7] = s.c1.w;
+  } else if (BITS == 3) {
+    const unsigned w[6] = {s.c0.x, s.c0.y, s.c0.z, s.c0.w, s.c1.x, s.c1.y};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const unsigned a = w[3 * t], b = w[3 * t + 1], c = w[3 * t + 2];
+      cw[4 * t] = a & 0x77777777u;
+      cw[4 * t + 1] = b & 0x77777777u;
+      cw[4 * t + 2] = c & 0x77777777u;
+      cw[4 * t + 3] = ((a >> 3) & 0x11111111u) | ((b >> 2) & 0x22222222u) | ((c >> 1) & 0x44444444u);
+    }
   } else {
     const unsigned w[4] = {s.c0.x, s.c0.y, s.c0.z, s.c0.w};
 #pragma unroll
@@ -627,7 +649,7 @@ __device__ inline float slot_dot(const Slot& s, const Dig& D) {
   }
   const int plo = S0 + (S1 << 4) + (S2 << 8);
   const int phi = S3 + (S4 << 4) + (S5 << 8);
-  const float pf = fmaf((float)phi, 4096.f, (float)plo);  // sum((q-8)*i) or sum(q*i)
+  const float pf = fmaf((float)phi, 4096.f, (float)plo);  // 4-bit sum((q-8)*i), else sum(q*i)
   const float sc = bf16lo_to_f32(s.sb), bi = bf16hi_to_f32(s.sb);
   if (BITS == 4) return fmaf(sc, (pf + D.X8) * D.xs, bi * D.Xf);
   return fmaf(sc, pf * D.xs, bi * D.Xf);
@@ -1847,18 +1869,20 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
                     a.pre_router && a.pre_shared && a.pre_down && a.n_lds_layers == r.L &&
                     (g_pre_mask & 8);
   const bool gate = spec && r.any_sgate;
-  auto kern = c.bits == 4
-                  ? (spec ? (gate ? decode_kernel<4, true, true> : decode_kernel<4, true, false>)
-                          : decode_kernel<4, false>)
-                  : (spec ? (gate ? decode_kernel<2, true, true> : decode_kernel<2, true, false>)
-                          : decode_kernel<2, false>);
-  static bool attr_set[6] = {false, false, false, false, false, false};
-  const int ki = (c.bits == 4 ? 3 : 0) + (spec ? (gate ? 2 : 1) : 0);
-  if (lds > 64 * 1024 && !attr_set[ki]) {
+  // [bits - 2][generic, specialised, specialised with the shared-expert gate]
+  typedef void (*DecodeKernel)(DecodeArgs, int, int, int);
+  static const DecodeKernel kernels[3][3] = {
+      {decode_kernel<2, false>, decode_kernel<2, true, false>, decode_kernel<2, true, true>},
+      {decode_kernel<3, false>, decode_kernel<3, true, false>, decode_kernel<3, true, true>},
+      {decode_kernel<4, false>, decode_kernel<4, true, false>, decode_kernel<4, true, true>}};
+  static bool attr_set[3][3] = {};
+  const int kv = spec ? (gate ? 2 : 1) : 0;
+  const DecodeKernel kern = kernels[c.bits - 2][kv];
+  if (lds > 64 * 1024 && !attr_set[c.bits - 2][kv]) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
     if (e != hipSuccess) return e;
-    attr_set[ki] = true;
+    attr_set[c.bits - 2][kv] = true;
   }
   // every exchange slot of this call starts at epoch 0
   // every exchange slot, the selection words and the epoch-tagged previous sets

@@ -28,6 +28,8 @@ constexpr int kDigitStride = 52;  // dwords per (vector, group) in LDS: 48 digit
 // lane (lane-contiguous, fully coalesced 16-byte loads):
 //   4-bit: [chunk0: 64 slots x 16 B][chunk1: 64 slots x 16 B][sb: 64 slots x 4 B]
 //          = 2304 B; chunk c of a slot holds codes 32c..32c+31 of the group.
+//   3-bit: [plane0: 64 slots x 16 B][plane1: 64 slots x 8 B][sb: 64 slots x 4 B]
+//          = 1792 B.
 //   2-bit: [codes: 64 slots x 16 B][sb: 64 slots x 4 B] = 1280 B.
 // sb = (bias_bf16 << 16) | scale_bf16.
 // Inside a 4-bit chunk, dword j holds the 8 codes 8j'..8j'+7 of the group
@@ -36,6 +38,12 @@ constexpr int kDigitStride = 52;  // dwords per (vector, group) in LDS: 48 digit
 // Inside a 2-bit slot, dword j holds codes 16j..16j+15: bits [4n, 4n+2) hold code
 // 16j + d(n) and bits [4n+2, 4n+4) hold code 16j + 8 + d(n), d(2m) = m,
 // d(2m+1) = 4 + m, unsigned.
+// A 3-bit slot holds six dwords w0..w5 (plane0 = w0..w3, plane1 = w4, w5) in two
+// triples (w0, w1, w2) and (w3, w4, w5). Triple t covers codes 32t..32t+31: for
+// i = 0, 1, 2, bits [4n, 4n+3) of its i-th dword hold code 32t + 8i + d(n) and
+// bit 4n+3 holds bit i of code 32t + 24 + d(n) (d as above, unsigned codes). So
+// masking a dword with 0x77777777 gives eight 3-bit codes in nibbles, and the
+// fourth octet of a triple is gathered from the three top bits of each nibble.
 // An expert is [gate blocks][up blocks][down blocks]; gate/up have R = I, C = H
 // and down has R = H, C = I. Blocks are multiples of 256 B, so every block of an
 // expert that starts 256-B aligned is 256-B aligned too.
@@ -64,12 +72,19 @@ __host__ __device__ constexpr bool pow2_dim_ok(int v) {
   return v >= 64 && v <= kMaxDim && (v & (v - 1)) == 0;
 }
 
+// Byte offset of the (scale, bias) words inside a block, and of the second code
+// plane (4- and 3-bit; its slots are 16 and 8 bytes wide).
+__host__ __device__ constexpr int sb_offset(int bits) {
+  return bits == 4 ? 2048 : bits == 3 ? 1536 : 1024;
+}
+constexpr int kPlane1Offset = 1024;
+
 __host__ __device__ constexpr Geo make_geo(int H, int I, int bits) {
   Geo g{};
   g.H = H; g.I = I; g.bits = bits;
   g.Gh = H / kGroup; g.Ph = kWave / g.Gh;
   g.Gi = I / kGroup; g.Pi = kWave / g.Gi;
-  g.blk = bits == 4 ? 2304 : 1280;
+  g.blk = sb_offset(bits) + 4 * kWave;
   g.nblk_gu = (I + g.Ph - 1) / g.Ph;
   g.nblk_d = (H + g.Pi - 1) / g.Pi;
   g.off_up = (size_t)g.nblk_gu * g.blk;

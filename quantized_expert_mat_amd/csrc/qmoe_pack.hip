@@ -1,7 +1,8 @@
 // qmoe_pack.hip -- canonical experts -> packed expert-major device layout.
 //
 // One thread writes one slot of one block: the codes of one 64-element group of one
-// row (two 16-byte chunks for 4-bit, one for 2-bit) and its (scale, bias) word.
+// row (two 16-byte chunks for 4-bit, 16 + 8 bytes for 3-bit, one 16-byte chunk for
+// 2-bit) and its (scale, bias) word.
 // Consecutive threads write consecutive slots, so the stores are fully coalesced;
 // each thread reads its 64 canonical codes as four 16-byte loads.
 #include "qmoe_internal.h"
@@ -45,7 +46,6 @@ __global__ __launch_bounds__(256) void pack_kernel(Geo geo, int n, const uint8_t
     const int p = slot / G, g = slot % G;
     const int row = b * P + p;
     uint8_t* blk = packed + (size_t)e * geo.expert_bytes + mat_off + (size_t)b * geo.blk;
-    const int code_bytes = geo.bits == 4 ? 2048 : 1024;
     uint4 c0 = make_uint4(0, 0, 0, 0), c1 = make_uint4(0, 0, 0, 0);
     unsigned sb = 0;
     if (p < P && row < R) {
@@ -67,6 +67,21 @@ __global__ __launch_bounds__(256) void pack_kernel(Geo geo, int n, const uint8_t
         }
         c0 = make_uint4(w[0], w[1], w[2], w[3]);
         c1 = make_uint4(w[4], w[5], w[6], w[7]);
+      } else if (geo.bits == 3) {
+        for (int t = 0; t < 2; ++t) {
+          for (int i = 0; i < 3; ++i) {
+            unsigned v = 0;
+            for (int nib = 0; nib < 8; ++nib) {
+              const int d = (nib & 1) ? 4 + (nib >> 1) : (nib >> 1);
+              const unsigned lo = check_code(q[32 * t + 8 * i + d], maxq, &bad);
+              const unsigned top = check_code(q[32 * t + 24 + d], maxq, &bad);
+              v |= (lo << (4 * nib)) | (((top >> i) & 1u) << (4 * nib + 3));
+            }
+            w[3 * t + i] = v;
+          }
+        }
+        c0 = make_uint4(w[0], w[1], w[2], w[3]);
+        c1 = make_uint4(w[4], w[5], 0, 0);
       } else {
         for (int j = 0; j < 4; ++j) {
           unsigned v = 0;
@@ -85,8 +100,9 @@ __global__ __launch_bounds__(256) void pack_kernel(Geo geo, int n, const uint8_t
       sb = (unsigned)scales[gi] | ((unsigned)biases[gi] << 16);
     }
     reinterpret_cast<uint4*>(blk)[slot] = c0;
-    if (geo.bits == 4) reinterpret_cast<uint4*>(blk + 1024)[slot] = c1;
-    reinterpret_cast<unsigned*>(blk + code_bytes)[slot] = sb;
+    if (geo.bits == 4) reinterpret_cast<uint4*>(blk + kPlane1Offset)[slot] = c1;
+    if (geo.bits == 3) reinterpret_cast<uint2*>(blk + kPlane1Offset)[slot] = make_uint2(c1.x, c1.y);
+    reinterpret_cast<unsigned*>(blk + sb_offset(geo.bits))[slot] = sb;
   }
   if (bad) set_dev_err(err, DEV_BAD_CODE);
 }

@@ -43,6 +43,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kChunkT = 2048;      // tokens per pass (bounds the workspace)
 constexpr int kBM = 64;            // rows (token-expert pairs) per thick m-tile
@@ -458,8 +459,8 @@ constexpr int kThickMT = 4;               // subtiles of a thick m-tile (64 rows
 
 // Codes and (scale, bias) of one lane's group for one chunk.
 struct WFrag {
-  u32x4 c0, c1;  // 4-bit: codes 0..31 and 32..63 of the group; 2-bit: c0 holds all 64
-  unsigned sb;
+  u32x4 c0, c1;  // 4-bit: codes 0..31 and 32..63 of the group; 3-bit: c0 and c1[0..1]
+  unsigned sb;   // (the packed slot's six dwords); 2-bit: c0 holds all 64
 };
 
 // Hides a value's known bits from the optimiser so that byte-to-float conversions
@@ -478,6 +479,20 @@ __device__ inline bf16x8 deq_octet(const WFrag& f, int i) {
     const unsigned d = (i < 4 ? f.c0[i & 3] : f.c1[i & 3]) ^ 0x88888888u;  // stored q ^ 8
     lo = opaque(d & 0x0F0F0F0Fu);
     hi = opaque((d >> 4) & 0x0F0F0F0Fu);
+  } else if (BITS == 3) {
+    // octets 0..3 come from dwords 0..2, octets 4..7 from dwords 3..5; the fourth
+    // octet of each triple is gathered from the top bits of the three dwords
+    const unsigned w[6] = {f.c0[0], f.c0[1], f.c0[2], f.c0[3], f.c1[0], f.c1[1]};
+    const int t = i >> 2, r = i & 3;
+    unsigned d;
+    if (r < 3) {
+      d = w[3 * t + r];
+    } else {
+      d = ((w[3 * t] >> 3) & 0x11111111u) | ((w[3 * t + 1] >> 2) & 0x22222222u) |
+          ((w[3 * t + 2] >> 1) & 0x44444444u);
+    }
+    lo = opaque(d & 0x07070707u);
+    hi = opaque((d >> 4) & 0x07070707u);
   } else {
     const unsigned d = f.c0[i >> 1] >> (2 * (i & 1));
     lo = opaque(d & 0x03030303u);
@@ -513,10 +528,12 @@ __device__ inline const uint8_t* expert_base(const PArgs& a, int e) {
 }
 
 // One work item as seen by one lane. Chunk ch of a lane's weight row starts 64*ch
-// bytes after wc (each code plane) and 4*ch words after wsb ((scale, bias)).
+// bytes after wc (code plane 0; plane 1 of 4-bit codes is 1024 bytes further), 32*ch
+// bytes after wc1 (plane 1 of 3-bit codes) and 4*ch words after wsb ((scale, bias)).
 struct Job {
   int row0, nrows, K, nch;
   const uint8_t* wc[2];    // codes of chunk 0 of this lane's row in each set
+  const uint8_t* wc1[2];   // 3-bit: second code plane of chunk 0
   const unsigned* wsb[2];  // (scale, bias) word of chunk 0
   unsigned sbmask;         // 0 where the lane's group lies beyond K (K < 256)
   int col[2];              // output column of this lane in each set
@@ -525,12 +542,13 @@ struct Job {
 
 template <int BITS>
 __device__ inline void job_row(const Geo& g, const uint8_t* mat, int row, int P, int G, int kk,
-                               const uint8_t*& wc, const unsigned*& wsb) {
+                               const uint8_t*& wc, const uint8_t*& wc1, const unsigned*& wsb) {
   const int grp = kk < G ? kk : 0;
   const uint8_t* blk = mat + (size_t)(row / P) * g.blk;
   const int slot = (row % P) * G + grp;
-  wc = blk + slot * 16;  // 4-bit: plane 1 is 1024 bytes further
-  wsb = reinterpret_cast<const unsigned*>(blk + (BITS == 4 ? 2048 : 1024)) + slot;
+  wc = blk + slot * 16;
+  wc1 = blk + kPlane1Offset + slot * 8;
+  wsb = reinterpret_cast<const unsigned*>(blk + sb_offset(BITS)) + slot;
 }
 
 template <int BITS, bool DOWN>
@@ -552,8 +570,8 @@ __device__ inline bool make_job(const PArgs& a, const int4* list, Job& jb) {
   jb.sbmask = kk < G ? 0xFFFFFFFFu : 0u;
   if (!DOWN) {
     const int j = nt * kGuCols + wave * 16 + (lane & 15);
-    job_row<BITS>(g, W, j, g.Ph, g.Gh, kk, jb.wc[0], jb.wsb[0]);
-    job_row<BITS>(g, W + g.off_up, j, g.Ph, g.Gh, kk, jb.wc[1], jb.wsb[1]);
+    job_row<BITS>(g, W, j, g.Ph, g.Gh, kk, jb.wc[0], jb.wc1[0], jb.wsb[0]);
+    job_row<BITS>(g, W + g.off_up, j, g.Ph, g.Gh, kk, jb.wc[1], jb.wc1[1], jb.wsb[1]);
     jb.col[0] = jb.col[1] = j;
     jb.on[0] = jb.on[1] = true;
   } else {
@@ -563,7 +581,7 @@ __device__ inline bool make_job(const PArgs& a, const int4* list, Job& jb) {
       jb.on[s] = base + 16 * s < a.H;
       const int n = jb.on[s] ? base + 16 * s + (lane & 15) : 0;
       jb.col[s] = n;
-      job_row<BITS>(g, W + g.off_down, n, g.Pi, g.Gi, kk, jb.wc[s], jb.wsb[s]);
+      job_row<BITS>(g, W + g.off_down, n, g.Pi, g.Gi, kk, jb.wc[s], jb.wc1[s], jb.wsb[s]);
     }
   }
   return true;
@@ -577,8 +595,13 @@ __device__ inline void load_wpair(const Job& jb, int ch, WFrag& f0, WFrag& f1) {
   f0.c0 = *reinterpret_cast<const u32x4*>(jb.wc[0] + ch * 64);
   f1.c0 = *reinterpret_cast<const u32x4*>(jb.wc[1] + ch * 64);
   if (BITS == 4) {
-    f0.c1 = *reinterpret_cast<const u32x4*>(jb.wc[0] + 1024 + ch * 64);
-    f1.c1 = *reinterpret_cast<const u32x4*>(jb.wc[1] + 1024 + ch * 64);
+    f0.c1 = *reinterpret_cast<const u32x4*>(jb.wc[0] + kPlane1Offset + ch * 64);
+    f1.c1 = *reinterpret_cast<const u32x4*>(jb.wc[1] + kPlane1Offset + ch * 64);
+  } else if (BITS == 3) {
+    const u32x2 h0 = *reinterpret_cast<const u32x2*>(jb.wc1[0] + ch * 32);
+    const u32x2 h1 = *reinterpret_cast<const u32x2*>(jb.wc1[1] + ch * 32);
+    f0.c1 = u32x4{h0[0], h0[1], 0u, 0u};
+    f1.c1 = u32x4{h1[0], h1[1], 0u, 0u};
   } else {
     f0.c1 = u32x4{0u, 0u, 0u, 0u};
     f1.c1 = u32x4{0u, 0u, 0u, 0u};
@@ -759,6 +782,22 @@ int next_pow2(int v) {
   return p;
 }
 
+dim3 xcd_grid(int items) { return dim3((unsigned)(8 * ((items + 7) / 8))); }
+
+// The gate/up and down passes, thin (one m-tile) and thick (kThickMT m-tiles) items.
+template <int BITS>
+void launch_gemms(const PArgs& a, int thin_max, int thick_max, int nt_gu, int nt_dn, hipStream_t stream) {
+  const size_t lds_thin = 2 * kSubBytes, lds_thick = 2 * kThickMT * kSubBytes;
+  hipLaunchKernelGGL((gemm_grouped<BITS, false, 1>), xcd_grid(thin_max * nt_gu), dim3(256), lds_thin, stream, a);
+  if (thick_max > 0)
+    hipLaunchKernelGGL((gemm_grouped<BITS, false, kThickMT>), xcd_grid(thick_max * nt_gu), dim3(256), lds_thick,
+                       stream, a);
+  hipLaunchKernelGGL((gemm_grouped<BITS, true, 1>), xcd_grid(thin_max * nt_dn), dim3(256), lds_thin, stream, a);
+  if (thick_max > 0)
+    hipLaunchKernelGGL((gemm_grouped<BITS, true, kThickMT>), xcd_grid(thick_max * nt_dn), dim3(256), lds_thick,
+                       stream, a);
+}
+
 }  // namespace
 
 size_t prefill_ws_bytes(const moe_config& c, int T) { return p_layout(c, T).total; }
@@ -838,27 +877,9 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
     const int thin_max = nz + c.n_shared;
     const int thick_max = TK / 17 + c.n_shared * (n / 17);
     const int nt_gu = c.inter / kGuCols, nt_dn = (c.hidden + kDnCols - 1) / kDnCols;
-    auto grid = [](int items) { return dim3((unsigned)(8 * ((items + 7) / 8))); };
-    const size_t lds_thin = 2 * kSubBytes, lds_thick = 2 * kThickMT * kSubBytes;
-    if (c.bits == 4) {
-      hipLaunchKernelGGL((gemm_grouped<4, false, 1>), grid(thin_max * nt_gu), dim3(256), lds_thin, stream, a);
-      if (thick_max > 0)
-        hipLaunchKernelGGL((gemm_grouped<4, false, kThickMT>), grid(thick_max * nt_gu), dim3(256),
-                           lds_thick, stream, a);
-      hipLaunchKernelGGL((gemm_grouped<4, true, 1>), grid(thin_max * nt_dn), dim3(256), lds_thin, stream, a);
-      if (thick_max > 0)
-        hipLaunchKernelGGL((gemm_grouped<4, true, kThickMT>), grid(thick_max * nt_dn), dim3(256),
-                           lds_thick, stream, a);
-    } else {
-      hipLaunchKernelGGL((gemm_grouped<2, false, 1>), grid(thin_max * nt_gu), dim3(256), lds_thin, stream, a);
-      if (thick_max > 0)
-        hipLaunchKernelGGL((gemm_grouped<2, false, kThickMT>), grid(thick_max * nt_gu), dim3(256),
-                           lds_thick, stream, a);
-      hipLaunchKernelGGL((gemm_grouped<2, true, 1>), grid(thin_max * nt_dn), dim3(256), lds_thin, stream, a);
-      if (thick_max > 0)
-        hipLaunchKernelGGL((gemm_grouped<2, true, kThickMT>), grid(thick_max * nt_dn), dim3(256),
-                           lds_thick, stream, a);
-    }
+    if (c.bits == 4) launch_gemms<4>(a, thin_max, thick_max, nt_gu, nt_dn, stream);
+    else if (c.bits == 3) launch_gemms<3>(a, thin_max, thick_max, nt_gu, nt_dn, stream);
+    else launch_gemms<2>(a, thin_max, thick_max, nt_gu, nt_dn, stream);
     const size_t nthreads = (size_t)n * (c.hidden / 4);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
                        stream, a);

@@ -28,11 +28,13 @@ def test_library_exports_every_declared_symbol():
 
 def test_packed_expert_bytes_closed_form():
     # 3 matrices of H*I codes at bits/8 bytes + one bf16 (scale, bias) pair per 64 codes
-    for H, I, bits in [(4096, 1024, 4), (4096, 1024, 2), (1024, 256, 4), (64, 64, 2), (4096, 4096, 4)]:
+    for H, I, bits in [(4096, 1024, 4), (4096, 1024, 3), (4096, 1024, 2), (1024, 256, 4), (64, 64, 2),
+                       (64, 64, 3), (4096, 4096, 4)]:
         cfg = q.Config.make(H, I, 8, 4, 1, bits)
         assert q.moe_packed_expert_bytes(cfg) == 3 * H * I * bits // 8 + 3 * H * I // 64 * 4
     assert q.moe_packed_expert_bytes(q.Config.make(4096, 1024, 512)) == 7_077_888  # 6.75 MiB
     assert q.moe_packed_expert_bytes(q.Config.make(4096, 1024, 512, bits=2)) == 3_932_160
+    assert q.moe_packed_expert_bytes(q.Config.make(4096, 1024, 512, bits=3)) == 5_505_024
 
 
 def test_workspace_bytes_positive_and_monotone():
@@ -44,7 +46,8 @@ def test_workspace_bytes_positive_and_monotone():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bits=3), q.MOE_ERR_UNSUPPORTED), (dict(hidden=1000), q.MOE_ERR_UNSUPPORTED),
+    (dict(bits=5), q.MOE_ERR_UNSUPPORTED), (dict(bits=1), q.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=1000), q.MOE_ERR_UNSUPPORTED),
     (dict(hidden=8192), q.MOE_ERR_UNSUPPORTED), (dict(top_k=17), q.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=2, top_k=4), q.MOE_ERR_SHAPE), (dict(n_experts=2000), q.MOE_ERR_SHAPE),
     (dict(n_shared=3), q.MOE_ERR_UNSUPPORTED), (dict(group=32), q.MOE_ERR_UNSUPPORTED),
@@ -90,7 +93,7 @@ def test_null_misaligned_and_small_workspace_rejected():
 
 
 def test_binding_raises_with_message():
-    cfg = q.Config.make(1024, 256, 64, bits=3)
+    cfg = q.Config.make(1024, 256, 64, bits=5)
     with pytest.raises(q.MoeError) as ei:
         q._check(q.lib().moe_expert_forward(ctypes.byref(cfg), None, 1, None, None, None, 0, None))
-    assert "bits=3" in str(ei.value)
+    assert "bits=5" in str(ei.value)
