@@ -290,3 +290,45 @@ def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=N
 
 def silu(z):
     return z / (1.0 + math.exp(-z)) if z > -700 else 0.0 * z
+
+
+def expert_cache_hits(sets, C):
+    """Host-memory tier with an HBM cache of C experts for one layer (the pages stream
+    experts from SSD and find about 27% of a token's experts repeating from the token
+    before: "Flash-MoE", section "SSD Expert Streaming"; "Autoresearch impulsa a
+    Qwen3.5-397B ...", section "Optimizaciones Efectivas"). The cache policy is the
+    library's own, stated with its streamed decode entry point:
+
+    the cache has C numbered slots, each empty or holding one expert with the token
+    at which it was last used. For token t with selected set S_t, every expert of S_t
+    already held by a slot is a hit, and that slot's last use becomes t. The other
+    experts of S_t, in increasing index, each go into the slot chosen as follows:
+    among slots whose last use is not t, an empty one if any (lowest number first),
+    else the one used least recently (lowest number on equal last use); its last use
+    becomes t.
+
+    sets: sequence over tokens of the selected experts (any order).
+    Returns a list over tokens of the set of experts that were hits."""
+    slots = [None] * C  # None or [expert, last_use]
+    out = []
+    for t, sel in enumerate(sets):
+        sel = sorted(set(int(e) for e in sel))
+        assert len(sel) <= C
+        hits = set()
+        for e in sel:
+            for sl in slots:
+                if sl is not None and sl[0] == e:
+                    sl[1] = t
+                    hits.add(e)
+        for e in sel:
+            if e in hits:
+                continue
+            free = [i for i in range(C) if slots[i] is None]
+            if free:
+                victim = free[0]
+            else:
+                cands = [i for i in range(C) if slots[i][1] != t]
+                victim = min(cands, key=lambda i: (slots[i][1], i))
+            slots[victim] = [e, t]
+        out.append(hits)
+    return out

@@ -367,3 +367,45 @@ def test_zipf_gumbel_first_pick_follows_power_law():
     exp = p[:top] * T
     chi2 = ((obs - exp) ** 2 / exp).sum()
     assert chi2 < 45.3                           # chi-square, 20 dof, p = 0.001
+
+
+# ---------------------------------------------------------------- expert cache (host-memory tier)
+
+def test_expert_cache_hand_worked_trace():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "expert_cache_trace.json")))
+    hits = ref.expert_cache_hits(g["sets"], g["cache_slots"])
+    assert [sorted(h) for h in hits] == g["hits"]
+
+
+def test_expert_cache_of_k_slots_hits_exactly_the_repeats_from_the_token_before():
+    rng = np.random.default_rng(21)
+    for K, E in [(4, 16), (2, 5), (6, 12)]:
+        sets = [rng.choice(E, K, replace=False) for _ in range(40)]
+        hits = ref.expert_cache_hits(sets, K)
+        assert hits[0] == set()
+        for t in range(1, len(sets)):
+            assert hits[t] == set(sets[t].tolist()) & set(sets[t - 1].tolist())
+
+
+def test_expert_cache_never_full_hits_every_expert_seen_before():
+    rng = np.random.default_rng(22)
+    K, E = 4, 20
+    sets = [rng.choice(E, K, replace=False) for _ in range(30)]
+    hits = ref.expert_cache_hits(sets, E)
+    seen = set()
+    for t, st in enumerate(sets):
+        assert hits[t] == set(st.tolist()) & seen
+        seen |= set(st.tolist())
+
+
+def test_expert_cache_holds_the_current_set_and_at_most_c_experts():
+    # after each token the current set is cached (a later token repeating it hits
+    # in full when nothing else came between), for any C >= K
+    rng = np.random.default_rng(23)
+    K, E = 4, 24
+    for C in (4, 5, 8, 13):
+        sets = [rng.choice(E, K, replace=False) for _ in range(25)]
+        for t in range(len(sets)):
+            again = sets[:t + 1] + [sets[t]]
+            assert ref.expert_cache_hits(again, C)[-1] == set(sets[t].tolist())
+
