@@ -167,6 +167,39 @@ moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_layer_we
                             int32_t* idx_trace, float* w_trace, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* The decode stack of moe_stack_decode with the routed experts streamed from host
+ * memory: the host-memory tier for expert sets larger than HBM. The pages stream
+ * experts from SSD through the page cache, read each expert as one unit, and
+ * find that 27% of a token's routed experts repeat from the token before
+ * ("Flash-MoE - Chạy mô hình 397 tỷ tham số trên laptop", vi.news.hada.io,
+ * section "SSD Expert Streaming"; "Autoresearch impulsa a Qwen3.5-397B a 20.34
+ * tok/s en M5 Max mediante transmision SSD", openclawradar.com, section
+ * "Optimizaciones Efectivas"). Here the device reads the experts from pinned host
+ * memory over PCIe and keeps recently used ones in an HBM cache, so a repeat costs
+ * HBM bandwidth instead of PCIe bandwidth. Results are those of moe_stack_decode
+ * on the same inputs; only where the bytes come from differs.
+ *   layers      host [L]: experts = PINNED HOST memory (hipHostMalloc or an
+ *               equivalent allocation the device can read), one allocation holding
+ *               all E packed experts, 256-B aligned; shared, router_w, gamma,
+ *               shared_gate are device memory as in moe_stack_decode.
+ *   cache       dev [L][cache_slots][moe_packed_expert_bytes] bytes, 256-B aligned,
+ *               no initialisation needed; cache_bytes its size.
+ *   cache_slots experts cached per layer, top_k..64. Policy per layer: a selected
+ *               expert found in the cache is read from it (a hit); each other one,
+ *               taken in increasing expert index, is read from host memory and
+ *               copied into the least recently used slot not used by the current
+ *               token (empty slots first, lowest slot on ties). The cache starts
+ *               empty at every call.
+ *   hit_trace   dev [T][L][K] uint8 or NULL: 1 where idx_trace's expert was a hit.
+ * Other arguments as in moe_stack_decode. MOE_F_PHASED is not accepted. Pointers
+ * that are not pinned host memory are rejected with MOE_ERR_ARG before anything
+ * is enqueued. */
+moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe_layer_weights* layers,
+                                     int32_t T, const float* x0, const uint8_t* boost_mask, float* y,
+                                     int32_t* idx_trace, float* w_trace, uint8_t* hit_trace, void* cache,
+                                     size_t cache_bytes, int32_t cache_slots, void* ws, size_t ws_bytes,
+                                     void* stream);
+
 /* Message for the last non-OK status returned on this host thread. */
 const char* moe_last_error(void);
 

@@ -17,8 +17,8 @@ MOE_F_RMSNORM, MOE_F_RESIDUAL, MOE_F_SELECT_BY_BIAS = 1, 2, 4
 MOE_F_PREFILL_BF16, MOE_F_PHASED = 8, 16
 
 EXPORTS = ["moe_packed_expert_bytes", "moe_workspace_bytes", "moe_pack_weights", "moe_route",
-           "moe_expert_forward", "moe_layer_forward", "moe_stack_decode", "moe_last_error",
-           "moe_device_status"]
+           "moe_expert_forward", "moe_layer_forward", "moe_stack_decode", "moe_stack_decode_streamed",
+           "moe_last_error", "moe_device_status"]
 
 
 class MoeError(RuntimeError):
@@ -72,6 +72,9 @@ def lib():
         L.moe_layer_forward.argtypes = [C, ctypes.POINTER(LayerWeights), i32, P, P, P, P, P, P, P, sz, P]
         L.moe_stack_decode.restype = st
         L.moe_stack_decode.argtypes = [C, i32, ctypes.POINTER(LayerWeights), i32, P, P, P, P, P, P, sz, P]
+        L.moe_stack_decode_streamed.restype = st
+        L.moe_stack_decode_streamed.argtypes = [C, i32, ctypes.POINTER(LayerWeights), i32, P, P, P, P, P, P,
+                                                P, sz, i32, P, sz, P]
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_device_status.restype = st
@@ -146,6 +149,17 @@ def moe_stack_decode(cfg, layers, T, x0, y, ws, boost_mask=None, idx_trace=None,
     return _check(lib().moe_stack_decode(ctypes.byref(cfg), len(layers), arr, T, _ptr(x0), _ptr(boost_mask),
                                          _ptr(y), _ptr(idx_trace), _ptr(w_trace), _ptr(ws),
                                          ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_stack_decode_streamed(cfg, layers, T, x0, y, ws, cache, cache_slots, boost_mask=None, idx_trace=None,
+                              w_trace=None, hit_trace=None, stream=None):
+    """layers[l].experts must point to pinned host memory (e.g. a torch CPU tensor
+    made with pin_memory=True); cache is a device byte tensor."""
+    arr = (LayerWeights * len(layers))(*layers)
+    return _check(lib().moe_stack_decode_streamed(
+        ctypes.byref(cfg), len(layers), arr, T, _ptr(x0), _ptr(boost_mask), _ptr(y), _ptr(idx_trace),
+        _ptr(w_trace), _ptr(hit_trace), _ptr(cache), cache.numel() * cache.element_size(), cache_slots,
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_device_status(ws, stream=None):

@@ -5,6 +5,8 @@
 #include <cstring>
 #include <string>
 
+#include <vector>
+
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -305,6 +307,78 @@ moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_layer_we
   r.phased = (cfg->flags & MOE_F_PHASED) != 0;
   r.any_sgate = false;
   for (int l = 0; l < L; ++l) r.any_sgate = r.any_sgate || (cfg->n_shared > 0 && layers[l].shared_gate);
+  return run_decode(r, st);
+}
+
+moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe_layer_weights* layers,
+                                     int32_t T, const float* x0, const uint8_t* boost_mask, float* y,
+                                     int32_t* idx_trace, float* w_trace, uint8_t* hit_trace, void* cache,
+                                     size_t cache_bytes, int32_t cache_slots, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  REQUIRE(L >= 1 && T >= 0, MOE_ERR_ARG, "L=%d T=%d", L, T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(!(cfg->flags & (MOE_F_PREFILL_BF16 | MOE_F_SELECT_BY_BIAS | MOE_F_PHASED)), MOE_ERR_ARG,
+          "streamed stack decode takes none of MOE_F_PREFILL_BF16, MOE_F_SELECT_BY_BIAS, MOE_F_PHASED");
+  REQUIRE(layers && x0 && y && cache, MOE_ERR_ARG, "NULL pointer");
+  REQUIRE(aligned(x0, 16) && aligned(y, 16), MOE_ERR_ALIGN, "x0/y must be 16-byte aligned");
+  REQUIRE(aligned(cache, 256), MOE_ERR_ALIGN, "cache must be 256-byte aligned");
+  REQUIRE(cache_slots >= cfg->top_k && cache_slots <= kMaxCacheSlots, MOE_ERR_ARG,
+          "cache_slots=%d: must be top_k..%d", cache_slots, kMaxCacheSlots);
+  const size_t eb = make_geo(cfg->hidden, cfg->inter, cfg->bits).expert_bytes;
+  REQUIRE(cache_bytes >= (size_t)L * cache_slots * eb, MOE_ERR_ARG, "cache %zu bytes, need %zu",
+          cache_bytes, (size_t)L * cache_slots * eb);
+  s = check_ws(cfg, T, L, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  // every layer's routed experts must be pinned host memory the device can read:
+  // the first and the last byte of the [E][expert_bytes] range are checked
+  std::vector<moe_layer_weights> lw(layers, layers + L);
+  for (int l = 0; l < L; ++l) {
+    const uint8_t* ex = static_cast<const uint8_t*>(layers[l].experts);
+    REQUIRE(ex, MOE_ERR_ARG, "layer %d: experts is NULL", l);
+    const uint8_t* ends[2] = {ex, ex + (size_t)cfg->n_experts * eb - 1};
+    void* dev[2] = {nullptr, nullptr};
+    for (int i = 0; i < 2; ++i) {
+      hipPointerAttribute_t at;
+      hipError_t e = hipPointerGetAttributes(&at, ends[i]);
+      if (e != hipSuccess || at.type != hipMemoryTypeHost || !at.devicePointer) {
+        (void)hipGetLastError();
+        return fail(MOE_ERR_ARG, "layer %d: experts must be pinned host memory (hipHostMalloc) "
+                    "covering all %d experts", l, cfg->n_experts);
+      }
+      dev[i] = at.devicePointer;
+    }
+    REQUIRE(static_cast<uint8_t*>(dev[1]) - static_cast<uint8_t*>(dev[0]) ==
+                (ptrdiff_t)((size_t)cfg->n_experts * eb - 1),
+            MOE_ERR_ARG, "layer %d: experts must be one pinned host allocation", l);
+    lw[l].experts = dev[0];
+  }
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  const WsLayout wl = ws_layout(*cfg, T, L);
+  s = upload_layers(*cfg, L, lw.data(), w8, wl, st);
+  if (s != MOE_OK) return s;
+  DecodeRequest r = {};
+  r.mode = 0;
+  r.cfg = *cfg;
+  r.L = L;
+  r.T = T;
+  r.layers_dev = reinterpret_cast<const LayerPtrs*>(w8 + wl.layers);
+  r.x0 = x0;
+  r.y = y;
+  r.boost_mask = boost_mask;
+  r.idx_out = idx_trace;
+  r.w_out = w_trace;
+  r.ws = w8;
+  r.wl = wl;
+  r.phased = false;
+  r.any_sgate = false;
+  for (int l = 0; l < L; ++l) r.any_sgate = r.any_sgate || (cfg->n_shared > 0 && layers[l].shared_gate);
+  r.stream = true;
+  r.cache = static_cast<uint8_t*>(cache);
+  r.cslots = cache_slots;
+  r.hit_out = hit_trace;
   return run_decode(r, st);
 }
 

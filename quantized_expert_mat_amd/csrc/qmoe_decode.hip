@@ -104,6 +104,12 @@ struct DecodeArgs {
   int n_lds_layers;
   int const_pass;  // 1: read the pass table from these arguments (compile-time constants)
   int lds_words;
+  // streamed stack: routed experts live in host memory (LayerPtrs::experts) and an
+  // HBM cache holds cslots experts per layer ([L][cslots][expert_bytes])
+  uint8_t* cache;
+  int cslots;
+  unsigned long long* ctab;  // [nwg][L][cslots] per-workgroup cache tables
+  uint8_t* hit_out;          // [T][L][K] 1 where a routed expert came from the cache
 };
 
 // Small per-workgroup state kept in LDS across phases.
@@ -113,6 +119,8 @@ struct Small {
   float redf[kNW][kMaxPass + 2];
   int sel_idx[kMaxK];
   float sel_w[kMaxK];
+  int sel_slot[kMaxK];  // streamed stack: cache slot of each selected expert
+  int sel_hit[kMaxK];   // and whether the slot already held it
   int ok;
   float sgc[kMaxShared];       // shared-expert gate factors of the current layer
   float sgp[kNW][kMaxShared];  // their per-wave partial dot products
@@ -611,6 +619,20 @@ __device__ inline Slot ld_slot(const uint8_t* blk, int slot, bool in_lds) {
   return s;
 }
 
+typedef __attribute__((address_space(1))) v4u gl_v4u_w;
+typedef __attribute__((address_space(1))) v2u gl_v2u_w;
+typedef __attribute__((address_space(1))) unsigned gl_u32_w;
+
+// Stores one slot into a block laid out like ld_slot's source (vector stores).
+template <int BITS>
+__device__ inline void st_slot(uint8_t* blk, int slot, const Slot& s) {
+  const uintptr_t b = (uintptr_t)blk;
+  *(gl_v4u_w*)(b + slot * 16) = v4u{s.c0.x, s.c0.y, s.c0.z, s.c0.w};
+  if (BITS == 4) *(gl_v4u_w*)(b + kPlane1Offset + slot * 16) = v4u{s.c1.x, s.c1.y, s.c1.z, s.c1.w};
+  if (BITS == 3) *(gl_v2u_w*)(b + kPlane1Offset + slot * 8) = v2u{s.c1.x, s.c1.y};
+  *(gl_u32_w*)(b + sb_offset(BITS) + slot * 4) = s.sb;
+}
+
 // Contribution of one (row, group) slot: scale*sum(q*x) + bias*sum(x).
 template <int BITS>
 __device__ inline float slot_dot(const Slot& s, const Dig& D) {
@@ -739,8 +761,9 @@ __device__ __forceinline__ bool prepare_x(const DecodeArgs& a, const Lds& s, int
 // (i - i0) % kNW. src(i, gate, up, hidx, row0) names the gate and up blocks (global
 // or LDS) and the index of the item's h vector in the exchange. after_issue() runs
 // once, right after the first batch of loads is issued (or at once if the wave has
-// no items).
-template <int BITS, typename ItemFn, typename Hook>
+// no items). WB: src takes two more outputs, blocks that the gate and up slots are
+// copied to after use (NULL: none).
+template <int BITS, bool WB = false, typename ItemFn, typename Hook>
 __device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, int i0, int i1, bool in_lds,
                              unsigned epoch, ItemFn src, Hook after_issue) {
   const Geo& g = a.geo;
@@ -759,6 +782,7 @@ __device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, 
   for (int ib = i0 + w; ib < i1; ib += kBatch * kNW) {
     Slot G[kBatch], U[kBatch];
     int hv[kBatch], row[kBatch];
+    uint8_t *wg[kBatch], *wu[kBatch];
     // loads are issued unconditionally (items past the range re-read the wave's
     // first item and are not reduced): straight-line loads let the compiler wait
     // for exactly the item it reduces next
@@ -767,7 +791,10 @@ __device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, 
       const int i = ib + j * kNW;
       const uint8_t *gb, *ub;
       int row0, hvec;
-      src(i < i1 ? i : i0 + w, gb, ub, hvec, row0);
+      if constexpr (WB)
+        src(i < i1 ? i : i0 + w, gb, ub, hvec, row0, wg[j], wu[j]);
+      else
+        src(i < i1 ? i : i0 + w, gb, ub, hvec, row0);
       G[j] = ld_slot<BITS>(gb, lane, in_lds);
       U[j] = ld_slot<BITS>(ub, lane, in_lds);
       hv[j] = i < i1 ? hvec : -1;
@@ -782,6 +809,12 @@ __device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, 
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (hv[j] < 0) continue;
+      if constexpr (WB) {
+        if (wg[j]) {
+          st_slot<BITS>(wg[j], lane, G[j]);
+          st_slot<BITS>(wu[j], lane, U[j]);
+        }
+      }
       const float pg = seg_sum(slot_dot<BITS>(G[j], D), g.Gh);
       const float pu = seg_sum(slot_dot<BITS>(U[j], D), g.Gh);
       if (grp == 0 && row[j] < g.I) xput(hxv, hv[j] * g.I + row[j], silu(pg) * pu, epoch);
@@ -1066,10 +1099,61 @@ __device__ inline unsigned ord_f32(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Streamed stack: the HBM expert cache of layer l. Each slot holds one expert;
+// its table entry is (last use, expert) with last use = token + 1 (0: empty). A
+// selected expert found in a slot is a hit; the misses, taken in increasing expert
+// index, each replace the least recently used slot not used at this token (empty
+// slots first, then the lowest slot). Every workgroup keeps its own copy of the
+// tables and, making the same selections, the same decisions, so no workgroup
+// waits for another's; and every byte of a cache slot is written and read by one
+// workgroup only (its gate/up blocks and its down rows), so the copy a workgroup
+// wrote is the one it reads. Runs on wave 0, lanes 0..K-1 holding the selection.
+__device__ __forceinline__ void cache_decide(const DecodeArgs& a, const Lds& s, int t, int l, int my_idx) {
+  const int lane = threadIdx.x, K = a.K, C = a.cslots;
+  unsigned long long* tab = a.ctab + ((size_t)blockIdx.x * a.L + l) * C;
+  unsigned long long ent = lane < C ? tab[lane] : 0ull;
+  const unsigned now = (unsigned)t + 1u;
+  int rank = 0;  // position of my expert in increasing index order
+  for (int j = 0; j < K; ++j) {
+    const int other = __builtin_amdgcn_readlane(my_idx, j);
+    rank += (j != lane && other < my_idx) ? 1 : 0;
+  }
+  int my_slot = 0, my_hit = 0;
+  for (int k = 0; k < K; ++k) {
+    const unsigned e = (unsigned)__builtin_amdgcn_readlane(my_idx, k);
+    const unsigned long long m = __ballot(lane < C && (ent >> 32) != 0ull && (unsigned)ent == e);
+    if (m) {
+      const int sl = __builtin_ctzll(m);  // a slot holds at most one expert, an expert one slot
+      if (lane == sl) ent = ((unsigned long long)now << 32) | e;
+      if (lane == k) {
+        my_slot = sl;
+        my_hit = 1;
+      }
+    }
+  }
+  for (int r = 0; r < K; ++r) {
+    const int k = __builtin_ctzll(__ballot(lane < K && rank == r));
+    if (__builtin_amdgcn_readlane(my_hit, k)) continue;
+    const unsigned e = (unsigned)__builtin_amdgcn_readlane(my_idx, k);
+    const unsigned use = (unsigned)(ent >> 32);
+    const unsigned long long key =
+        (lane < C && use != now) ? (((unsigned long long)use << 8) | (unsigned)lane) : ~0ull;
+    const int sl = (int)(~wave_max_u64(~key) & 255ull);  // C >= K: some slot is free at this token
+    if (lane == sl) ent = ((unsigned long long)now << 32) | e;
+    if (lane == k) my_slot = sl;
+  }
+  if (lane < C) tab[lane] = ent;
+  if (lane < K) {
+    s.sm->sel_slot[lane] = my_slot;
+    s.sm->sel_hit[lane] = my_hit;
+    if (blockIdx.x == 0 && a.hit_out) a.hit_out[((size_t)t * a.L + l) * K + lane] = (uint8_t)my_hit;
+  }
+}
+
 // Top-K with the temporal tier, then softmax over the selected logits. Runs on
 // wave 0 (kCh chunks of 4 logits per lane); the result is left in LDS (sel_idx,
-// sel_w).
-template <int kCh>
+// sel_w, and for the streamed stack sel_slot, sel_hit).
+template <int kCh, bool STREAM = false>
 __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, int t, int l) {
   if (threadIdx.x >= kWave) return;
   const int E = a.E, K = a.K, lane = threadIdx.x;
@@ -1226,6 +1310,7 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
     s.sm->sel_idx[lane] = my_idx;
     s.sm->sel_w[lane] = wk;
   }
+  if constexpr (STREAM) cache_decide(a, s, t, l, my_idx);
   if (blockIdx.x == 0) {
     // publish for a following phase launch, the outputs, and the sorted set for the
     // next token's temporal tier
@@ -1251,19 +1336,43 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
 }
 
 // The expert-list entry li of phase C: its packed expert and routing weight.
+// Streamed stack: routed entry k is read from its cache slot when the slot already
+// holds it, else from host memory, and then wb names the slot it is copied into.
+__device__ inline const uint8_t* routed_source(const DecodeArgs& a, const Lds& s, int l, int k,
+                                               uint8_t*& wb) {
+  const size_t eb = a.geo.expert_bytes;
+  uint8_t* slot = a.cache + ((size_t)l * a.cslots + s.sm->sel_slot[k]) * eb;
+  if (s.sm->sel_hit[k]) {
+    wb = nullptr;
+    return slot;
+  }
+  wb = slot;
+  return get_layer(a, s, l).experts + (size_t)s.sm->sel_idx[k] * eb;
+}
+
+// wb (streamed stack only): where the entry's expert is copied to, or NULL.
+template <bool STREAM = false>
 __device__ inline const uint8_t* list_expert(const DecodeArgs& a, const Lds& s, int l, int li,
-                                             float& wk) {
+                                             float& wk, uint8_t*& wb) {
   const Geo& g = a.geo;
+  wb = nullptr;
   if (a.mode == MODE_EXPERT) {
     wk = 1.f;
     return a.single_expert;
   }
   if (li < a.K) {
     wk = s.sm->sel_w[li];
+    if constexpr (STREAM) return routed_source(a, s, l, li, wb);
     return get_layer(a, s, l).experts + (size_t)s.sm->sel_idx[li] * g.expert_bytes;
   }
   wk = a.any_sgate ? s.sm->sgc[li - a.K] : 1.f;
   return get_layer(a, s, l).shared + (size_t)(li - a.K) * g.expert_bytes;
+}
+
+__device__ inline const uint8_t* list_expert(const DecodeArgs& a, const Lds& s, int l, int li,
+                                             float& wk) {
+  uint8_t* wb;
+  return list_expert<false>(a, s, l, li, wk, wb);
 }
 
 // Job k (0-based) of this lane in phase C's down projection: the k-th (pass, chunk)
@@ -1275,9 +1384,11 @@ struct DnJob {
   int pass;    // -1: no job k on this wave
   int li, row, slot;
   const uint8_t* blk;
+  uint8_t* wb;  // streamed stack: the cache block the slot is copied to, or NULL
   float wk;
 };
 
+template <bool STREAM = false>
 __device__ __forceinline__ DnJob down_job(const DecodeArgs& a, const Lds& s, int l, int k) {
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -1286,7 +1397,7 @@ __device__ __forceinline__ DnJob down_job(const DecodeArgs& a, const Lds& s, int
   DnJob j;
   j.on = false;
   j.pass = -1;
-  j.li = 0; j.row = 0; j.slot = 0; j.blk = nullptr; j.wk = 0.f;
+  j.li = 0; j.row = 0; j.slot = 0; j.blk = nullptr; j.wb = nullptr; j.wk = 0.f;
   // all divisors are powers of two: shifts and masks only
   for (int pi = 0; pi < npass; ++pi) {
     const int first = a.mode == MODE_EXPERT ? 0 : pass_first_of(a, s, pi);
@@ -1301,8 +1412,10 @@ __device__ __forceinline__ DnJob down_job(const DecodeArgs& a, const Lds& s, int
       j.li = first + kl;
       j.row = r0 + (c << lPp) + p;
       j.on = j.row < r1;
-      const uint8_t* ex = list_expert(a, s, l, j.li, j.wk);
+      uint8_t* wb;
+      const uint8_t* ex = list_expert<STREAM>(a, s, l, j.li, j.wk, wb);
       j.blk = ex + g.off_down + (size_t)(j.row >> g.lPi) * g.blk;
+      if constexpr (STREAM) j.wb = wb ? wb + g.off_down + (size_t)(j.row >> g.lPi) * g.blk : nullptr;
       j.slot = ((j.row & (g.Pi - 1)) << g.lGi) + grp;
       return j;
     }
@@ -1311,21 +1424,21 @@ __device__ __forceinline__ DnJob down_job(const DecodeArgs& a, const Lds& s, int
   return j;
 }
 
-template <int BITS>
+template <int BITS, bool STREAM = false>
 __device__ __forceinline__ void load_down(const DecodeArgs& a, const Lds& s, int l, DownPre& dp) {
   // unconditional loads (a lane without job k re-reads a valid slot it ignores), so
   // the compiler's wait counts stay exact
   const uint8_t* any = a.mode == MODE_EXPERT ? a.single_expert : get_layer(a, s, l).experts;
 #pragma unroll
   for (int k = 0; k < kDnPre; ++k) {
-    const DnJob j = down_job(a, s, l, k);
+    const DnJob j = down_job<STREAM>(a, s, l, k);
     dp.d[k] = ld_slot<BITS>(j.on ? j.blk : any, j.on ? j.slot : 0, false);
   }
 }
 
 // Phase C's down projection from prefetched slots; partial sums per (pass, row) go
 // to s.acc exactly as in the direct loop.
-template <int BITS>
+template <int BITS, bool STREAM = false>
 __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s, int l,
                                                const DownPre& dp) {
   const Geo& g = a.geo;
@@ -1335,7 +1448,7 @@ __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s
   int dig_pass = -1;  // the h digits in D are those of this pass's entries
 #pragma unroll
   for (int k = 0; k < kDnPre; ++k) {
-    const DnJob j = down_job(a, s, l, k);
+    const DnJob j = down_job<STREAM>(a, s, l, k);
     if (j.pass < 0) continue;
     const int n = a.mode == MODE_EXPERT ? 1 : pass_count_of(a, s, j.pass);
     const int seg = n * g.Gi, grp = lane & (g.Gi - 1);
@@ -1344,6 +1457,8 @@ __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s
       dig_pass = j.pass;
     }
     float part = j.on ? slot_dot<BITS>(dp.d[k], D) * j.wk : 0.f;
+    if constexpr (STREAM)
+      if (j.on && j.wb) st_slot<BITS>(j.wb, j.slot, dp.d[k]);
     part = seg_sum(part, seg);
     if (j.on && (lane % seg) == 0) s.acc[j.pass * a.rpw + (j.row - r0)] = part;
   }
@@ -1403,7 +1518,7 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
   }
 }
 
-template <int BITS, bool SPEC = false>
+template <int BITS, bool SPEC = false, bool STREAM = false>
 __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t, int l, DownPre& dp,
                                         bool prefetch) {
   const Geo& g = a.geo;
@@ -1427,7 +1542,7 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   if constexpr (SPEC)
     select_topk<(kSpecE + 4 * kWave - 1) / (4 * kWave)>(a, s, t, l);
   else
-    select_topk<kMaxE / (4 * kWave)>(a, s, t, l);
+    select_topk<kMaxE / (4 * kWave), STREAM>(a, s, t, l);
   __syncthreads();
   if (!s.sm->ok) return false;
   SUBSTAMP(10);
@@ -1435,6 +1550,29 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   if (a.mode != MODE_LAYER) return true;
   if constexpr (SPEC) {
     gateup_down_spec<BITS>(a, s, t, l, dp);
+    return true;
+  }
+  if constexpr (STREAM) {
+    // a workgroup owns whole gate/up blocks (all K entries of each), so a cached
+    // expert's block is always read by the workgroup that copied it in
+    int b0, b1;
+    split_range(g.nblk_gu, a.nwg, blockIdx.x, b0, b1);
+    const int K = a.K;
+    auto src = [&](int i, const uint8_t*& gb, const uint8_t*& ub, int& hvec, int& row0, uint8_t*& wg,
+                   uint8_t*& wu) {
+      const int b = i / K, k = i - b * K;
+      uint8_t* wb;
+      gb = routed_source(a, s, l, k, wb) + (size_t)b * g.blk;
+      ub = gb + g.off_up;
+      wg = wb ? wb + (size_t)b * g.blk : nullptr;
+      wu = wb ? wg + g.off_up : nullptr;
+      hvec = k;
+      row0 = b << g.lPh;
+    };
+    auto hook = [&] {
+      if (prefetch) load_down<BITS, true>(a, s, l, dp);
+    };
+    gateup_items<BITS, true>(a, s, b0 * K, b1 * K, false, epoch_of(a, t, l), src, hook);
     return true;
   }
   const uint8_t* experts = get_layer(a, s, l).experts;
@@ -1459,7 +1597,7 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
 // chunks per thread that poll the whole h exchange of the specialised shape at once
 constexpr int kSpecHPer = (kSpecK + kSpecS) * kSpecI / 2 / kThreads;
 
-template <int BITS, bool SPEC = false>
+template <int BITS, bool SPEC = false, bool STREAM = false>
 __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t, int l,
                                         bool pre_down, DownPre& dp, bool down_loaded,
                                         StaticPre& sp, bool prefetch_static) {
@@ -1492,8 +1630,8 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int npass = expert_mode ? 1 : a.npass;
   if (pre_down) {
-    if (!down_loaded) load_down<BITS>(a, s, l, dp);
-    down_from_regs<BITS>(a, s, l, dp);
+    if (!down_loaded) load_down<BITS, STREAM>(a, s, l, dp);
+    down_from_regs<BITS, STREAM>(a, s, l, dp);
   } else if (r0 < r1) {
     for (int pi = 0; pi < npass; ++pi) {
       const int first = expert_mode ? 0 : pass_first_of(a, s, pi);
@@ -1503,8 +1641,10 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
       const int grp = lane % g.Gi, kl = (lane / g.Gi) % n, p = lane / seg;
       const int li = first + kl;  // index in the expert list
       float wk;
-      const uint8_t* ex = list_expert(a, s, l, li, wk);
+      uint8_t* wb;
+      const uint8_t* ex = list_expert<STREAM>(a, s, l, li, wk, wb);
       const uint8_t* down = ex + g.off_down;
+      uint8_t* down_wb = STREAM && wb ? wb + g.off_down : nullptr;
       const int nchunk = (r1 - r0 + Pp - 1) / Pp;
       if (w >= nchunk) continue;
       Dig D;
@@ -1526,6 +1666,9 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
           const int c = c0 + j * kNW;
           if (c >= nchunk) continue;
           const bool valid = row[j] < r1;
+          if constexpr (STREAM)
+            if (valid && down_wb)
+              st_slot<BITS>(down_wb + (size_t)(row[j] / g.Pi) * g.blk, (row[j] % g.Pi) * g.Gi + grp, S[j]);
           float part = valid ? slot_dot<BITS>(S[j], D) * wk : 0.f;
           part = seg_sum(part, seg);
           if (valid && (lane % seg) == 0) s.acc[pi * rpw + (row[j] - r0)] = part;
@@ -1557,7 +1700,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
 // The layer/stack chain in one persistent launch: every phase runs for every
 // (token, layer), so registers prefetched in one phase are handed to the next.
 // Used when the router rows and the down slots fit the register prefetch.
-template <int BITS, bool SPEC>
+template <int BITS, bool SPEC, bool STREAM = false>
 __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) {
   StaticPre sp;
   DownPre dp;
@@ -1575,11 +1718,11 @@ __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) 
       if (!phase_a<BITS, SPEC>(a, s, t, l, sp, true)) return;
       if (tr) s.sm->trl[1] = wall_clock64();
       if (twg) s.sm->twl[0] = wall_clock64();
-      if (!phase_b<BITS, SPEC>(a, s, t, l, dp, true)) return;
+      if (!phase_b<BITS, SPEC, STREAM>(a, s, t, l, dp, true)) return;
       if (tr) s.sm->trl[3] = wall_clock64();
       if (twg) s.sm->twl[2] = wall_clock64();
       const bool more = !(t == a.T - 1 && l == a.L - 1);
-      if (!phase_c<BITS, SPEC>(a, s, t, l, true, dp, true, sp, more)) return;
+      if (!phase_c<BITS, SPEC, STREAM>(a, s, t, l, true, dp, true, sp, more)) return;
       if (tr) {
         s.sm->trl[5] = wall_clock64();
         for (int i = 0; i < 16; ++i) ((gl_u64*)(uintptr_t)tr)[i] = s.sm->trl[i];
@@ -1614,7 +1757,7 @@ __device__ __forceinline__ void specialise(DecodeArgs& a, bool gate) {
 // only_phase < 0: persistent (all tokens, all layers; phases wait on their inputs'
 // epochs). only_phase = 0/1/2: run that phase for token t_only, layer l_only.
 // SPEC: the specialised stack kernel (persistent, layer mode, flash-moe shape).
-template <int BITS, bool SPEC>
+template <int BITS, bool SPEC, bool STREAM = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_raw, int only_phase,
                                             int t_only, int l_only) {
   const Lds s = lds_view(lds_raw, a);
@@ -1637,7 +1780,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
     return;
   }
   if (persistent && a.mode == MODE_LAYER && a.pre_router && a.pre_down) {
-    decode_chain<BITS, false>(a, s);
+    decode_chain<BITS, false, STREAM>(a, s);
     return;
   }
   const int t0 = persistent ? 0 : t_only, t1 = persistent ? a.T : t_only + 1;
@@ -1654,7 +1797,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
       }
       if (persistent || only_phase == 1) {
         if (!have_x && a.mode != MODE_ROUTE && !prepare_x(a, s, t, l)) return;
-        if (!phase_b<BITS>(a, s, t, l, dp, false)) return;
+        if (!phase_b<BITS, false, STREAM>(a, s, t, l, dp, false)) return;
       }
       if (a.mode != MODE_ROUTE && (persistent || only_phase == 2)) {
         if (!persistent && a.mode == MODE_LAYER) {
@@ -1674,14 +1817,15 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
             s.sm->sgc[threadIdx.x] = __int_as_float(ld_coh(a.sel + 2 * kMaxK + threadIdx.x));
           __syncthreads();
         }
-        if (!phase_c<BITS>(a, s, t, l, a.pre_down, dp, false, sp, false)) return;
+        if (!phase_c<BITS, false, STREAM>(a, s, t, l, a.pre_down, dp, false, sp, false)) return;
       }
     }
   }
 }
 
 // GATE (specialised kernel only): some layer has a shared-expert gate.
-template <int BITS, bool SPEC, bool GATE = false>
+// STREAM (general kernel only): the streamed stack (routed experts in host memory).
+template <int BITS, bool SPEC, bool GATE = false, bool STREAM = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a_in, int only_phase, int t_only,
                                                           int l_only) {
   extern __shared__ __align__(16) unsigned lds_raw[];
@@ -1690,8 +1834,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a_in, int o
     specialise<BITS>(a, GATE);
     decode_body<BITS, true>(a, lds_raw, only_phase, t_only, l_only);
   } else {
-    decode_body<BITS, false>(a_in, lds_raw, only_phase, t_only, l_only);
+    decode_body<BITS, false, STREAM>(a_in, lds_raw, only_phase, t_only, l_only);
   }
+}
+
+__global__ void zero_u64(unsigned long long* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0ull;
 }
 
 // Clears the abort flag, the error word and every exchange slot (epoch 0 never
@@ -1770,6 +1919,12 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.poll_sleep = g_poll_sleep;
   a.trace = g_trace;
   a.trace_wg = g_trace_wg;
+  if (r.stream) {
+    a.cache = r.cache;
+    a.cslots = r.cslots;
+    a.ctab = reinterpret_cast<unsigned long long*>(ws + r.wl.ctab);
+    a.hit_out = r.hit_out;
+  }
 
   // Expert passes for phase C: routed experts in power-of-two groups that fit a
   // wave (lanes = rows x experts x groups), then the shared experts.
@@ -1864,19 +2019,22 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   }
 
   // the specialised kernel when the call is exactly the flash-moe stack shape
-  const bool spec = r.mode == MODE_LAYER && !r.phased && c.hidden == kSpecH && c.inter == kSpecI &&
+  const bool spec = !r.stream && r.mode == MODE_LAYER && !r.phased && c.hidden == kSpecH && c.inter == kSpecI &&
                     a.E == kSpecE && a.K == kSpecK && a.S == kSpecS && nwg == kSpecNwg &&
                     a.pre_router && a.pre_shared && a.pre_down && a.n_lds_layers == r.L &&
                     (g_pre_mask & 8);
   const bool gate = spec && r.any_sgate;
-  // [bits - 2][generic, specialised, specialised with the shared-expert gate]
+  // [bits - 2][general, specialised, specialised with the shared-expert gate, streamed]
   typedef void (*DecodeKernel)(DecodeArgs, int, int, int);
-  static const DecodeKernel kernels[3][3] = {
-      {decode_kernel<2, false>, decode_kernel<2, true, false>, decode_kernel<2, true, true>},
-      {decode_kernel<3, false>, decode_kernel<3, true, false>, decode_kernel<3, true, true>},
-      {decode_kernel<4, false>, decode_kernel<4, true, false>, decode_kernel<4, true, true>}};
-  static bool attr_set[3][3] = {};
-  const int kv = spec ? (gate ? 2 : 1) : 0;
+  static const DecodeKernel kernels[3][4] = {
+      {decode_kernel<2, false>, decode_kernel<2, true, false>, decode_kernel<2, true, true>,
+       decode_kernel<2, false, false, true>},
+      {decode_kernel<3, false>, decode_kernel<3, true, false>, decode_kernel<3, true, true>,
+       decode_kernel<3, false, false, true>},
+      {decode_kernel<4, false>, decode_kernel<4, true, false>, decode_kernel<4, true, true>,
+       decode_kernel<4, false, false, true>}};
+  static bool attr_set[3][4] = {};
+  const int kv = r.stream ? 3 : spec ? (gate ? 2 : 1) : 0;
   const DecodeKernel kern = kernels[c.bits - 2][kv];
   if (lds > 64 * 1024 && !attr_set[c.bits - 2][kv]) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1890,6 +2048,12 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, stream, a.sync, a.err, a.xx, nx);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (r.stream) {
+    // every workgroup's cache tables start empty: nothing cached by an earlier call is used
+    hipLaunchKernelGGL(zero_u64, dim3(256), dim3(256), 0, stream, a.ctab, (size_t)nwg * r.L * r.cslots);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (r.phased) {
     for (int t = 0; t < r.T; ++t)
       for (int l = 0; l < r.L; ++l)

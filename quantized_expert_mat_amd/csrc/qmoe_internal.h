@@ -16,6 +16,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxShared = 2;
 constexpr int kMaxDim = 4096;
 constexpr int kMaxNwg = 1024;     // workgroups a decode launch may use
+constexpr int kMaxCacheSlots = 64;  // HBM expert-cache slots per layer (streamed stack)
 constexpr int kRep = 8;           // replicas of every exchanged vector (spreads polling)
 constexpr int kDigitStride = 52;  // dwords per (vector, group) in LDS: 48 digit dwords + pad
 
@@ -106,7 +107,7 @@ struct LayerPtrs {
 
 // Workspace layout (byte offsets from the workspace base; all 256-B aligned).
 struct WsLayout {
-  size_t err, sync, xbuf, logits, hbuf, sel, prev, layers, pack_err, total;
+  size_t err, sync, xbuf, logits, hbuf, sel, prev, layers, ctab, pack_err, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -126,6 +127,8 @@ inline WsLayout ws_layout(const moe_config& c, int T, int L) {
   w.sel = o; o = align256(o + sizeof(int) * (2 * kMaxK + kMaxShared));
   w.prev = o; o = align256(o + sizeof(uint64_t) * 2 * (size_t)(L > 0 ? L : 1) * kMaxK);
   w.layers = o; o = align256(o + sizeof(LayerPtrs) * (size_t)(L > 0 ? L : 1));
+  // streamed stack: every workgroup's copy of every layer's expert-cache table
+  w.ctab = o; o = align256(o + sizeof(uint64_t) * (size_t)kMaxNwg * (L > 0 ? L : 1) * kMaxCacheSlots);
   w.total = o;
   return w;
 }
@@ -149,6 +152,11 @@ struct DecodeRequest {
   WsLayout wl;
   bool phased;
   bool any_sgate;  // some layer has a shared-expert gate
+  // streamed stack: routed experts in host memory, an HBM cache of cslots per layer
+  bool stream;
+  uint8_t* cache;
+  int cslots;
+  uint8_t* hit_out;
 };
 
 hipError_t launch_pack(const Geo& geo, int n, const uint8_t* codes, const uint16_t* scales,

@@ -97,3 +97,29 @@ def test_binding_raises_with_message():
     with pytest.raises(q.MoeError) as ei:
         q._check(q.lib().moe_expert_forward(ctypes.byref(cfg), None, 1, None, None, None, 0, None))
     assert "bits=5" in str(ei.value)
+
+
+def test_streamed_stack_validation():
+    """The streamed stack rejects bad cache arguments before any device call."""
+    L = q.lib()
+    cfg = q.Config.make(1024, 256, 64)
+    p = ctypes.c_void_p(1 << 20)
+    big = q.moe_workspace_bytes(cfg, 2, 2)
+    cache_need = 2 * 8 * q.moe_packed_expert_bytes(cfg)
+    arr = (q.LayerWeights * 2)(q.LayerWeights(1 << 20, 1 << 20, 1 << 20, None),
+                               q.LayerWeights(1 << 20, 1 << 20, 1 << 20, None))
+
+    def call(c=cfg, slots=8, cache=p, cache_bytes=cache_need, ws_bytes=big):
+        return L.moe_stack_decode_streamed(ctypes.byref(c), 2, arr, 2, p, None, p, None, None, None, cache,
+                                           cache_bytes, slots, p, ws_bytes, None)
+
+    assert call(slots=3) == q.MOE_ERR_ARG          # fewer slots than top_k
+    assert call(slots=65) == q.MOE_ERR_ARG         # more than 64
+    assert call(cache_bytes=cache_need - 1) == q.MOE_ERR_ARG
+    assert call(cache=ctypes.c_void_p((1 << 20) + 64)) == q.MOE_ERR_ALIGN
+    assert call(cache=None) == q.MOE_ERR_ARG
+    assert call(c=cfg.with_flags(q.MOE_F_PHASED)) == q.MOE_ERR_ARG
+    assert call(ws_bytes=10) == q.MOE_ERR_WORKSPACE
+    assert L.moe_stack_decode_streamed(ctypes.byref(cfg), 2, arr, 0, None, None, None, None, None, None, None, 0,
+                                       0, None, 0, None) == q.MOE_OK  # T == 0: no-op
+
