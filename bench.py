@@ -11,6 +11,11 @@ kernel's algorithmic bytes (weights touched per token, the per-token figure
 below) against MI355X's 8 TB/s HBM; `cpu_baseline` is the CPU oracle timed on
 a bounded sample (the first tokens through all layers) and scaled to tokens/s.
 
+Other workloads (`--workload`): `prefill` (1155 tokens through one layer as an
+expert-grouped bf16 GEMM) and `streamed` (the stack with every layer's routed
+experts in pinned host memory, read over PCIe, and a per-layer HBM expert cache;
+its roofline is PCIe 5.0 x16). `--bits 3` selects 3-bit experts.
+
 Two helper modes feed the `traffic` figure (HBM bytes per launch measured by the
 FETCH_SIZE / WRITE_SIZE counters, calibrated against a plain copy):
   --copy-calibration   three 1 GiB device-to-device copies (run under rocprofv3 --pmc)
@@ -223,7 +228,7 @@ def prefill_bench(args, w):
         log(f"cpu oracle: {dt:.1f} s for {n} tokens -> {cpu['value']} tok/s")
 
     out = {
-        "metric": "prefill tok/s, one 4-bit MoE layer, expert-grouped bf16 GEMM",
+        "metric": f"prefill tok/s, one {w.bits}-bit MoE layer, expert-grouped bf16 GEMM",
         "value": round(T * args.steps / elapsed, 2),
         "unit": "tok/s",
         "n_gpus": 1,
@@ -252,6 +257,134 @@ def prefill_bench(args, w):
     del keep
 
 
+PCIE5_X16_GBS = 63.0  # PCIe 5.0 x16, one direction: 16 lanes x 32 GT/s x 128/130
+
+
+def h2d_rate(h, reps=3):
+    """Pinned host -> HBM copy rate of the pinned tensor h (the copy engine's
+    practical PCIe bound)."""
+    import torch
+    nbytes = h.numel()
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    return nbytes * reps / (time.perf_counter() - t0) / 1e9
+
+
+def stream_bench(args, w):
+    """One step = one moe_stack_decode_streamed call: T tokens through L layers with
+    every layer's routed experts in pinned host memory and a per-layer HBM cache of
+    args.cache_slots experts."""
+    import numpy as np
+    import torch
+    import quantized_expert_mat_amd as q
+    import workload as wl
+    from workload import device as wdev
+    from tests.helpers import DeviceLayer, config_for
+
+    L, T, K, H, C = w.n_layers, w.n_tokens, w.top_k, w.hidden, args.cache_slots
+    cfg = config_for(w)
+    eb = q.moe_packed_expert_bytes(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    ws = torch.empty(q.moe_workspace_bytes(cfg, T, L), dtype=torch.uint8, device=dev)
+    pins, dls, lws = [], [], []
+    for l in range(L):
+        d = DeviceLayer(w, l, chunk=8, ws=ws)
+        h = torch.empty(d.experts.numel(), dtype=torch.uint8, pin_memory=True)
+        h.copy_(d.experts)
+        torch.cuda.synchronize()
+        d.experts = None  # only the host copy stays
+        pins.append(h)
+        dls.append(d)
+        lws.append(q.layer_weights(h, d.shared, d.router))
+        if l % 4 == 3 or l == L - 1:
+            log(f"layer {l + 1}/{L} generated and moved to pinned host memory "
+                f"({time.perf_counter() - t_setup:.1f} s)")
+    cache = torch.empty(L * C * eb, dtype=torch.uint8, device=dev)
+    x0 = torch.empty((T, H), dtype=torch.float32, device=dev)
+    keep = wdev.tokens_x(w.seed + 1000, T, H, x0)
+    mask = torch.from_numpy(wl.boost_mask(w.seed + 7, T, L, K, w.temporal_p or 0.0)).to(dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, L, K), dtype=torch.int32, device=dev)
+    hit = torch.empty((T, L, K), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    log(f"setup {setup_s:.1f} s; pinned host experts {sum(p.numel() for p in pins) / 1e9:.1f} GB, "
+        f"HBM cache {cache.numel() / 1e9:.2f} GB ({C} slots per layer)")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        q.moe_stack_decode_streamed(cfg, lws, T, x0, y, ws, cache, C, boost_mask=mask, idx_trace=idx,
+                                    hit_trace=hit, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    q.moe_device_status(ws)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    q.moe_device_status(ws)
+    avg_s = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps / 1e3
+    hh = hit.cpu().numpy()
+    misses = int((hh == 0).sum())
+    hit_rate = float(hh.mean())
+    pcie_bytes = misses * eb  # routed experts read from host memory per step
+    pcie_gbs = pcie_bytes / avg_s / 1e9
+    ih = idx.cpu().numpy()
+    rep = np.mean([len(set(ih[t, l]) & set(ih[t - 1, l])) / K for t in range(1, T) for l in range(L)])
+    h2d = h2d_rate(pins[0])
+    log(f"streamed: {T * args.steps / elapsed:.1f} tok/s ({L} layers), launch avg {avg_s * 1e3:.2f} ms, "
+        f"hit rate {hit_rate:.3f}, {pcie_gbs:.1f} GB/s from host memory (copy engine {h2d:.1f} GB/s)")
+
+    cpu, par = None, None
+    if not args.no_cpu:
+        n = min(args.cpu_tokens, T)
+        dt, par = cpu_baseline_and_parity(w.replace(n_tokens=T), x0.cpu().numpy(), y.cpu().numpy(), ih, n)
+        cpu = {"value": round(n / dt, 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
+               "sample": f"tokens 0-{n - 1} through all {L} layers (temporal tier replayed), "
+                         f"{dt:.1f} s of single-threaded fp64 oracle arithmetic"}
+    out = {
+        "metric": f"streamed decode tok/s, {L}-layer {w.bits}-bit MoE stack, routed experts in host memory",
+        "value": round(T * args.steps / elapsed, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i4",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}-streamed", "layers": L, "tokens_per_step": T, "hidden": H,
+                   "inter": w.inter, "experts": w.n_experts, "top_k": K, "shared": w.n_shared, "bits": w.bits,
+                   "cache_slots": C, "temporal_repeat_target": w.temporal_p,
+                   "temporal_repeat_realised": round(float(rep), 4), "cache_hit_rate": round(hit_rate, 4),
+                   "host_bytes_per_step": pcie_bytes},
+        "roofline": {"bound": "pcie", "achieved": round(pcie_gbs, 2), "peak": PCIE5_X16_GBS, "unit": "GB/s",
+                     "frac": round(pcie_gbs / PCIE5_X16_GBS, 4), "traffic": None,
+                     "copy_engine_gbs": round(h2d, 2)},
+        "cpu_baseline": cpu,
+        "parity": par,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+    del keep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,8 +400,11 @@ def main():
     ap.add_argument("--phased", action="store_true")
     ap.add_argument("--shared-gate", action="store_true",
                     help="give every layer a shared-expert gate (sigmoid(g . x_n) scales the shared expert)")
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
-                    help="decode: the 60-layer stack (default); prefill: 1155 tokens through one layer")
+    ap.add_argument("--workload", choices=["decode", "prefill", "streamed"], default="decode",
+                    help="decode: the 60-layer stack (default); prefill: 1155 tokens through one layer; "
+                         "streamed: the stack with routed experts in pinned host memory "
+                         "(default 16 layers, 64 tokens)")
+    ap.add_argument("--cache-slots", type=int, default=16, help="streamed: HBM cache slots per layer")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     args = ap.parse_args()
@@ -286,9 +422,15 @@ def main():
     import workload as wl
     if args.workload == "prefill":
         w = wl.CONFIGS[4]
+        if args.bits == 3:
+            w = w.replace(name="prefill1155-3bit", bits=3, sigma_scale=0.04)
         if args.tokens:
             w = w.replace(n_tokens=args.tokens)
         return prefill_bench(args, w)
+    if args.workload == "streamed":
+        w = wl.STACK60_3BIT if args.bits == 3 else wl.CONFIGS[args.config]
+        w = w.replace(n_layers=args.layers or 16, n_tokens=args.tokens or 64)
+        return stream_bench(args, w)
 
     import numpy as np
     import torch
