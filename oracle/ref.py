@@ -292,6 +292,24 @@ def silu(z):
     return z / (1.0 + math.exp(-z)) if z > -700 else 0.0 * z
 
 
+def qkv(mats, x, gamma=None, norm=False, eps=1e-6):
+    """Fused Q/K/V projection: three group-affine dequant mat-vecs of one input
+    ("Autoresearch impulsa a Qwen3.5-397B ...", section "Optimizaciones Efectivas":
+    the fused Q/K/V kernel reads the input once instead of three times; the mat-vec
+    itself is that of "Flash-MoE", section "Metal Compute Shaders").
+    mats: [(codes, scales, biases)] for Wq, Wk, Wv, each [R][H]. The input is
+    x_n = RMSNorm(x) * gamma with norm, else x * gamma (gamma None: 1).
+    Returns (q, k, v) in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    if norm:
+        xn = rmsnorm(x, gamma, eps)
+    elif gamma is not None:
+        xn = x * np.asarray(gamma, dtype=np.float32).astype(np.float64)
+    else:
+        xn = x
+    return tuple(matvec(c, sc, bi, xn) for c, sc, bi in mats)
+
+
 def expert_cache_hits(sets, C):
     """Host-memory tier with an HBM cache of C experts for one layer (the pages stream
     experts from SSD and find about 27% of a token's experts repeating from the token

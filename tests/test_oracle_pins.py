@@ -409,3 +409,49 @@ def test_expert_cache_holds_the_current_set_and_at_most_c_experts():
             again = sets[:t + 1] + [sets[t]]
             assert ref.expert_cache_hits(again, C)[-1] == set(sets[t].tolist())
 
+
+# ---------------------------------------------------------------- fused Q/K/V projection
+
+def _qkv_closed_form_mats(rng, H, rq, rk, rv):
+    G = H // 64
+    ones = np.full((rq, G), BF16_ONE, np.uint16)
+    wq = (np.ones((rq, H), np.uint8), ones, np.zeros((rq, G), np.uint16))  # every row sums x_n
+    bk = wl.bf16_bits_from_f32(rng.normal(0, 1, (rk, G)).astype(np.float32))
+    wk = (rng.integers(0, 16, (rk, H), dtype=np.uint8), np.zeros((rk, G), np.uint16), bk)  # bias only
+    cols = rng.integers(0, H, rv)
+    cv = np.zeros((rv, H), np.uint8)
+    cv[np.arange(rv), cols] = 1
+    wv = (cv, np.full((rv, G), BF16_ONE, np.uint16), np.zeros((rv, G), np.uint16))  # reads one column
+    return [wq, wk, wv], bk, cols
+
+
+def test_qkv_each_output_has_its_own_closed_form():
+    rng = np.random.default_rng(31)
+    H, rq, rk, rv = 512, 7, 5, 6
+    mats, bk, cols = _qkv_closed_form_mats(rng, H, rq, rk, rv)
+    x = rng.integers(-8, 9, H).astype(np.float64)
+    q, k, v = ref.qkv(mats, x)
+    assert np.array_equal(q, np.full(rq, x.sum()))
+    Xg = x.reshape(H // 64, 64).sum(axis=1)
+    np.testing.assert_allclose(k, wl.bf16_bits_to_f32(bk).astype(np.float64) @ Xg, rtol=0, atol=1e-9)
+    assert np.array_equal(v, x[cols])
+
+
+def test_qkv_normalises_the_input_once():
+    # x = c * ones: RMSNorm gives c / sqrt(c^2 + eps) * gamma for every element
+    rng = np.random.default_rng(32)
+    H, rq, rk, rv = 256, 3, 2, 4
+    mats, bk, cols = _qkv_closed_form_mats(rng, H, rq, rk, rv)
+    c, eps = 2.5, 1e-6
+    gamma = np.full(H, 0.75, np.float32)
+    xn = c / math.sqrt(c * c + eps) * 0.75
+    q, k, v = ref.qkv(mats, np.full(H, c), gamma=gamma, norm=True, eps=eps)
+    np.testing.assert_allclose(q, np.full(rq, H * xn), rtol=1e-12)
+    np.testing.assert_allclose(v, np.full(rv, xn), rtol=1e-12)
+    np.testing.assert_allclose(k, wl.bf16_bits_to_f32(bk).astype(np.float64) @ np.full(H // 64, 64 * xn),
+                               rtol=1e-12, atol=1e-12)
+    # without the norm only gamma scales the input
+    q2, _, v2 = ref.qkv(mats, np.full(H, c), gamma=gamma)
+    np.testing.assert_allclose(q2, np.full(rq, H * c * 0.75), rtol=1e-12)
+    np.testing.assert_allclose(v2, np.full(rv, c * 0.75), rtol=1e-12)
+
