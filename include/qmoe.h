@@ -71,6 +71,23 @@ typedef struct {
   float eps;         /* RMSNorm epsilon (inside the square root) */
 } moe_config;
 
+/* The fused Q/K/V projection: three group-affine quantized matrices that read one
+ * input. "Autoresearch impulsa a Qwen3.5-397B a 20.34 tok/s en M5 Max mediante
+ * transmision SSD" (openclawradar.com), section "Optimizaciones Efectivas", fuses
+ * the Q/K/V projections so that the input vector is read once instead of three
+ * times; the mat-vec is the dequant mat-vec of "Flash-MoE" (section "Metal
+ * Compute Shaders"). The pages give no attention widths; they are arguments. */
+typedef struct {
+  int32_t hidden;  /* H: input width, 64 * 2^k, 64..4096 */
+  int32_t q_rows;  /* Rq, Rk, Rv: output widths, each >= 1, Rq + Rk + Rv <= 65536 */
+  int32_t k_rows;
+  int32_t v_rows;
+  int32_t bits;    /* code width: 4, 3 or 2 */
+  int32_t group;   /* 64 */
+  int32_t flags;   /* 0 or MOE_F_RMSNORM */
+  float eps;       /* RMSNorm epsilon (inside the square root) */
+} moe_qkv_config;
+
 /* One layer's weights, all device pointers, 256-byte aligned. */
 typedef struct {
   const void* experts;   /* n_experts packed experts, moe_packed_expert_bytes() apart */
@@ -199,6 +216,28 @@ moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe
                                      int32_t* idx_trace, float* w_trace, uint8_t* hit_trace, void* cache,
                                      size_t cache_bytes, int32_t cache_slots, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* Bytes of the packed fused Q/K/V matrix (Rq + Rk + Rv rows of H columns, the
+ * block layout of an expert's gate matrix). 0 if the config is invalid. */
+size_t moe_qkv_packed_bytes(const moe_qkv_config* cfg);
+
+/* Pack the fused matrix: codes dev [Rq + Rk + Rv][H] uint8 (the rows of Wq, then
+ * Wk, then Wv; values < 2^bits), scales and biases dev [Rq + Rk + Rv][H/64] bf16
+ * bit patterns; packed dev, moe_qkv_packed_bytes bytes, 256-B aligned. ws: any
+ * workspace of at least 1024 bytes (its first word is the device error word that
+ * moe_device_status reads: codes out of range). */
+moe_status moe_qkv_pack(const moe_qkv_config* cfg, const uint8_t* codes, const uint16_t* scales,
+                        const uint16_t* biases, void* packed, size_t packed_bytes, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* q[t] = Wq x_n[t], k[t] = Wk x_n[t], v[t] = Wv x_n[t] for T tokens, float32, with
+ * x_n = RMSNorm(x) * gamma under MOE_F_RMSNORM, else x * gamma (gamma NULL: 1).
+ * Every row's dot product uses one encoding of its token's input.
+ *   packed dev (moe_qkv_pack), 256-B aligned;  gamma dev [H] float32 or NULL, 16-B
+ *   aligned;  x dev [T][H] float32, 16-B aligned;  q dev [T][Rq], k dev [T][Rk],
+ *   v dev [T][Rv] float32. No workspace: the kernel needs none. */
+moe_status moe_qkv_forward(const moe_qkv_config* cfg, const void* packed, const float* gamma, int32_t T,
+                           const float* x, float* q, float* k, float* v, void* stream);
 
 /* Message for the last non-OK status returned on this host thread. */
 const char* moe_last_error(void);

@@ -18,7 +18,7 @@ MOE_F_PREFILL_BF16, MOE_F_PHASED = 8, 16
 
 EXPORTS = ["moe_packed_expert_bytes", "moe_workspace_bytes", "moe_pack_weights", "moe_route",
            "moe_expert_forward", "moe_layer_forward", "moe_stack_decode", "moe_stack_decode_streamed",
-           "moe_last_error", "moe_device_status"]
+           "moe_qkv_packed_bytes", "moe_qkv_pack", "moe_qkv_forward", "moe_last_error", "moe_device_status"]
 
 
 class MoeError(RuntimeError):
@@ -39,6 +39,16 @@ class Config(ctypes.Structure):
     def with_flags(self, flags):
         return Config(self.hidden, self.inter, self.n_experts, self.top_k, self.n_shared, self.bits,
                       self.group, flags, self.eps)
+
+
+class QkvConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("q_rows", ctypes.c_int32), ("k_rows", ctypes.c_int32),
+                ("v_rows", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+    @classmethod
+    def make(cls, hidden, q_rows, k_rows, v_rows, bits=4, flags=0, eps=1e-6, group=64):
+        return cls(hidden, q_rows, k_rows, v_rows, bits, group, flags, eps)
 
 
 class LayerWeights(ctypes.Structure):
@@ -75,6 +85,13 @@ def lib():
         L.moe_stack_decode_streamed.restype = st
         L.moe_stack_decode_streamed.argtypes = [C, i32, ctypes.POINTER(LayerWeights), i32, P, P, P, P, P, P,
                                                 P, sz, i32, P, sz, P]
+        Q = ctypes.POINTER(QkvConfig)
+        L.moe_qkv_packed_bytes.restype = sz
+        L.moe_qkv_packed_bytes.argtypes = [Q]
+        L.moe_qkv_pack.restype = st
+        L.moe_qkv_pack.argtypes = [Q, P, P, P, P, sz, P, sz, P]
+        L.moe_qkv_forward.restype = st
+        L.moe_qkv_forward.argtypes = [Q, P, P, i32, P, P, P, P, P]
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_device_status.restype = st
@@ -160,6 +177,21 @@ def moe_stack_decode_streamed(cfg, layers, T, x0, y, ws, cache, cache_slots, boo
         ctypes.byref(cfg), len(layers), arr, T, _ptr(x0), _ptr(boost_mask), _ptr(y), _ptr(idx_trace),
         _ptr(w_trace), _ptr(hit_trace), _ptr(cache), cache.numel() * cache.element_size(), cache_slots,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_qkv_packed_bytes(cfg):
+    return lib().moe_qkv_packed_bytes(ctypes.byref(cfg))
+
+
+def moe_qkv_pack(cfg, codes, scales, biases, packed, ws, stream=None):
+    return _check(lib().moe_qkv_pack(ctypes.byref(cfg), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(packed),
+                                     packed.numel() * packed.element_size(), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_qkv_forward(cfg, packed, T, x, q_out, k_out, v_out, gamma=None, stream=None):
+    return _check(lib().moe_qkv_forward(ctypes.byref(cfg), _ptr(packed), _ptr(gamma), T, _ptr(x), _ptr(q_out),
+                                        _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
 def moe_device_status(ws, stream=None):

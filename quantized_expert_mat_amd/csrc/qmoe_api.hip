@@ -76,6 +76,21 @@ moe_status check_ws(const moe_config* c, int T, int L, void* ws, size_t ws_bytes
     if (!(cond)) return fail(status, __VA_ARGS__); \
   } while (0)
 
+moe_status check_qkv(const moe_qkv_config* c) {
+  if (!c) return fail(MOE_ERR_ARG, "config is NULL");
+  if (!pow2_dim_ok(c->hidden))
+    return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: must be 64*2^k, 64..4096", c->hidden);
+  if (c->q_rows < 1 || c->k_rows < 1 || c->v_rows < 1 ||
+      (long long)c->q_rows + c->k_rows + c->v_rows > 65536)
+    return fail(MOE_ERR_SHAPE, "rows %d/%d/%d: each >= 1, sum <= 65536", c->q_rows, c->k_rows, c->v_rows);
+  if (c->group != 64) return fail(MOE_ERR_UNSUPPORTED, "group=%d: only 64", c->group);
+  if (c->bits < 2 || c->bits > 4) return fail(MOE_ERR_UNSUPPORTED, "bits=%d: only 2, 3 or 4", c->bits);
+  if (c->flags & ~MOE_F_RMSNORM) return fail(MOE_ERR_ARG, "flags 0x%x: only MOE_F_RMSNORM", c->flags);
+  if ((c->flags & MOE_F_RMSNORM) && !(c->eps > 0.f && c->eps < 1.f))
+    return fail(MOE_ERR_ARG, "eps=%g must be in (0, 1)", (double)c->eps);
+  return MOE_OK;
+}
+
 moe_status upload_layers(const moe_config& c, int L, const moe_layer_weights* layers, uint8_t* ws,
                          const WsLayout& wl, hipStream_t st) {
   LayerPtrs tmp[64];
@@ -147,7 +162,7 @@ moe_status moe_pack_weights(const moe_config* cfg, int32_t n, const uint8_t* cod
           "packed_bytes %zu < %d x %zu", packed_bytes, n, geo.expert_bytes);
   const WsLayout wl = ws_layout(*cfg, 0, 1);
   unsigned* err = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(ws) + wl.err);
-  hipError_t e = launch_pack(geo, n, codes, scales, biases, packed, err, (hipStream_t)stream);
+  hipError_t e = launch_pack(geo, n, 3, codes, scales, biases, packed, err, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "pack launch");
   return MOE_OK;
 }
@@ -380,6 +395,45 @@ moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe
   r.cslots = cache_slots;
   r.hit_out = hit_trace;
   return run_decode(r, st);
+}
+
+size_t moe_qkv_packed_bytes(const moe_qkv_config* cfg) {
+  if (check_qkv(cfg) != MOE_OK) return 0;
+  return make_matrix_geo(cfg->hidden, cfg->q_rows + cfg->k_rows + cfg->v_rows, cfg->bits).expert_bytes;
+}
+
+moe_status moe_qkv_pack(const moe_qkv_config* cfg, const uint8_t* codes, const uint16_t* scales,
+                        const uint16_t* biases, void* packed, size_t packed_bytes, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_status s = check_qkv(cfg);
+  if (s != MOE_OK) return s;
+  REQUIRE(codes && scales && biases && packed && ws, MOE_ERR_ARG, "NULL pointer");
+  REQUIRE(aligned(codes, 16) && aligned(packed, 256) && aligned(ws, 256), MOE_ERR_ALIGN,
+          "codes must be 16-byte, packed and ws 256-byte aligned");
+  REQUIRE(ws_bytes >= 1024, MOE_ERR_WORKSPACE, "workspace %zu bytes, need 1024", ws_bytes);
+  const Geo geo = make_matrix_geo(cfg->hidden, cfg->q_rows + cfg->k_rows + cfg->v_rows, cfg->bits);
+  REQUIRE(packed_bytes >= geo.expert_bytes, MOE_ERR_SHAPE, "packed %zu bytes, need %zu", packed_bytes,
+          geo.expert_bytes);
+  unsigned* err = static_cast<unsigned*>(ws);
+  hipError_t e = launch_pack(geo, 1, 1, codes, scales, biases, packed, err, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return MOE_OK;
+}
+
+moe_status moe_qkv_forward(const moe_qkv_config* cfg, const void* packed, const float* gamma, int32_t T,
+                           const float* x, float* q, float* k, float* v, void* stream) {
+  moe_status s = check_qkv(cfg);
+  if (s != MOE_OK) return s;
+  REQUIRE(T >= 0, MOE_ERR_ARG, "T=%d", T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(packed && x && q && k && v, MOE_ERR_ARG, "NULL pointer");
+  REQUIRE(aligned(packed, 256) && aligned(x, 16) && (!gamma || aligned(gamma, 16)) && aligned(q, 4) &&
+              aligned(k, 4) && aligned(v, 4),
+          MOE_ERR_ALIGN, "packed must be 256-byte, x and gamma 16-byte aligned");
+  hipError_t e = launch_qkv(*cfg, static_cast<const uint8_t*>(packed), gamma, T, x, q, k, v,
+                            (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "qkv launch");
+  return MOE_OK;
 }
 
 const char* moe_last_error(void) { return g_msg.c_str(); }

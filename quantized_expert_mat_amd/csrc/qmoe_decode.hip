@@ -2080,4 +2080,118 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
                                     args, (unsigned)lds, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Fused Q/K/V projection. The three matrices are one packed matrix of R = Rq + Rk +
+// Rv rows (the gate-matrix block layout); every workgroup stages, normalises and
+// encodes a token's input once and reduces its blocks' rows against it. A wave's
+// first kQkvB blocks are requested before the input is staged, the next ones while
+// the current ones are reduced.
+// ---------------------------------------------------------------------------
+struct QkvArgs {
+  Geo geo;  // H columns, I = R rows
+  int rq, rk, R, T, nwg, norm;
+  float eps;
+  const uint8_t* w;
+  const float* gamma;
+  const float* x;
+  float *yq, *yk, *yv;
+};
+
+constexpr int kQkvB = 4;  // blocks per wave in flight together
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void qkv_kernel(QkvArgs a) {
+  __shared__ __align__(16) float xn[kMaxDim];
+  __shared__ __align__(16) unsigned dig[(kMaxDim / kGroup) * kDigitStride];
+  __shared__ __align__(16) float sums[4 * (kMaxDim / kGroup)];
+  __shared__ float red[kNW];
+  const Geo& g = a.geo;
+  const int H = g.H;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int p = lane >> g.lGh, grp = lane & (g.Gh - 1);
+  int b0, b1;
+  split_range(g.nblk_gu, a.nwg, blockIdx.x, b0, b1);
+  if (b0 >= b1) return;  // whole workgroup: no block here
+  const int first = b0 + w < b1 ? b0 + w : b0;  // a wave without blocks re-reads a valid one
+  auto blk_of = [&](int b) { return a.w + (size_t)(b < b1 ? b : first) * g.blk; };
+  for (int t = 0; t < a.T; ++t) {
+    Slot S[kQkvB];
+#pragma unroll
+    for (int j = 0; j < kQkvB; ++j) S[j] = ld_slot<BITS>(blk_of(b0 + w + j * kNW), lane, false);
+    issue_order();
+    const float* xt = a.x + (size_t)t * H;
+    float ss = 0.f;
+    for (int i = threadIdx.x * 4; i < H; i += kThreads * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xt + i);
+      *reinterpret_cast<float4*>(xn + i) = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    if (a.norm) {
+      ss = wave_sum(ss);
+      if (lane == 0) red[w] = ss;
+    }
+    __syncthreads();
+    float rinv = 1.f;
+    if (a.norm) {
+      ss = 0.f;
+      for (int i = 0; i < kNW; ++i) ss += red[i];
+      rinv = 1.f / sqrtf(ss / (float)H + a.eps);
+    }
+    if (a.norm || a.gamma)
+      encode_vectors<true>(xn, 1, H, rinv, a.gamma, dig, sums);
+    else
+      encode_vectors<false>(xn, 1, H, 1.f, nullptr, dig, sums);
+    __syncthreads();
+    Dig D;
+    load_dig(D, dig, sums, grp);
+    for (int ib = b0 + w; ib < b1; ib += kQkvB * kNW) {
+      Slot C[kQkvB];
+#pragma unroll
+      for (int j = 0; j < kQkvB; ++j) C[j] = S[j];
+#pragma unroll
+      for (int j = 0; j < kQkvB; ++j) S[j] = ld_slot<BITS>(blk_of(ib + (kQkvB + j) * kNW), lane, false);
+#pragma unroll
+      for (int j = 0; j < kQkvB; ++j) {
+        const int b = ib + j * kNW;
+        if (b >= b1) continue;
+        const float r = seg_sum(slot_dot<BITS>(C[j], D), g.Gh);
+        const int row = (b << g.lPh) + p;
+        if (grp == 0 && row < a.R) {
+          if (row < a.rq) a.yq[(size_t)t * a.rq + row] = r;
+          else if (row < a.rq + a.rk) a.yk[(size_t)t * a.rk + (row - a.rq)] = r;
+          else a.yv[(size_t)t * (a.R - a.rq - a.rk) + (row - a.rq - a.rk)] = r;
+        }
+      }
+    }
+    __syncthreads();  // the next token overwrites the staged input and its digits
+  }
+}
+
+hipError_t launch_qkv(const moe_qkv_config& c, const uint8_t* w, const float* gamma, int T, const float* x,
+                      float* q, float* k, float* v, hipStream_t stream) {
+  hipError_t e = device_info();
+  if (e != hipSuccess) return e;
+  QkvArgs a;
+  memset(&a, 0, sizeof(a));
+  a.R = c.q_rows + c.k_rows + c.v_rows;
+  a.geo = make_matrix_geo(c.hidden, a.R, c.bits);
+  a.rq = c.q_rows;
+  a.rk = c.k_rows;
+  a.T = T;
+  a.norm = (c.flags & MOE_F_RMSNORM) ? 1 : 0;
+  a.eps = c.eps;
+  a.w = w;
+  a.gamma = gamma;
+  a.x = x;
+  a.yq = q;
+  a.yk = k;
+  a.yv = v;
+  // kQkvB blocks per wave, at most 4 workgroups per compute unit
+  const int per = kNW * kQkvB;
+  a.nwg = std::max(1, std::min((a.geo.nblk_gu + per - 1) / per, 4 * g_num_cu));
+  auto kern = c.bits == 4 ? qkv_kernel<4> : c.bits == 3 ? qkv_kernel<3> : qkv_kernel<2>;
+  hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace qmoe

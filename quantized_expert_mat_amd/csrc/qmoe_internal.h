@@ -96,6 +96,22 @@ __host__ __device__ constexpr Geo make_geo(int H, int I, int bits) {
   return g;
 }
 
+// Geometry of one packed matrix of R rows and H columns, laid out like an expert's
+// gate matrix (blocks of Ph = 64/Gh rows); expert_bytes is the matrix's size.
+inline Geo make_matrix_geo(int H, int R, int bits) {
+  Geo g{};
+  g.H = H; g.I = R; g.bits = bits;
+  g.Gh = H / kGroup; g.Ph = kWave / g.Gh;
+  g.Gi = 1; g.Pi = 1;
+  g.blk = sb_offset(bits) + 4 * kWave;
+  g.nblk_gu = (R + g.Ph - 1) / g.Ph;
+  g.nblk_d = 0;
+  g.expert_bytes = (size_t)g.nblk_gu * g.blk;
+  g.off_up = g.off_down = g.expert_bytes;
+  g.lGh = log2i(g.Gh); g.lPh = log2i(g.Ph);
+  return g;
+}
+
 // Device copy of one layer's pointers.
 struct LayerPtrs {
   const uint8_t* experts;
@@ -159,8 +175,11 @@ struct DecodeRequest {
   uint8_t* hit_out;
 };
 
-hipError_t launch_pack(const Geo& geo, int n, const uint8_t* codes, const uint16_t* scales,
+// mats: 3 (n experts: gate, up, down) or 1 (n matrices of geo.I rows, geo.H columns)
+hipError_t launch_pack(const Geo& geo, int n, int mats, const uint8_t* codes, const uint16_t* scales,
                        const uint16_t* biases, void* packed, unsigned* err, hipStream_t stream);
+hipError_t launch_qkv(const moe_qkv_config& c, const uint8_t* w, const float* gamma, int T, const float* x,
+                      float* q, float* k, float* v, hipStream_t stream);
 hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char** why);
 
 // Device error codes (written to the workspace error word; first error wins).

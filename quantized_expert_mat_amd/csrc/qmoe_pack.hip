@@ -14,16 +14,16 @@ __device__ inline unsigned check_code(unsigned q, unsigned maxq, unsigned* bad) 
   return q & maxq;
 }
 
-__global__ __launch_bounds__(256) void pack_kernel(Geo geo, int n, const uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(256) void pack_kernel(Geo geo, int n, int mats, const uint8_t* __restrict__ codes,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint16_t* __restrict__ biases,
                                                    uint8_t* __restrict__ packed, unsigned* err) {
-  const int bpe = 2 * geo.nblk_gu + geo.nblk_d;  // blocks per expert
+  const int bpe = mats == 3 ? 2 * geo.nblk_gu + geo.nblk_d : geo.nblk_gu;  // blocks per unit
   const size_t total = (size_t)n * bpe * kWave;
   const size_t codes_per_mat_gu = (size_t)geo.I * geo.H;
-  const size_t codes_per_expert = 3 * codes_per_mat_gu;
+  const size_t codes_per_expert = mats * codes_per_mat_gu;
   const size_t groups_per_mat_gu = codes_per_mat_gu / kGroup;
-  const size_t groups_per_expert = 3 * groups_per_mat_gu;
+  const size_t groups_per_expert = mats * groups_per_mat_gu;
   const unsigned maxq = (1u << geo.bits) - 1u;
   unsigned bad = 0;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -111,14 +111,14 @@ __global__ void zero_err(unsigned* err) {
   if (threadIdx.x == 0) *err = 0u;
 }
 
-hipError_t launch_pack(const Geo& geo, int n, const uint8_t* codes, const uint16_t* scales,
+hipError_t launch_pack(const Geo& geo, int n, int mats, const uint8_t* codes, const uint16_t* scales,
                        const uint16_t* biases, void* packed, unsigned* err, hipStream_t stream) {
-  const size_t total = (size_t)n * (2 * geo.nblk_gu + geo.nblk_d) * kWave;
+  const size_t total = (size_t)n * (mats == 3 ? 2 * geo.nblk_gu + geo.nblk_d : geo.nblk_gu) * kWave;
   size_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(zero_err, dim3(1), dim3(64), 0, stream, err);
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, geo, n, codes,
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, geo, n, mats, codes,
                      scales, biases, static_cast<uint8_t*>(packed), err);
   return hipGetLastError();
 }

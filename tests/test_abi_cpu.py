@@ -123,3 +123,26 @@ def test_streamed_stack_validation():
     assert L.moe_stack_decode_streamed(ctypes.byref(cfg), 2, arr, 0, None, None, None, None, None, None, None, 0,
                                        0, None, 0, None) == q.MOE_OK  # T == 0: no-op
 
+
+def test_qkv_sizes_and_validation():
+    # Rq + Rk + Rv rows of H codes at bits/8 bytes + one (scale, bias) pair per 64 codes
+    for H, rows, bits in [(4096, (4096, 512, 512), 4), (4096, (4096, 512, 512), 3), (512, (200, 40, 44), 4),
+                          (64, (5, 3, 2), 2)]:
+        cfg = q.QkvConfig.make(H, *rows, bits=bits)
+        P = 64 // (H // 64)  # rows per block
+        nblk = -(-sum(rows) // P)
+        assert q.moe_qkv_packed_bytes(cfg) == nblk * P * H * bits // 8 + nblk * P * (H // 64) * 4
+    assert q.moe_qkv_packed_bytes(q.QkvConfig.make(4096, 4096, 512, 512)) == 11_796_480
+    for bad in [q.QkvConfig.make(1000, 8, 8, 8), q.QkvConfig.make(512, 0, 8, 8), q.QkvConfig.make(512, 8, 8, 8, bits=5),
+                q.QkvConfig.make(512, 8, 8, 8, flags=q.MOE_F_RESIDUAL), q.QkvConfig.make(512, 65536, 1, 1)]:
+        assert q.moe_qkv_packed_bytes(bad) == 0
+    L = q.lib()
+    cfg = q.QkvConfig.make(512, 8, 8, 8)
+    p = ctypes.c_void_p(1 << 20)
+    assert L.moe_qkv_forward(ctypes.byref(cfg), p, None, 1, p, p, p, None, None) == q.MOE_ERR_ARG
+    assert L.moe_qkv_forward(ctypes.byref(cfg), ctypes.c_void_p((1 << 20) + 16), None, 1, p, p, p, p,
+                             None) == q.MOE_ERR_ALIGN
+    assert L.moe_qkv_forward(ctypes.byref(cfg), None, None, 0, None, None, None, None, None) == q.MOE_OK
+    assert L.moe_qkv_pack(ctypes.byref(cfg), p, p, p, p, 10, p, 1024, None) == q.MOE_ERR_SHAPE
+    assert L.moe_qkv_pack(ctypes.byref(cfg), p, p, p, p, 1 << 20, p, 100, None) == q.MOE_ERR_WORKSPACE
+
