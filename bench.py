@@ -14,7 +14,9 @@ a bounded sample (the first tokens through all layers) and scaled to tokens/s.
 Other workloads (`--workload`): `prefill` (1155 tokens through one layer as an
 expert-grouped bf16 GEMM) and `streamed` (the stack with every layer's routed
 experts in pinned host memory, read over PCIe, and a per-layer HBM expert cache;
-its roofline is PCIe 5.0 x16). `--bits 3` selects 3-bit experts.
+its roofline is PCIe 5.0 x16) and `qkv` (the fused Q/K/V projection of hidden 4096
+into 4096 + 512 + 512 rows, one token per call by default). `--bits 3` selects
+3-bit codes.
 
 Two helper modes feed the `traffic` figure (HBM bytes per launch measured by the
 FETCH_SIZE / WRITE_SIZE counters, calibrated against a plain copy):
@@ -385,14 +387,109 @@ def stream_bench(args, w):
     del keep
 
 
+def qkv_bench(args):
+    """One step = one moe_qkv_forward call: the fused Q/K/V projection of hidden 4096
+    into 4096 + 512 + 512 rows (RMSNorm and gamma on), T tokens (default 1)."""
+    import numpy as np
+    import torch
+    import quantized_expert_mat_amd as q
+    import workload as wl
+
+    H, rows, bits = 4096, (4096, 512, 512), args.bits or 4
+    T = args.tokens or 1
+    cfg = q.QkvConfig.make(H, *rows, bits=bits, flags=q.MOE_F_RMSNORM)
+    R = sum(rows)
+    rng = np.random.default_rng(17)
+    codes = rng.integers(0, 1 << bits, size=(R, H), dtype=np.uint8)
+    sc = wl.bf16_bits_from_f32(np.abs(rng.normal(0, {4: 0.02, 3: 0.04, 2: 0.06}[bits], (R, H // 64)))
+                               .astype(np.float32))
+    bi = wl.bf16_bits_from_f32(rng.normal(0, 0.01, (R, H // 64)).astype(np.float32))
+    gamma_h = (1.0 + 0.1 * rng.normal(size=H)).astype(np.float32)
+    packed = torch.empty(q.moe_qkv_packed_bytes(cfg), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    q.moe_qkv_pack(cfg, torch.from_numpy(codes).cuda(), torch.from_numpy(sc.view(np.int16)).cuda(),
+                   torch.from_numpy(bi.view(np.int16)).cuda(), packed, ws)
+    q.moe_device_status(ws)
+    x_h = wl.tokens_x(99, T, H)
+    x = torch.from_numpy(x_h).cuda()
+    gamma = torch.from_numpy(gamma_h).cuda()
+    outs = [torch.empty((T, r), dtype=torch.float32, device="cuda") for r in rows]
+    stream = torch.cuda.current_stream()
+    n = max(args.steps, 1) * 100  # calls per timed run: a call takes microseconds
+
+    def step():
+        q.moe_qkv_forward(cfg, packed, T, x, *outs, gamma=gamma, stream=stream)
+
+    for _ in range(max(args.warmup, 1) * 100):
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg_s = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / n / 1e3
+    nbytes = packed.numel() + T * H * 4 + H * 4 + T * R * 4
+    achieved = nbytes / avg_s / 1e9
+    log(f"qkv: {n / elapsed:.0f} calls/s, launch avg {avg_s * 1e6:.2f} us, {achieved:.0f} GB/s")
+
+    cpu, par = None, None
+    if not args.no_cpu:
+        from oracle import ref
+        from tests.helpers import parity
+        mats, r0 = [], 0
+        for r in rows:
+            mats.append((codes[r0:r0 + r], sc[r0:r0 + r], bi[r0:r0 + r]))
+            r0 += r
+        got = [o.cpu().numpy() for o in outs]
+        worst = (0.0, 0.0)
+        t1 = time.perf_counter()
+        for t in range(T):
+            want = ref.qkv(mats, x_h[t], gamma=gamma_h, norm=True)
+            for g_, w_ in zip(got, want):
+                rm, rl = parity(g_[t], w_, f"qkv token {t}")
+                worst = (max(worst[0], rm), max(worst[1], rl))
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(T / dt, 3), "unit": "calls/s" if T == 1 else "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"all {T} token(s) of one call, {dt:.2f} s of single-threaded fp64 oracle arithmetic"}
+        par = {"tokens": T, "max_rel_err": float(worst[0]), "rel_l2": float(worst[1])}
+    out = {
+        "metric": f"fused Q/K/V projection calls/s, hidden 4096 -> 4096+512+512, {bits}-bit, {T} token(s)",
+        "value": round(n / elapsed, 1),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": max(args.warmup, 1) * 100,
+        "ms_per_step": round(elapsed / n * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i4",
+        "data": "synthetic",
+        "config": {"workload": "qkv-h4096", "hidden": H, "rows": list(rows), "bits": bits, "tokens": T,
+                   "rmsnorm": True, "bytes_per_call": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel_us": round(avg_s * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "parity": par,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=2, help="2: 4-bit stack, 3: 2-bit stack")
-    ap.add_argument("--bits", type=int, choices=[3], default=None,
-                    help="3: the 60-layer stack with 3-bit experts (instead of --config)")
+    ap.add_argument("--bits", type=int, choices=[2, 3, 4], default=None,
+                    help="3: the 60-layer stack with 3-bit experts (instead of --config); "
+                         "qkv: the code width (default 4)")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--cpu-tokens", type=int, default=4)
@@ -400,7 +497,7 @@ def main():
     ap.add_argument("--phased", action="store_true")
     ap.add_argument("--shared-gate", action="store_true",
                     help="give every layer a shared-expert gate (sigmoid(g . x_n) scales the shared expert)")
-    ap.add_argument("--workload", choices=["decode", "prefill", "streamed"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "streamed", "qkv"], default="decode",
                     help="decode: the 60-layer stack (default); prefill: 1155 tokens through one layer; "
                          "streamed: the stack with routed experts in pinned host memory "
                          "(default 16 layers, 64 tokens)")
@@ -427,6 +524,8 @@ def main():
         if args.tokens:
             w = w.replace(n_tokens=args.tokens)
         return prefill_bench(args, w)
+    if args.workload == "qkv":
+        return qkv_bench(args)
     if args.workload == "streamed":
         w = wl.STACK60_3BIT if args.bits == 3 else wl.CONFIGS[args.config]
         w = w.replace(n_layers=args.layers or 16, n_tokens=args.tokens or 64)
