@@ -330,3 +330,39 @@ def test_stack_decode_top10_with_tier():
             for j in range(K):
                 if mask[t, l, j]:
                     assert prev[j] in ih[t, l]
+
+
+@pytest.mark.parametrize("bits,gated", [(4, False), (3, False), (4, True)])
+def test_stack_decode_full_shape_specialised(bits, gated):
+    """The launch configuration the benchmark times: the specialised kernel (hidden
+    4096, I 1024, 512 experts, top-4 + shared, 256 workgroups), here over 3 layers and
+    4 tokens with the temporal tier, against the oracle on every output."""
+    from tests.helpers import DeviceCanonicalLayer
+    w = wl.CONFIGS[2].replace(n_layers=3, n_tokens=4)
+    if bits == 3:
+        w = wl.STACK60_3BIT.replace(n_layers=3, n_tokens=4)
+    L, T, K = w.n_layers, w.n_tokens, w.top_k
+    cfg = config_for(w)
+    dls = [DeviceLayer(w, l, chunk=8, gated=gated) for l in range(L)]
+    hls = [DeviceCanonicalLayer(w, l) for l in range(L)]
+    x = xs(w, T)
+    mask = wl.boost_mask(w.seed + 7, T, L, K, w.temporal_p)
+    y = torch.empty((T, w.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, L, K), dtype=torch.int32, device="cuda")
+    ws = ws_for(cfg, T, L)
+    q.moe_stack_decode(cfg, [d.weights() for d in dls], T, torch.from_numpy(x).cuda(), y, ws,
+                       boost_mask=torch.from_numpy(mask).cuda(), idx_trace=idx)
+    q.moe_device_status(ws)
+    ih = idx.cpu().numpy()
+
+    def follow(t, l, oi, gap):
+        if same_set(oi, ih[t, l]):
+            return None
+        assert gap < NEAR_TIE, f"t={t} l={l}: sets differ, gap {gap}"
+        return ih[t, l]
+
+    sg = (lambda l: wl.shared_gate_weights(w.seed, l, w.n_shared, w.hidden)) if gated else None
+    ys, sets, _ = ref.stack_decode(x, L, lambda l: hls[l].router, lambda l, e: hls[l].expert(e),
+                                   lambda l: hls[l].shared(), K, boost=mask, follow=follow, shared_gate_of=sg)
+    for t in range(T):
+        parity(y.cpu().numpy()[t], ys[t], f"full-shape stack token {t}")
