@@ -146,3 +146,31 @@ def test_qkv_sizes_and_validation():
     assert L.moe_qkv_pack(ctypes.byref(cfg), p, p, p, p, 10, p, 1024, None) == q.MOE_ERR_SHAPE
     assert L.moe_qkv_pack(ctypes.byref(cfg), p, p, p, p, 1 << 20, p, 100, None) == q.MOE_ERR_WORKSPACE
 
+
+
+def test_c_program_links_and_calls_the_abi(tmp_path):
+    """The header is plain C99 and a C program links against the library: it calls
+    the size functions (no device needed) and gets the closed forms."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include "qmoe.h"
+int main(void) {
+  moe_config c = {4096, 1024, 512, 4, 1, 4, 64, 0, 1e-6f};
+  moe_qkv_config k = {4096, 4096, 512, 512, 4, 64, 0, 1e-6f};
+  moe_config bad = c;
+  bad.bits = 5;
+  printf("%zu %zu %zu\n", moe_packed_expert_bytes(&c), moe_qkv_packed_bytes(&k), moe_packed_expert_bytes(&bad));
+  return 0;
+}
+""")
+    lib_dir = os.path.dirname(q.LIB_PATH)
+    exe = tmp_path / "abi"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    "-L", lib_dir, "-lqmoe", f"-Wl,-rpath,{lib_dir}"], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert out == ["7077888", "11796480", "0"]
