@@ -67,6 +67,36 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}), flush=True)
 
 
+def copy_rate_gbs(nbytes=1 << 31, reps=5):
+    """Device-to-device copy rate (bytes read + bytes written per second): a practical
+    HBM ceiling to read the roofline fraction against, beside the 8 TB/s peak."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    rate = 2 * nbytes * reps / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return rate
+
+
+def host_cpu():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _counter_rows(path, counter):
     import csv
     rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
@@ -593,6 +623,9 @@ def main():
     log(f"{tok_s:.1f} tok/s, {elapsed / args.steps * 1e3:.2f} ms/step, launch avg {avg_launch_s * 1e3:.3f} ms, "
         f"{achieved:.0f} GB/s")
 
+    copy_gbs = copy_rate_gbs()
+    log(f"device copy {copy_gbs:.0f} GB/s (read + write)")
+
     # realised temporal repeat fraction (routing workload check)
     ih = idx.cpu().numpy()
     rep = np.mean([len(set(ih[t, l]) & set(ih[t - 1, l])) / K for t in range(1, T) for l in range(L)])
@@ -604,7 +637,8 @@ def main():
         dt, par = cpu_baseline_and_parity(w, x0.cpu().numpy(), y.cpu().numpy(), ih, n, gated=args.shared_gate)
         cpu = {"value": round(n / dt, 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
                "sample": f"tokens 0-{n - 1} through all {L} layers (temporal tier replayed), "
-                         f"{dt:.1f} s of single-threaded fp64 oracle arithmetic"}
+                         f"{dt:.1f} s of single-threaded fp64 oracle arithmetic",
+               "host": f"{host_cpu()}, {os.cpu_count()} logical CPUs visible, 1 used"}
         log(f"cpu oracle: {dt:.1f} s for {n} tokens x {L} layers -> {cpu['value']:.4f} tok/s")
 
     traffic = None
@@ -638,7 +672,8 @@ def main():
                    "bytes_per_token": ptb, "mode": "phased" if args.phased else "persistent",
                    "shared_gate": bool(args.shared_gate)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "device_copy_gbs": round(copy_gbs, 1)},
         "cpu_baseline": cpu,
         "parity": par,
         "effective_hbm_gbs": round(ptb * tok_s / 1e9, 1),
