@@ -1437,10 +1437,10 @@ __device__ __forceinline__ void load_down(const DecodeArgs& a, const Lds& s, int
 }
 
 // Phase C's down projection from prefetched slots; partial sums per (pass, row) go
-// to s.acc exactly as in the direct loop.
+// to s.acc exactly as in the direct loop. only_pass >= 0: that pass's jobs only.
 template <int BITS, bool STREAM = false>
 __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s, int l,
-                                               const DownPre& dp) {
+                                               const DownPre& dp, int only_pass = -1) {
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave;
   const int r0 = blockIdx.x * a.rpw;
@@ -1450,6 +1450,7 @@ __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s
   for (int k = 0; k < kDnPre; ++k) {
     const DnJob j = down_job<STREAM>(a, s, l, k);
     if (j.pass < 0) continue;
+    if (only_pass >= 0 && j.pass != only_pass) continue;
     const int n = a.mode == MODE_EXPERT ? 1 : pass_count_of(a, s, j.pass);
     const int seg = n * g.Gi, grp = lane & (g.Gi - 1);
     if (j.pass != dig_pass) {
@@ -1594,8 +1595,9 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   return true;
 }
 
-// chunks per thread that poll the whole h exchange of the specialised shape at once
-constexpr int kSpecHPer = (kSpecK + kSpecS) * kSpecI / 2 / kThreads;
+// chunks per thread that poll the shared and the routed h of the specialised shape
+constexpr int kSpecShHPer = kSpecS * kSpecI / 2 / kThreads;
+constexpr int kSpecRtHPer = kSpecK * kSpecI / 2 / kThreads;
 
 template <int BITS, bool SPEC = false, bool STREAM = false>
 __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t, int l,
@@ -1611,16 +1613,28 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   // h vectors of this layer (polled; the down slots prefetched in phase B were
   // requested before these polls, so they have landed when the polls complete)
   float* hs = s.hstage;
-  {
+  if constexpr (SPEC) {
+    // The shared expert's h was published in phase A, long before the routed
+    // experts' h: its digits and its down pass (pass 1) are done first, while the
+    // routed h is still arriving; then the routed h and pass 0.
+    const Xv hv = xv_h(a);
+    const int K = a.K, Gi = g.Gi;
+    const Xv sh{hv.base + (size_t)K * I, a.S * I, hv.n_pad};
+    if (!wg_all(s.sm, xget<kSpecShHPer>(a, sh, hs + K * I, epoch_of(a, t, l)))) return false;
+    encode_vectors<false>(hs + K * I, a.S, I, 1.f, nullptr, s.hdig + K * Gi * kDigitStride,
+                          s.hsum + 4 * K * Gi);
+    __syncthreads();
+    down_from_regs<BITS, STREAM>(a, s, l, dp, 1);
+    const Xv rt{hv.base, K * I, hv.n_pad};
+    if (!wg_all(s.sm, xget<kSpecRtHPer>(a, rt, hs, epoch_of(a, t, l)))) return false;
+    SUBSTAMP(13);
+    encode_vectors<false>(hs, K, I, 1.f, nullptr, s.hdig, s.hsum);
+    __syncthreads();
+  } else {
     {
       const Xv hv = xv_h(a);
       const Xv part{hv.base, nlist * I, hv.n_pad};
-      bool ok;
-      if constexpr (SPEC)
-        ok = xget<kSpecHPer>(a, part, hs, epoch_of(a, t, l));
-      else
-        ok = xget(a, part, hs, epoch_of(a, t, l));
-      if (!wg_all(s.sm, ok)) return false;
+      if (!wg_all(s.sm, xget(a, part, hs, epoch_of(a, t, l)))) return false;
     }
     SUBSTAMP(13);
     encode_vectors<false>(hs, nlist, I, 1.f, nullptr, s.hdig, s.hsum);
@@ -1629,7 +1643,9 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   SUBSTAMP(11);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int npass = expert_mode ? 1 : a.npass;
-  if (pre_down) {
+  if constexpr (SPEC) {
+    down_from_regs<BITS, STREAM>(a, s, l, dp, 0);  // the routed pass (the shared one is done)
+  } else if (pre_down) {
     if (!down_loaded) load_down<BITS, STREAM>(a, s, l, dp);
     down_from_regs<BITS, STREAM>(a, s, l, dp);
   } else if (r0 < r1) {
