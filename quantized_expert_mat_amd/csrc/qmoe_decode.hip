@@ -94,6 +94,7 @@ struct DecodeArgs {
   int any_sgate;                 // some layer has a shared-expert gate
   int exact_rows;                // nwg * rpw == H: every workgroup owns exactly rpw rows
   int npass;
+  int npass_routed;  // passes [0, npass_routed) hold routed experts, the rest shared ones
   int pass_first[kMaxPass], pass_count[kMaxPass];
   int pre_router;                // router rows of a workgroup fit the register prefetch
   int pre_shared;                // shared gate/up items of a workgroup fit it
@@ -1437,10 +1438,10 @@ __device__ __forceinline__ void load_down(const DecodeArgs& a, const Lds& s, int
 }
 
 // Phase C's down projection from prefetched slots; partial sums per (pass, row) go
-// to s.acc exactly as in the direct loop. only_pass >= 0: that pass's jobs only.
+// to s.acc exactly as in the direct loop; only jobs of passes [p_lo, p_hi).
 template <int BITS, bool STREAM = false>
 __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s, int l,
-                                               const DownPre& dp, int only_pass = -1) {
+                                               const DownPre& dp, int p_lo = 0, int p_hi = kMaxPass) {
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave;
   const int r0 = blockIdx.x * a.rpw;
@@ -1450,7 +1451,7 @@ __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s
   for (int k = 0; k < kDnPre; ++k) {
     const DnJob j = down_job<STREAM>(a, s, l, k);
     if (j.pass < 0) continue;
-    if (only_pass >= 0 && j.pass != only_pass) continue;
+    if (j.pass < p_lo || j.pass >= p_hi) continue;
     const int n = a.mode == MODE_EXPERT ? 1 : pass_count_of(a, s, j.pass);
     const int seg = n * g.Gi, grp = lane & (g.Gi - 1);
     if (j.pass != dig_pass) {
@@ -1616,7 +1617,8 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   if constexpr (SPEC) {
     // The shared expert's h was published in phase A, long before the routed
     // experts' h: its digits and its down pass (pass 1) are done first, while the
-    // routed h is still arriving; then the routed h and pass 0.
+    // routed h is still arriving; then the routed h and pass 0. (The general
+    // kernel keeps one poll: there the split measured slower.)
     const Xv hv = xv_h(a);
     const int K = a.K, Gi = g.Gi;
     const Xv sh{hv.base + (size_t)K * I, a.S * I, hv.n_pad};
@@ -1624,7 +1626,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
     encode_vectors<false>(hs + K * I, a.S, I, 1.f, nullptr, s.hdig + K * Gi * kDigitStride,
                           s.hsum + 4 * K * Gi);
     __syncthreads();
-    down_from_regs<BITS, STREAM>(a, s, l, dp, 1);
+    down_from_regs<BITS, STREAM>(a, s, l, dp, a.npass_routed, a.npass);
     const Xv rt{hv.base, K * I, hv.n_pad};
     if (!wg_all(s.sm, xget<kSpecRtHPer>(a, rt, hs, epoch_of(a, t, l)))) return false;
     SUBSTAMP(13);
@@ -1644,7 +1646,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int npass = expert_mode ? 1 : a.npass;
   if constexpr (SPEC) {
-    down_from_regs<BITS, STREAM>(a, s, l, dp, 0);  // the routed pass (the shared one is done)
+    down_from_regs<BITS, STREAM>(a, s, l, dp, 0, a.npass_routed);  // the shared pass is done
   } else if (pre_down) {
     if (!down_loaded) load_down<BITS, STREAM>(a, s, l, dp);
     down_from_regs<BITS, STREAM>(a, s, l, dp);
@@ -1763,6 +1765,7 @@ __device__ __forceinline__ void specialise(DecodeArgs& a, bool gate) {
   a.rpw = kSpecH / kSpecNwg;
   a.exact_rows = 1;
   a.npass = 2;
+  a.npass_routed = 1;
   a.pass_first[0] = 0; a.pass_count[0] = kSpecK;
   a.pass_first[1] = kSpecK; a.pass_count[1] = kSpecS;
   a.const_pass = 1;
@@ -1964,6 +1967,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
     np = 1;
   } else {
     add_passes(0, a.K);
+    a.npass_routed = np;
     add_passes(a.K, a.S);
   }
   a.npass = np;
