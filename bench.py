@@ -539,16 +539,16 @@ def main():
         return copy_calibration()
     if args.traffic_record:
         import workload as wl
-        w = wl.STACK60_3BIT if args.bits == 3 else wl.CONFIGS[args.config]
+        w = wl.STACK60_3BIT if args.bits == 3 else wl.WORKLOADS[args.config]
         return traffic_record(*args.traffic_record, w.name, args.layers or w.n_layers, args.tokens or w.n_tokens)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: the decode stack fits one MI355X's HBM and this build has "
+        print(f"bench.py runs on one GPU: the decode stack fits one MI355X's HBM and the library has "
               f"no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import workload as wl
     if args.workload == "prefill":
-        w = wl.CONFIGS[4]
+        w = wl.PREFILL1155
         if args.bits == 3:
             w = w.replace(name="prefill1155-3bit", bits=3, sigma_scale=0.04)
         if args.tokens:
@@ -557,7 +557,7 @@ def main():
     if args.workload == "qkv":
         return qkv_bench(args)
     if args.workload == "streamed":
-        w = wl.STACK60_3BIT if args.bits == 3 else wl.CONFIGS[args.config]
+        w = wl.STACK60_3BIT if args.bits == 3 else wl.WORKLOADS[args.config]
         w = w.replace(n_layers=args.layers or 16, n_tokens=args.tokens or 64)
         return stream_bench(args, w)
 
@@ -567,7 +567,7 @@ def main():
     from workload import device as wdev
     from tests.helpers import DeviceLayer, config_for
 
-    w = wl.STACK60_3BIT if args.bits == 3 else wl.CONFIGS[args.config]
+    w = wl.STACK60_3BIT if args.bits == 3 else wl.WORKLOADS[args.config]
     if args.layers or args.tokens:
         w = w.replace(n_layers=args.layers or w.n_layers, n_tokens=args.tokens or w.n_tokens)
     L, T, K, H = w.n_layers, w.n_tokens, w.top_k, w.hidden

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 SIGMA3 = 0.04
-LAYER3 = wl.CONFIGS[1].replace(name="layer-h4096-e512-3bit", bits=3, sigma_scale=SIGMA3)
+LAYER3 = wl.LAYER_H4096.replace(name="layer-h4096-e512-3bit", bits=3, sigma_scale=SIGMA3)
 
 
 def small(**kw):

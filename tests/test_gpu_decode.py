@@ -12,8 +12,8 @@ from workload import device as wdev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TINY = wl.CONFIGS[0]   # H 1024, I 256, E 64, no norm / residual
-LAYER = wl.CONFIGS[1]  # H 4096, I 1024, E 512, norm + residual
+TINY = wl.TINY_LAYER   # H 1024, I 256, E 64, no norm / residual
+LAYER = wl.LAYER_H4096  # H 4096, I 1024, E 512, norm + residual
 
 
 def small(**kw):
@@ -338,7 +338,7 @@ def test_stack_decode_full_shape_specialised(bits, gated):
     4096, I 1024, 512 experts, top-4 + shared, 256 workgroups), here over 3 layers and
     4 tokens with the temporal tier, against the oracle on every output."""
     from tests.helpers import DeviceCanonicalLayer
-    w = wl.CONFIGS[2].replace(n_layers=3, n_tokens=4)
+    w = wl.STACK60_4BIT.replace(n_layers=3, n_tokens=4)
     if bits == 3:
         w = wl.STACK60_3BIT.replace(n_layers=3, n_tokens=4)
     L, T, K = w.n_layers, w.n_tokens, w.top_k

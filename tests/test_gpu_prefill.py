@@ -13,7 +13,7 @@ from tests.helpers import (NEAR_TIE, DeviceCanonicalLayer, DeviceLayer, HostLaye
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-PREFILL = wl.CONFIGS[4]  # 1155 tokens, H 4096, I 1024, E 512, Zipf(1.1) routing
+PREFILL = wl.PREFILL1155  # 1155 tokens, H 4096, I 1024, E 512, Zipf(1.1) routing
 
 
 def small(**kw):

@@ -12,7 +12,7 @@ from tests.helpers import NEAR_TIE, DeviceLayer, HostLayer, config_for, parity, 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-LAYER = wl.CONFIGS[1]  # H 4096, I 1024, E 512, norm + residual
+LAYER = wl.LAYER_H4096  # H 4096, I 1024, E 512, norm + residual
 
 
 def small(**kw):

@@ -109,7 +109,7 @@ def test_streamed_equals_resident_stack():
 def test_streamed_full_layer_shape():
     """Hidden 4096, I 1024, 512 experts, top-4 + shared: two layers, 7.2 GB of
     pinned host experts."""
-    w = wl.CONFIGS[1].replace(name="streamed-h4096", n_layers=2, n_tokens=3, temporal_p=0.27)
+    w = wl.LAYER_H4096.replace(name="streamed-h4096", n_layers=2, n_tokens=3, temporal_p=0.27)
     dls = [DeviceLayer(w, l) for l in range(w.n_layers)]
     hls = [DeviceCanonicalLayer(w, l) for l in range(w.n_layers)]
     x = wl.tokens_x(w.seed + 1000, w.n_tokens, w.hidden)

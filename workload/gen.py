@@ -33,7 +33,8 @@ __all__ = [
     "mix64", "stream_key", "words", "codes", "normals", "f32_from_normals",
     "bf16_bits_from_f32", "bf16_bits_to_f32", "bf16_from_normals",
     "ExpertSpec", "expert_canonical", "router_weights", "shared_gate_weights", "tokens_x",
-    "boost_mask", "zipf_gumbel_scores", "WorkloadConfig", "CONFIGS", "STACK60_3BIT",
+    "boost_mask", "zipf_gumbel_scores", "WorkloadConfig", "WORKLOADS", "TINY_LAYER", "LAYER_H4096",
+    "STACK60_4BIT", "STACK60_2BIT", "PREFILL1155", "STACK60_3BIT",
 ]
 
 M64 = (1 << 64) - 1
@@ -214,14 +215,13 @@ class WorkloadConfig:
 # The five workloads: a tiny layer, one layer at the flash-moe shape, the 60-layer
 # 4-bit decode stack with 27% temporal routing correlation, the same stack with
 # 2-bit experts, and a 1155-token prefill through one layer with Zipf(1.1) routing.
-CONFIGS = [
-    WorkloadConfig("tiny-layer", 1024, 256, 64, rmsnorm=False, residual=False),
-    WorkloadConfig("layer-h4096-e512", 4096, 1024, 512),
-    WorkloadConfig("stack60-4bit", 4096, 1024, 512, n_layers=60, n_tokens=256, temporal_p=0.27),
-    WorkloadConfig("stack60-2bit", 4096, 1024, 512, bits=2, sigma_scale=0.06, n_layers=60,
-                   n_tokens=256, temporal_p=0.27),
-    WorkloadConfig("prefill1155", 4096, 1024, 512, n_tokens=1155, zipf=1.1),
-]
+TINY_LAYER = WorkloadConfig("tiny-layer", 1024, 256, 64, rmsnorm=False, residual=False)
+LAYER_H4096 = WorkloadConfig("layer-h4096-e512", 4096, 1024, 512)
+STACK60_4BIT = WorkloadConfig("stack60-4bit", 4096, 1024, 512, n_layers=60, n_tokens=256, temporal_p=0.27)
+STACK60_2BIT = WorkloadConfig("stack60-2bit", 4096, 1024, 512, bits=2, sigma_scale=0.06, n_layers=60,
+                              n_tokens=256, temporal_p=0.27)
+PREFILL1155 = WorkloadConfig("prefill1155", 4096, 1024, 512, n_tokens=1155, zipf=1.1)
+WORKLOADS = [TINY_LAYER, LAYER_H4096, STACK60_4BIT, STACK60_2BIT, PREFILL1155]
 
 # The 60-layer decode stack with 3-bit experts: a synthetic group-affine stand-in
 # for the 3-bit experts of the autoresearch page ("Optimizaciones Efectivas"),
