@@ -50,9 +50,7 @@ constexpr int kBM = 64;            // rows (token-expert pairs) per thick m-tile
 constexpr int kGuCols = 64;        // intermediate columns per gate/up workgroup
 constexpr int kDnCols = 128;       // output columns per down workgroup
 constexpr int kSortMax = 16384;    // routed (token, expert) pairs per pass
-constexpr int kPairBits = 14;      // pair index bits in a sort key
-static_assert((1 << kPairBits) >= kSortMax && (long long)kMaxE << kPairBits <= (1ll << 32),
-              "sort keys hold an expert and a pair index");
+constexpr int kGroupWaves = 1024 / kWave;  // waves of the grouping workgroup
 
 // ---------------------------------------------------------------------------
 // Workspace layout of one prefill pass
@@ -332,10 +330,10 @@ __global__ __launch_bounds__(256) void select_kernel(PArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// group: one workgroup of 1024 threads. Sorting the keys (expert << 14 | pair)
-// orders pairs by expert and, within an expert, by (token, slot): a stable counting
-// sort. Writes rowtok, pos and the m-tile table (routed experts in index order, then
-// the shared experts, whose rows are all tokens in order).
+// group: one workgroup of 1024 threads, a counting sort of the (token, slot) pairs by
+// expert: per-expert counts, their exclusive scan, then every pair takes the next
+// free row of its expert. Writes rowtok, pos and the m-tile table (routed experts in
+// index order, then the shared experts, whose rows are all tokens in order).
 // ---------------------------------------------------------------------------
 // (thin << 16) | thick: the m-tiles of an expert with c > 0 rows: full thick tiles
 // of kBM rows, then the remainder as a thin (<= 16 rows) or a thick tile.
@@ -355,71 +353,77 @@ __device__ inline void write_tiles(const PArgs& a, int e, int row0, int c, int t
   else if (rem > 0) a.thin[1 + thin_at] = make_int4(e, row0 + full * kBM, rem, 0);
 }
 
-__global__ __launch_bounds__(1024) void group_kernel(PArgs a, int n2) {
-  extern __shared__ unsigned gl[];
-  unsigned* keys = gl;                               // [n2]
-  int* first = reinterpret_cast<int*>(gl + n2);      // [E]
-  int* last = first + a.E;                           // [E]
-  int* scan = last + a.E;                            // [1024]
+// Inclusive prefix sum over the 1024 threads of a workgroup: a shuffle scan inside
+// each wave, then one over the 16 wave totals. wsum: 16 ints of LDS.
+__device__ inline int block_scan_1024(int v, int* wsum) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  __syncthreads();  // a previous call's readers of wsum are done
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  if (lane == kWave - 1) wsum[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int t = lane < kGroupWaves ? wsum[lane] : 0;
+    for (int o = 1; o < kGroupWaves; o <<= 1) {
+      const int u = __shfl_up(t, o, kWave);
+      if (lane >= o) t += u;
+    }
+    if (lane < kGroupWaves) wsum[lane] = t;
+  }
+  __syncthreads();
+  return v + (w > 0 ? wsum[w - 1] : 0);
+}
+
+__global__ __launch_bounds__(1024) void group_kernel(PArgs a) {
+  extern __shared__ int gl[];
+  const int E = a.E;
+  int* cnt = gl;              // [E] pairs per expert, then the rows placed so far
+  int* off = cnt + E;         // [E] first row of each expert
+  int* scan = off + E;        // [kGroupWaves] block-scan wave totals
   const int tid = threadIdx.x;
   const int np = a.n * a.K;
-  for (int i = tid; i < n2; i += 1024) {
-    unsigned k = 0xFFFFFFFFu;
-    if (i < np) {
-      int e = a.idx[i];
-      if (e < 0 || e >= a.E) {
-        set_dev_err(a.err, DEV_BAD_INDEX);
-        e = 0;
-      }
-      k = ((unsigned)e << kPairBits) | (unsigned)i;
-    }
-    keys[i] = k;
-  }
-  for (int e = tid; e < a.E; e += 1024) { first[e] = -1; last[e] = -2; }
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (n2 >> 1); i += 1024) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const unsigned x = keys[lo], y = keys[hi];
-        if ((x > y) == up) { keys[lo] = y; keys[hi] = x; }
-      }
-      __syncthreads();
-    }
-  }
   for (int i = tid; i < np; i += 1024) {
-    const unsigned k = keys[i];
-    const int e = (int)(k >> kPairBits), p = (int)(k & ((1u << kPairBits) - 1));
-    a.rowtok[i] = p / a.K;
-    a.pos[p] = i;
-    if (i == 0 || (int)(keys[i - 1] >> kPairBits) != e) first[e] = i;
-    if (i == np - 1 || (int)(keys[i + 1] >> kPairBits) != e) last[e] = i;
+    int e = a.idx[i];
+    if (e < 0 || e >= E) {
+      set_dev_err(a.err, DEV_BAD_INDEX);
+      e = 0;
+    }
+    atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the counts (one expert per thread, E <= 1024): off[e]
+  const int c = tid < E ? cnt[tid] : 0;
+  const int c_incl = block_scan_1024(c, scan);
+  if (tid < E) {
+    off[tid] = c_incl - c;
+    cnt[tid] = 0;
+  }
+  __syncthreads();
+  // each pair takes the next free row of its expert (LDS atomics: the order of an
+  // expert's rows varies from call to call, its rows' results do not, since every
+  // row of a tile is computed on its own)
+  for (int i = tid; i < np; i += 1024) {
+    int e = a.idx[i];
+    if (e < 0 || e >= E) e = 0;
+    const int row = off[e] + atomicAdd(&cnt[e], 1);
+    a.rowtok[row] = i / a.K;
+    a.pos[i] = row;
   }
   for (int s = 0; s < a.S; ++s)
     for (int t = tid; t < a.n; t += 1024) a.rowtok[np + s * a.n + t] = t;
-  __syncthreads();
-  // m-tiles of an expert with c rows: full 128-row tiles, then the remainder as a
+  // m-tiles of an expert with c rows: full kBM-row tiles, then the remainder as a
   // thin tile (<= 16 rows) or a thick one. Exclusive scan over experts of the packed
   // counts (thin << 16 | thick), one expert per thread (E <= 1024).
-  int c = 0, cnt = 0;
-  if (tid < a.E) {
-    c = last[tid] - first[tid] + 1;
-    if (c > 0) cnt = tile_counts(c);
-  }
-  scan[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  const int tot = scan[1023];
-  if (cnt > 0) {
-    const int ex = scan[tid] - cnt;
-    write_tiles(a, tid, first[tid], c, ex >> 16, ex & 0xFFFF);
+  const int tiles = c > 0 ? tile_counts(c) : 0;
+  const int t_incl = block_scan_1024(tiles, scan);
+  const int tot = scan[kGroupWaves - 1];
+  if (tiles > 0) {
+    const int ex = t_incl - tiles;
+    write_tiles(a, tid, off[tid], c, ex >> 16, ex & 0xFFFF);
   }
   // shared experts after the routed ones (one thread each; S <= 2)
   if (tid == 0) {
@@ -776,12 +780,6 @@ __global__ void clear_err(unsigned* err) {
   if (threadIdx.x == 0) *err = 0u;
 }
 
-int next_pow2(int v) {
-  int p = 1;
-  while (p < v) p <<= 1;
-  return p;
-}
-
 dim3 xcd_grid(int items) { return dim3((unsigned)(8 * ((items + 7) / 8))); }
 
 // The gate/up and down passes, thin (one m-tile) and thick (kThickMT m-tiles) items.
@@ -839,7 +837,7 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
   a.sgc = reinterpret_cast<float*>(ws + pl.sgc);
 
   static bool attr_done = false;
-  const size_t group_lds_max = sizeof(unsigned) * (kSortMax + 2 * kMaxE + 1024);
+  const size_t group_lds_max = sizeof(int) * (2 * (size_t)kMaxE + kGroupWaves);
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&group_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -867,9 +865,8 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
       hipLaunchKernelGGL(router_kernel, dim3((c.n_experts + 63) / 64, (n + 63) / 64), dim3(256), 0,
                          stream, a);
     hipLaunchKernelGGL(select_kernel, dim3((n + 3) / 4), dim3(256), 0, stream, a);
-    const int n2 = next_pow2(n * c.top_k < 2 ? 2 : n * c.top_k);
-    const size_t glds = sizeof(unsigned) * ((size_t)n2 + 2 * c.n_experts + 1024);
-    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), glds, stream, a, n2);
+    const size_t glds = sizeof(int) * (2 * (size_t)c.n_experts + kGroupWaves);
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), glds, stream, a);
     // grids: upper bounds of the m-tiles this pass can have, rounded to whole XCDs.
     // Every expert has at most one thin tile; a thick tile has at least 17 rows.
     const int TK = n * c.top_k;

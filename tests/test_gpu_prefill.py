@@ -180,3 +180,18 @@ def test_prefill_top10(T):
     yh, ih, wh = run_prefill(w, dl, x, sel)
     toks = range(T) if T <= 64 else list(range(0, T, 97)) + [1637, 1638, 1639, T - 1]
     check_tokens(w, hl, x, yh, ih, wh, sel, toks, what=f"top-10 T={T}")
+
+
+def test_prefill_repeat_calls_bit_identical():
+    """Rows of an expert are placed by LDS atomics, so their order may change between
+    calls; every row is computed on its own, so the outputs may not."""
+    w = small(n_experts=8)
+    T = 300
+    dl = DeviceLayer(w, 0)
+    x = wl.tokens_x(w.seed + 1000, T, w.hidden)
+    sel, _ = wl.zipf_gumbel_scores(w.seed + 3, T, w.n_experts, 1.1)
+    outs = [run_prefill(w, dl, x, sel) for _ in range(3)]
+    for y, idx, wts in outs[1:]:
+        assert np.array_equal(y, outs[0][0])
+        assert np.array_equal(idx, outs[0][1])
+        assert np.array_equal(wts, outs[0][2])
