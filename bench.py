@@ -511,6 +511,91 @@ def qkv_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def layer_bench(args):
+    """One step = one moe_layer_forward call of one token through one layer at the
+    flash-moe layer shape (hidden 4096, 512 experts, I 1024, top-4 + shared), with the
+    caches flushed before each call (a 1 GiB buffer is rewritten), so the weights
+    come from HBM."""
+    import numpy as np
+    import torch
+    import quantized_expert_mat_amd as q
+    import workload as wl
+    from tests.helpers import DeviceLayer, config_for
+
+    w = wl.LAYER_H4096
+    T = args.tokens or 1
+    cfg = config_for(w)
+    ws = torch.empty(q.moe_workspace_bytes(cfg, T, 1), dtype=torch.uint8, device="cuda")
+    dl = DeviceLayer(w, 0, chunk=8, ws=ws)
+    x_h = wl.tokens_x(w.seed + 1000, T, w.hidden)
+    x = torch.from_numpy(x_h).cuda()
+    y = torch.empty_like(x)
+    idx = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    lw = dl.weights()
+    stream = torch.cuda.current_stream()
+    n = max(args.steps, 1) * 10
+    times = []
+    for i in range(max(args.warmup, 1) + n):
+        flush.add_(1)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        q.moe_layer_forward(cfg, lw, T, x, y, ws, idx_out=idx, stream=stream)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        if i >= max(args.warmup, 1):
+            times.append(s0.elapsed_time(s1) / 1e3)
+    q.moe_device_status(ws)
+    med = float(np.median(times))
+    nbytes = per_token_bytes(w.replace(n_layers=1)) * T
+    achieved = nbytes / med / 1e9
+    log(f"layer: median {med * 1e6:.1f} us per call ({T} token(s)), {achieved:.0f} GB/s")
+    cpu, par = None, None
+    if not args.no_cpu:
+        from oracle import ref
+        from tests.helpers import DeviceCanonicalLayer, NEAR_TIE, parity, same_set
+        cl = DeviceCanonicalLayer(w, 0)
+        ih = idx.cpu().numpy()
+        worst = (0.0, 0.0)
+        dt = 0.0
+        for t in range(T):
+            for e in ih[t]:
+                cl.expert(int(e))
+            cl.shared()
+            t1 = time.perf_counter()
+            r = ref.layer_decode(x_h[t], cl.router, cl.expert, cl.shared(), w.top_k)
+            dt += time.perf_counter() - t1
+            if not same_set(r.idx, ih[t]):
+                assert r.gap < NEAR_TIE
+                r = ref.layer_decode(x_h[t], cl.router, cl.expert, cl.shared(), w.top_k, force_idx=ih[t])
+            rm, rl = parity(y.cpu().numpy()[t], r.y, f"layer token {t}")
+            worst = (max(worst[0], rm), max(worst[1], rl))
+        cpu = {"value": round(T / dt, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
+               "sample": f"the call's {T} token(s) through the layer, {dt:.2f} s of single-threaded fp64 oracle "
+                         f"arithmetic"}
+        par = {"tokens": T, "max_rel_err": float(worst[0]), "rel_l2": float(worst[1])}
+    out = {
+        "metric": "single-layer decode latency, hidden 4096, 512 experts, top-4 + shared, 4-bit, cold caches",
+        "value": round(med * 1e6, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": max(args.warmup, 1),
+        "ms_per_step": round(med * 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i4",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "bytes_per_call": nbytes, "caches": "flushed before each call"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "parity": par,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -527,7 +612,7 @@ def main():
     ap.add_argument("--phased", action="store_true")
     ap.add_argument("--shared-gate", action="store_true",
                     help="give every layer a shared-expert gate (sigmoid(g . x_n) scales the shared expert)")
-    ap.add_argument("--workload", choices=["decode", "prefill", "streamed", "qkv"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "streamed", "qkv", "layer"], default="decode",
                     help="decode: the 60-layer stack (default); prefill: 1155 tokens through one layer; "
                          "streamed: the stack with routed experts in pinned host memory "
                          "(default 16 layers, 64 tokens)")
@@ -556,6 +641,8 @@ def main():
         return prefill_bench(args, w)
     if args.workload == "qkv":
         return qkv_bench(args)
+    if args.workload == "layer":
+        return layer_bench(args)
     if args.workload == "streamed":
         w = wl.STACK60_3BIT if args.bits == 3 else wl.WORKLOADS[args.config]
         w = w.replace(n_layers=args.layers or 16, n_tokens=args.tokens or 64)

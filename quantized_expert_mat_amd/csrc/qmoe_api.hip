@@ -91,6 +91,20 @@ moe_status check_qkv(const moe_qkv_config* c) {
   return MOE_OK;
 }
 
+moe_status layer_ptrs(const moe_config& c, const moe_layer_weights& w, int l, LayerPtrs& p) {
+  REQUIRE(w.experts && w.router_w, MOE_ERR_ARG, "layer %d: experts/router_w is NULL", l);
+  REQUIRE(c.n_shared == 0 || w.shared, MOE_ERR_ARG, "layer %d: shared is NULL", l);
+  REQUIRE(aligned(w.experts, 256) && aligned(w.router_w, 256) && (!w.shared || aligned(w.shared, 256)) &&
+              (!w.gamma || aligned(w.gamma, 16)) && (!w.shared_gate || aligned(w.shared_gate, 16)),
+          MOE_ERR_ALIGN, "layer %d: weight pointers must be 256-byte aligned (gamma, shared_gate 16-byte)", l);
+  p.experts = static_cast<const uint8_t*>(w.experts);
+  p.shared = static_cast<const uint8_t*>(w.shared);
+  p.router = w.router_w;
+  p.gamma = w.gamma;
+  p.sgate = c.n_shared > 0 ? w.shared_gate : nullptr;
+  return MOE_OK;
+}
+
 moe_status upload_layers(const moe_config& c, int L, const moe_layer_weights* layers, uint8_t* ws,
                          const WsLayout& wl, hipStream_t st) {
   LayerPtrs tmp[64];
@@ -98,18 +112,8 @@ moe_status upload_layers(const moe_config& c, int L, const moe_layer_weights* la
   for (int l0 = 0; l0 < L; l0 += 64) {
     const int n = L - l0 < 64 ? L - l0 : 64;
     for (int i = 0; i < n; ++i) {
-      const moe_layer_weights& w = layers[l0 + i];
-      REQUIRE(w.experts && w.router_w, MOE_ERR_ARG, "layer %d: experts/router_w is NULL", l0 + i);
-      REQUIRE(c.n_shared == 0 || w.shared, MOE_ERR_ARG, "layer %d: shared is NULL", l0 + i);
-      REQUIRE(aligned(w.experts, 256) && aligned(w.router_w, 256) &&
-                  (!w.shared || aligned(w.shared, 256)) && (!w.gamma || aligned(w.gamma, 16)) &&
-                  (!w.shared_gate || aligned(w.shared_gate, 16)),
-              MOE_ERR_ALIGN, "layer %d: weight pointers must be 256-byte aligned", l0 + i);
-      tmp[i].experts = static_cast<const uint8_t*>(w.experts);
-      tmp[i].shared = static_cast<const uint8_t*>(w.shared);
-      tmp[i].router = w.router_w;
-      tmp[i].gamma = w.gamma;
-      tmp[i].sgate = c.n_shared > 0 ? w.shared_gate : nullptr;
+      const moe_status s = layer_ptrs(c, layers[l0 + i], l0 + i, tmp[i]);
+      if (s != MOE_OK) return s;
     }
     hipError_t e = hipMemcpyAsync(dev + l0, tmp, sizeof(LayerPtrs) * n, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "uploading the layer table");
@@ -188,14 +192,15 @@ moe_status moe_route(const moe_config* cfg, int32_t T, const float* x, const flo
   moe_layer_weights lw = {router_w, nullptr, router_w, gamma, nullptr};  // experts unused when routing
   moe_config c1 = *cfg;
   c1.n_shared = 0;
-  s = upload_layers(c1, 1, &lw, w8, wl, st);
-  if (s != MOE_OK) return s;
   DecodeRequest r = {};
+  s = layer_ptrs(c1, lw, 0, r.layer0);
+  if (s != MOE_OK) return s;
+  r.inline_layer = true;
   r.mode = 1;  // MODE_ROUTE
   r.cfg = c1;
   r.L = 1;
   r.T = T;
-  r.layers_dev = reinterpret_cast<const LayerPtrs*>(w8 + wl.layers);
+  r.layers_dev = nullptr;
   r.x0 = x;
   r.sel_bias = sel_bias;
   r.boosted = boosted;
@@ -266,14 +271,15 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_layer_weights* lay
     return s;
   }
   const WsLayout wl = ws_layout(*cfg, T, 1);
-  s = upload_layers(*cfg, 1, layer, w8, wl, st);
-  if (s != MOE_OK) return s;
   DecodeRequest r = {};
+  s = layer_ptrs(*cfg, *layer, 0, r.layer0);
+  if (s != MOE_OK) return s;
+  r.inline_layer = true;
   r.mode = 0;  // MODE_LAYER
   r.cfg = *cfg;
   r.L = 1;
   r.T = T;
-  r.layers_dev = reinterpret_cast<const LayerPtrs*>(w8 + wl.layers);
+  r.layers_dev = nullptr;
   r.x0 = x;
   r.y = y;
   r.sel_bias = sel_bias;

@@ -67,7 +67,8 @@ struct DecodeArgs {
   int E, K, S, flags, mode;
   float eps;
   int L, T;
-  const LayerPtrs* layers;
+  const LayerPtrs* layers;       // [L] in device memory, or NULL: the one layer is layer0
+  LayerPtrs layer0;
   const uint8_t* single_expert;  // MODE_EXPERT
   const float* x0;               // [T][H]
   float* y;                      // [T][H]
@@ -1787,11 +1788,18 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
     s.sm->pass_count[threadIdx.x] = a.pass_count[threadIdx.x];
     s.sm->pass_lgn[threadIdx.x] = log2i(a.pass_count[threadIdx.x] > 0 ? a.pass_count[threadIdx.x] : 1);
   }
-  {
+  if (a.layers) {
     const __attribute__((address_space(1))) unsigned long long* src =
         (const __attribute__((address_space(1))) unsigned long long*)(uintptr_t)a.layers;
     unsigned long long* dst = reinterpret_cast<unsigned long long*>(lds_raw + a.lds_layers);
     for (int i = threadIdx.x; i < (int)(sizeof(LayerPtrs) / 8) * a.n_lds_layers; i += kThreads) dst[i] = src[i];
+  } else if (a.n_lds_layers == 1 && threadIdx.x == 0) {
+    LayerPtrs* dst = reinterpret_cast<LayerPtrs*>(lds_raw + a.lds_layers);
+    dst->experts = a.layer0.experts;
+    dst->shared = a.layer0.shared;
+    dst->router = a.layer0.router;
+    dst->gamma = a.layer0.gamma;
+    dst->sgate = a.layer0.sgate;
   }
   __syncthreads();
   if constexpr (SPEC) {
@@ -1916,6 +1924,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.L = r.L;
   a.T = r.T;
   a.layers = r.layers_dev;
+  if (r.inline_layer) a.layer0 = r.layer0;
   a.single_expert = r.single_expert;
   a.x0 = r.x0;
   a.y = r.y;
@@ -2006,7 +2015,10 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.lds_hsum = words; words = up4(words + 4 * nlist * Gi);
   a.lds_acc = words; words = up4(words + kMaxPass * rpw);
   a.lds_xres = words; words = up4(words + rpw);
-  a.n_lds_layers = (r.mode == MODE_EXPERT || !r.layers_dev) ? 0 : std::min(r.L, kLdsLayers);
+  a.n_lds_layers = r.mode == MODE_EXPERT ? 0
+                   : r.inline_layer ? 1
+                   : r.layers_dev   ? std::min(r.L, kLdsLayers)
+                                    : 0;
   a.lds_layers = (words + 1) & ~1;  // 8-byte aligned
   words = up4(a.lds_layers + a.n_lds_layers * (int)(sizeof(LayerPtrs) / 4));
   // register prefetch eligibility (see load_static / load_down)

@@ -173,6 +173,10 @@ struct DecodeRequest {
   uint8_t* cache;
   int cslots;
   uint8_t* hit_out;
+  // one-layer calls: the layer's pointers travel in the kernel arguments
+  // (layers_dev == NULL), so no table is copied to the device first
+  bool inline_layer;
+  LayerPtrs layer0;
 };
 
 // mats: 3 (n experts: gate, up, down) or 1 (n matrices of geo.I rows, geo.H columns)
