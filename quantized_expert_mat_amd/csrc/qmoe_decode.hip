@@ -1134,7 +1134,9 @@ __device__ __forceinline__ void cache_decide(const DecodeArgs& a, const Lds& s, 
     }
   }
   for (int r = 0; r < K; ++r) {
-    const int k = __builtin_ctzll(__ballot(lane < K && rank == r));
+    const unsigned long long who = __ballot(lane < K && rank == r);
+    if (!who) continue;  // the K selected experts are distinct: every rank is taken
+    const int k = __builtin_ctzll(who);
     if (__builtin_amdgcn_readlane(my_hit, k)) continue;
     const unsigned e = (unsigned)__builtin_amdgcn_readlane(my_idx, k);
     const unsigned use = (unsigned)(ent >> 32);
