@@ -366,3 +366,50 @@ def test_stack_decode_full_shape_specialised(bits, gated):
                                    lambda l: hls[l].shared(), K, boost=mask, follow=follow, shared_gate_of=sg)
     for t in range(T):
         parity(y.cpu().numpy()[t], ys[t], f"full-shape stack token {t}")
+
+
+def test_stack60_full_workload_sampled():
+    """The benchmark's workload and launch: 60 layers x 256 tokens of the 4-bit stack
+    (218 GB of experts resident), one launch. Tokens 0-1 against the oracle through
+    all 60 layers; every token's routing checked by properties that hold at any
+    size: indices in range and distinct, and every boosted expert of the temporal
+    tier selected."""
+    from tests.helpers import DeviceCanonicalLayer
+    w = wl.STACK60_4BIT
+    L, T, K, H = w.n_layers, w.n_tokens, w.top_k, w.hidden
+    cfg = config_for(w)
+    ws = ws_for(cfg, T, L)
+    dls = [DeviceLayer(w, l, chunk=8, ws=ws) for l in range(L)]
+    x = xs(w, T)
+    mask = wl.boost_mask(w.seed + 7, T, L, K, w.temporal_p)
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, L, K), dtype=torch.int32, device="cuda")
+    q.moe_stack_decode(cfg, [d.weights() for d in dls], T, torch.from_numpy(x).cuda(), y, ws,
+                       boost_mask=torch.from_numpy(mask).cuda(), idx_trace=idx)
+    q.moe_device_status(ws)
+    yh, ih = y.cpu().numpy(), idx.cpu().numpy()
+    del dls, ws
+    torch.cuda.empty_cache()  # hand the 218 GB back before the next tests
+    assert np.isfinite(yh).all()
+    assert ((ih >= 0) & (ih < w.n_experts)).all()
+    for t in range(T):
+        for l in range(L):
+            assert len(set(ih[t, l].tolist())) == K
+            if t > 0:
+                prev = sorted(ih[t - 1, l].tolist())
+                for j in range(K):
+                    if mask[t, l, j]:
+                        assert prev[j] in ih[t, l]
+    hls = [DeviceCanonicalLayer(w, l) for l in range(L)]
+
+    def follow(t, l, oi, gap):
+        if same_set(oi, ih[t, l]):
+            return None
+        assert gap < NEAR_TIE, f"t={t} l={l}: sets differ, gap {gap}"
+        return ih[t, l]
+
+    n = 2
+    ys, _, _ = ref.stack_decode(x[:n], L, lambda l: hls[l].router, lambda l, e: hls[l].expert(e),
+                                lambda l: hls[l].shared(), K, boost=mask[:n], follow=follow)
+    for t in range(n):
+        parity(yh[t], ys[t], f"60-layer stack token {t}")
