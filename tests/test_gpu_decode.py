@@ -243,6 +243,38 @@ def test_stack_decode_parity(bits, phased):
                     assert prev[j] in ih[t, l]
 
 
+def test_stack_decode_beyond_lds_layer_table():
+    """300 layers: the first 256 layer-table entries are read from LDS, the rest from
+    the workspace copy in global memory; the temporal tier runs through all of them."""
+    w = small(hidden=64, inter=64, n_experts=8, top_k=2, n_layers=300, n_tokens=3, temporal_p=0.27)
+    L, T, K = w.n_layers, w.n_tokens, w.top_k
+    cfg = config_for(w)
+    dls = [DeviceLayer(w, l) for l in range(L)]
+    hls = [HostLayer(w, l) for l in range(L)]
+    x = xs(w, T)
+    mask = wl.boost_mask(w.seed + 5, T, L, K, 0.5)
+    y = torch.empty((T, w.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, L, K), dtype=torch.int32, device="cuda")
+    ws = ws_for(cfg, T, L)
+    q.moe_stack_decode(cfg, [d.weights() for d in dls], T, torch.from_numpy(x).cuda(), y, ws,
+                       boost_mask=torch.from_numpy(mask).cuda(), idx_trace=idx)
+    q.moe_device_status(ws)
+    ih = idx.cpu().numpy()
+
+    def follow(t, l, oi, gap):
+        if same_set(oi, ih[t, l]):
+            return None
+        assert gap < NEAR_TIE, f"t={t} l={l}: sets differ, gap {gap}"
+        return ih[t, l]
+
+    ys, sets, _ = ref.stack_decode(x, L, lambda l: hls[l].router, lambda l, e: hls[l].expert(e),
+                                   lambda l: hls[l].shared(), K, boost=mask, follow=follow)
+    for t in range(T):
+        for l in range(L):
+            assert same_set(sets[t, l], ih[t, l])
+        parity(y.cpu().numpy()[t], ys[t], f"300-layer stack token {t}")
+
+
 def test_stack_decode_deterministic():
     w = small(n_layers=3, n_tokens=4)
     cfg = config_for(w)
