@@ -1885,6 +1885,18 @@ __global__ void zero_words(unsigned* sync, unsigned* err, unsigned long long* xc
 
 // ------------------------------------------------------------ host side
 static int g_num_cu = -1;
+
+// Compute units a stream may dispatch to (its CU mask); 0 if the mask cannot be read.
+static int stream_units(hipStream_t stream) {
+  uint32_t mask[32] = {};
+  if (hipExtStreamGetCUMask(stream, 32, mask) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int n = 0;
+  for (uint32_t m : mask) n += __builtin_popcount(m);
+  return n;
+}
 unsigned long long* g_trace = nullptr;     // set only by instrumented builds
 unsigned long long* g_trace_wg = nullptr;  // set only by instrumented builds
 static long long g_wall_khz = -1;
@@ -2076,8 +2088,8 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
     if (e != hipSuccess) return e;
     attr_set[c.bits - 2][kv] = true;
   }
-  // every exchange slot of this call starts at epoch 0
   // every exchange slot, the selection words and the epoch-tagged previous sets
+  // start at epoch 0
   const size_t nx = (size_t)(r.wl.layers - r.wl.xbuf) / sizeof(unsigned long long);
   hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, stream, a.sync, a.err, a.xx, nx);
   e = hipGetLastError();
@@ -2107,6 +2119,17 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   if (occ < 1) {
     *why = "decode kernel does not fit on a compute unit";
     return hipErrorInvalidConfiguration;
+  }
+  // The grid is one workgroup per compute unit and a workgroup fits on a unit
+  // (checked above), so on a stream allowed to use every unit all workgroups are
+  // resident together under a plain launch, which starts about 18 us sooner than a
+  // cooperative one. A stream restricted to fewer units takes the cooperative
+  // launch, whose residency the runtime checks. If other work holds units, the
+  // remaining workgroups start as it retires; every wait is bounded, so the worst
+  // outcome is DEV_SYNC_TIMEOUT, never a hang.
+  if (stream_units(stream) >= nwg) {
+    hipLaunchKernelGGL(kern, dim3(nwg), dim3(kThreads), lds, stream, a, -1, 0, 0);
+    return hipGetLastError();
   }
   int only = -1, zero = 0;
   void* args[] = {&a, &only, &zero, &zero};
