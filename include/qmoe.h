@@ -24,7 +24,12 @@
  *    returns a message (per host thread). A failed HIP launch returns
  *    MOE_ERR_HIP with the HIP error text.
  *  - Two calls may run concurrently only on different streams with disjoint
- *    workspaces and outputs.
+ *    workspaces and outputs. The decode entry points run one persistent grid of
+ *    one workgroup per compute unit; the library orders these grids one after
+ *    another on the device, whatever the streams, so overlapping calls never
+ *    share the compute units. A grid that still cannot get every unit (other
+ *    work holding them for longer than the 2 s bound of each wait) ends with
+ *    MOE_ERR_DEVICE from moe_device_status, never a hang.
  *  - Supported shapes: hidden and inter are 64 * 2^k (64 .. 4096); group 64;
  *    bits 4, 3 or 2; 1 <= top_k <= 16, top_k <= n_experts <= 1024; n_shared 0..2.
  */

@@ -41,7 +41,10 @@
 // instruction with exact int32 accumulation. One weight element then costs about
 // one VALU operation instead of two and a half for convert + FMA, which keeps the
 // 4-bit path under the HBM roofline instead of next to it.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
+#include <mutex>
 #include <cstring>
 
 #include "qmoe_internal.h"
@@ -1897,6 +1900,49 @@ static int stream_units(hipStream_t stream) {
   for (uint32_t m : mask) n += __builtin_popcount(m);
   return n;
 }
+// Persistent launches are put in one order on the device: a launch on another
+// stream than the previous one waits for the event that launch signalled on
+// completion (a launch on the same stream is ordered by the stream). So two
+// persistent grids never hold compute units at the same time, however the
+// callers' streams overlap, and a grid launched on a stream allowed to use every
+// unit finds all of them free of this library's persistent work.
+static std::mutex g_order_mu;
+static hipEvent_t g_order_ev = nullptr;
+static hipStream_t g_order_last = nullptr;
+static bool g_order_any = false;
+
+// Launches the persistent grid in that order (plain launch when the stream may use
+// every unit, else cooperative, whose residency the runtime checks).
+static hipError_t launch_ordered(const void* kern, int nwg, size_t lds, hipStream_t stream, void** args,
+                                 bool plain) {
+  std::lock_guard<std::mutex> lock(g_order_mu);
+  hipError_t e;
+  if (!g_order_ev) {
+    e = hipEventCreate(&g_order_ev);
+    if (e != hipSuccess) {
+      g_order_ev = nullptr;
+      return e;
+    }
+  }
+  if (g_order_any && stream != g_order_last) {
+    e = hipStreamWaitEvent(stream, g_order_ev, 0);
+    if (e != hipSuccess) return e;
+  }
+  if (plain) {
+    // the dispatch itself signals the event when the grid completes
+    e = hipExtLaunchKernel(kern, dim3(nwg), dim3(kThreads), args, lds, stream, nullptr, g_order_ev, 0);
+    if (e != hipSuccess) return e;
+  } else {
+    e = hipLaunchCooperativeKernel(kern, dim3(nwg), dim3(kThreads), args, (unsigned)lds, stream);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(g_order_ev, stream);
+    if (e != hipSuccess) return e;
+  }
+  g_order_last = stream;
+  g_order_any = true;
+  return hipSuccess;
+}
+
 unsigned long long* g_trace = nullptr;     // set only by instrumented builds
 unsigned long long* g_trace_wg = nullptr;  // set only by instrumented builds
 static long long g_wall_khz = -1;
@@ -2123,18 +2169,15 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   // The grid is one workgroup per compute unit and a workgroup fits on a unit
   // (checked above), so on a stream allowed to use every unit all workgroups are
   // resident together under a plain launch, which starts about 18 us sooner than a
-  // cooperative one. A stream restricted to fewer units takes the cooperative
-  // launch, whose residency the runtime checks. If other work holds units, the
+  // cooperative one; persistent launches are ordered (launch_ordered), so no other
+  // persistent grid of this library competes for the units. A stream restricted to
+  // fewer units takes the cooperative launch. If other work holds units, the
   // remaining workgroups start as it retires; every wait is bounded, so the worst
   // outcome is DEV_SYNC_TIMEOUT, never a hang.
-  if (stream_units(stream) >= nwg) {
-    hipLaunchKernelGGL(kern, dim3(nwg), dim3(kThreads), lds, stream, a, -1, 0, 0);
-    return hipGetLastError();
-  }
   int only = -1, zero = 0;
   void* args[] = {&a, &only, &zero, &zero};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(nwg), dim3(kThreads),
-                                    args, (unsigned)lds, stream);
+  return launch_ordered(reinterpret_cast<const void*>(kern), nwg, lds, stream, args,
+                        stream_units(stream) >= nwg);
 }
 
 // ---------------------------------------------------------------------------

@@ -291,6 +291,37 @@ def test_stack_decode_deterministic():
     assert np.array_equal(outs[0], outs[1])
 
 
+def test_stack_calls_on_two_streams_overlap_safely():
+    """Two persistent stack calls enqueued back to back on two streams (own
+    workspaces and outputs) both complete and match the same calls made one after
+    the other: the library orders its persistent grids across streams."""
+    w = small(n_layers=3, n_tokens=4)
+    cfg = config_for(w)
+    dls = [DeviceLayer(w, l) for l in range(3)]
+    lw = [d.weights() for d in dls]
+    xa = torch.from_numpy(xs(w, 4)).cuda()
+    xb = torch.from_numpy(xs(w, 4, seed_shift=7)).cuda()
+    mask = torch.from_numpy(wl.boost_mask(1, 4, 3, 4)).cuda()
+    want = []
+    for x in (xa, xb):
+        ws = ws_for(cfg, 4, 3)
+        y = torch.empty_like(x)
+        q.moe_stack_decode(cfg, lw, 4, x, y, ws, boost_mask=mask)
+        q.moe_device_status(ws)
+        want.append(y.cpu().numpy())
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    wss = [ws_for(cfg, 4, 3), ws_for(cfg, 4, 3)]
+    ys = [torch.empty_like(xa), torch.empty_like(xb)]
+    for _ in range(3):
+        q.moe_stack_decode(cfg, lw, 4, xa, ys[0], wss[0], boost_mask=mask, stream=s1)
+        q.moe_stack_decode(cfg, lw, 4, xb, ys[1], wss[1], boost_mask=mask, stream=s2)
+    torch.cuda.synchronize()
+    for ws, y, ref_y in zip(wss, ys, want):
+        q.moe_device_status(ws)
+        assert np.array_equal(y.cpu().numpy(), ref_y)
+
+
 def test_zero_tokens_is_a_no_op():
     w = small()
     cfg = config_for(w)
