@@ -433,7 +433,8 @@ def test_stack_decode_full_shape_specialised(bits, gated):
 
 def test_stack60_full_workload_sampled():
     """The benchmark's workload and launch: 60 layers x 256 tokens of the 4-bit stack
-    (218 GB of experts resident), one launch. Tokens 0-1 against the oracle through
+    (218 GB of experts resident), one launch, repeated on a second stream with
+    bit-identical outputs. Tokens 0-1 against the oracle through
     all 60 layers; every token's routing checked by properties that hold at any
     size: indices in range and distinct, and every boosted expert of the temporal
     tier selected."""
@@ -447,11 +448,20 @@ def test_stack60_full_workload_sampled():
     mask = wl.boost_mask(w.seed + 7, T, L, K, w.temporal_p)
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, L, K), dtype=torch.int32, device="cuda")
-    q.moe_stack_decode(cfg, [d.weights() for d in dls], T, torch.from_numpy(x).cuda(), y, ws,
-                       boost_mask=torch.from_numpy(mask).cuda(), idx_trace=idx)
+    xd, md = torch.from_numpy(x).cuda(), torch.from_numpy(mask).cuda()
+    q.moe_stack_decode(cfg, [d.weights() for d in dls], T, xd, y, ws, boost_mask=md, idx_trace=idx)
     q.moe_device_status(ws)
     yh, ih = y.cpu().numpy(), idx.cpu().numpy()
-    del dls, ws
+    # the same launch again on another stream: bit for bit the same outputs
+    s2 = torch.cuda.Stream()
+    y2, idx2 = torch.empty_like(y), torch.empty_like(idx)
+    torch.cuda.synchronize()
+    q.moe_stack_decode(cfg, [d.weights() for d in dls], T, xd, y2, ws, boost_mask=md, idx_trace=idx2,
+                       stream=s2)
+    torch.cuda.synchronize()
+    q.moe_device_status(ws)
+    assert np.array_equal(y2.cpu().numpy(), yh) and np.array_equal(idx2.cpu().numpy(), ih)
+    del dls, ws, y2, idx2
     torch.cuda.empty_cache()  # hand the 218 GB back before the next tests
     assert np.isfinite(yh).all()
     assert ((ih >= 0) & (ih < w.n_experts)).all()
