@@ -246,7 +246,8 @@ NEAR_TIE = 1e-5
 
 
 def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=None,
-                 rmsnorm_on=True, residual=True, eps=1e-6, follow=None, tokens=None, shared_gate_of=None):
+                 rmsnorm_on=True, residual=True, eps=1e-6, follow=None, tokens=None, shared_gate_of=None,
+                 gamma_of=None):
     """Decode stack: for each token t in order, for each layer l, x <- layer(x).
     Attention is the identity between MoE blocks.
 
@@ -256,6 +257,7 @@ def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=N
     it lets a caller follow another implementation's set at a near-tie.
     tokens: subset of token indices to evaluate (teacher-forced: token t's
     boosted set then needs ``prev_sets``, supplied through ``follow`` history).
+    gamma_of(l): layer l's RMSNorm weight [H] float32, or None (all ones).
     Returns (y [T][H] float64, idx [T][L][K] sorted by expert, gaps [T][L])."""
     T = len(x_tokens)
     H = np.asarray(x_tokens[0]).size
@@ -271,15 +273,16 @@ def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=N
                 ps = np.sort(prev[l])
                 boosted = tuple(int(ps[j]) for j in range(K) if boost[t][l][j])
             sg = None if shared_gate_of is None else shared_gate_of(l)
+            gm = None if gamma_of is None else gamma_of(l)
             r = layer_decode(x, router_of(l), lambda e, l=l: expert_of(l, e), shared_of(l), K,
                              rmsnorm_on=rmsnorm_on, residual=residual, eps=eps, boosted=boosted,
-                             shared_gate=sg)
+                             shared_gate=sg, gamma=gm)
             if follow is not None:
                 f = follow(t, l, r.idx, r.gap)
                 if f is not None and set(int(v) for v in f) != set(int(v) for v in r.idx):
                     r = layer_decode(x, router_of(l), lambda e, l=l: expert_of(l, e), shared_of(l), K,
                                      rmsnorm_on=rmsnorm_on, residual=residual, eps=eps,
-                                     boosted=boosted, force_idx=f, shared_gate=sg)
+                                     boosted=boosted, force_idx=f, shared_gate=sg, gamma=gm)
             sets[t, l] = np.sort(r.idx)
             gaps[t, l] = r.gap
             x = r.y
