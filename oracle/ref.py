@@ -26,9 +26,11 @@ Pins (see tests/test_oracle_*.py): integer-exact mat-vec (scale 1, bias 0),
 the bias-only closed form, one-hot column read-out, closed-form RMSNorm,
 softmax weights summing to 1, brute-force sort for selection, one-hot routing
 against a numpy float64 dense expert, zero experts giving the identity through
-a stack, the independent pure-Python brute force on tiny shapes, and the
-bf16-free prefill reducing to the decode oracle. No function is parity
-unpinned.
+a stack, the bf16-free prefill reducing to the decode oracle, and the
+independent pure-Python brute force (``oracle/brute.py``) on tiny shapes for the
+single layer, a per-element RMSNorm weight, the multi-layer stack with the
+temporal tier (layer chaining included) and the prefill with every rounding
+point (input off the bf16 grid). No function is parity unpinned.
 """
 import ctypes
 import math
