@@ -46,7 +46,7 @@ def per_token_bytes(w, gated=False):
     """Algorithmic bytes one token reads: per layer, the packed bytes of the K routed
     and S shared experts plus the float32 router (and the float32 shared-expert gate)."""
     import quantized_expert_mat_amd as q
-    from tests.helpers import config_for
+    from workload.device_layer import config_for
     eb = q.moe_packed_expert_bytes(config_for(w))
     gate = 4 * w.n_shared * w.hidden if gated else 0
     return w.n_layers * ((w.top_k + w.n_shared) * eb + 4 * w.n_experts * w.hidden + gate)
@@ -142,7 +142,8 @@ def cpu_baseline_and_parity(w, x0_host, y_gpu, idx_gpu, n_tokens, gated=False):
     compare with the GPU's outputs of the same tokens."""
     import numpy as np
     from oracle import ref
-    from tests.helpers import NEAR_TIE, DeviceCanonicalLayer, parity, same_set
+    from workload.device_layer import DeviceCanonicalLayer
+    from oracle.compare import NEAR_TIE, parity, same_set
     import workload as wl
     hls = [DeviceCanonicalLayer(w, l) for l in range(w.n_layers)]
     boost = wl.boost_mask(w.seed + 7, w.n_tokens, w.n_layers, w.top_k, w.temporal_p or 0.0)
@@ -178,7 +179,7 @@ def prefill_bench(args, w):
     import quantized_expert_mat_amd as q
     import workload as wl
     from workload import device as wdev
-    from tests.helpers import DeviceLayer, config_for
+    from workload.device_layer import DeviceLayer, config_for
 
     T, H, K, S, E = w.n_tokens, w.hidden, w.top_k, w.n_shared, w.n_experts
     cfg = config_for(w, q.MOE_F_PREFILL_BF16 | q.MOE_F_SELECT_BY_BIAS)
@@ -235,7 +236,8 @@ def prefill_bench(args, w):
     par = None
     if not args.no_cpu:
         from oracle import ref
-        from tests.helpers import DeviceCanonicalLayer, parity
+        from workload.device_layer import DeviceCanonicalLayer
+        from oracle.compare import parity
         cl = DeviceCanonicalLayer(w, 0)
         xh, yh, wh = x.cpu().numpy(), y.cpu().numpy(), wts.cpu().numpy()
         n = min(args.cpu_tokens, T)
@@ -316,7 +318,7 @@ def stream_bench(args, w):
     import quantized_expert_mat_amd as q
     import workload as wl
     from workload import device as wdev
-    from tests.helpers import DeviceLayer, config_for
+    from workload.device_layer import DeviceLayer, config_for
 
     L, T, K, H, C = w.n_layers, w.n_tokens, w.top_k, w.hidden, args.cache_slots
     cfg = config_for(w)
@@ -470,7 +472,7 @@ def qkv_bench(args):
     cpu, par = None, None
     if not args.no_cpu:
         from oracle import ref
-        from tests.helpers import parity
+        from oracle.compare import parity
         mats, r0 = [], 0
         for r in rows:
             mats.append((codes[r0:r0 + r], sc[r0:r0 + r], bi[r0:r0 + r]))
@@ -520,7 +522,7 @@ def layer_bench(args):
     import torch
     import quantized_expert_mat_amd as q
     import workload as wl
-    from tests.helpers import DeviceLayer, config_for
+    from workload.device_layer import DeviceLayer, config_for
 
     w = wl.LAYER_H4096
     T = args.tokens or 1
@@ -553,7 +555,8 @@ def layer_bench(args):
     cpu, par = None, None
     if not args.no_cpu:
         from oracle import ref
-        from tests.helpers import DeviceCanonicalLayer, NEAR_TIE, parity, same_set
+        from workload.device_layer import DeviceCanonicalLayer
+        from oracle.compare import NEAR_TIE, parity, same_set
         cl = DeviceCanonicalLayer(w, 0)
         ih = idx.cpu().numpy()
         worst = (0.0, 0.0)
@@ -652,7 +655,7 @@ def main():
     import torch
     import quantized_expert_mat_amd as q
     from workload import device as wdev
-    from tests.helpers import DeviceLayer, config_for
+    from workload.device_layer import DeviceLayer, config_for
 
     w = wl.STACK60_3BIT if args.bits == 3 else wl.WORKLOADS[args.config]
     if args.layers or args.tokens:

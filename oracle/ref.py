@@ -249,7 +249,7 @@ NEAR_TIE = 1e-5
 
 def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=None,
                  rmsnorm_on=True, residual=True, eps=1e-6, follow=None, tokens=None, shared_gate_of=None,
-                 gamma_of=None):
+                 gamma_of=None, on_layer=None):
     """Decode stack: for each token t in order, for each layer l, x <- layer(x).
     Attention is the identity between MoE blocks.
 
@@ -260,6 +260,7 @@ def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=N
     tokens: subset of token indices to evaluate (teacher-forced: token t's
     boosted set then needs ``prev_sets``, supplied through ``follow`` history).
     gamma_of(l): layer l's RMSNorm weight [H] float32, or None (all ones).
+    on_layer(t, l, x_in, result): called after every layer (inspection only).
     Returns (y [T][H] float64, idx [T][L][K] sorted by expert, gaps [T][L])."""
     T = len(x_tokens)
     H = np.asarray(x_tokens[0]).size
@@ -287,6 +288,8 @@ def stack_decode(x_tokens, n_layers, router_of, expert_of, shared_of, K, boost=N
                                      boosted=boosted, force_idx=f, shared_gate=sg, gamma=gm)
             sets[t, l] = np.sort(r.idx)
             gaps[t, l] = r.gap
+            if on_layer is not None:
+                on_layer(t, l, x, r)
             x = r.y
         ys[t] = x
         prev = sets[t]

@@ -41,6 +41,10 @@ def lib():
         L.qgen_normal.restype = ctypes.c_int
         L.qgen_normal.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_double,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        L.qgen_zero_mean_bias.restype = ctypes.c_int
+        L.qgen_zero_mean_bias.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong,
+                                          ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -77,6 +81,17 @@ def fill_normal(keys, n, sigma, out, absolute=False):
     return kt
 
 
+def fill_zero_mean_bias(skeys, bkeys, n, sigma_scale, sigma_bias, bits, out):
+    """out: bf16-bits CUDA tensor with len(bkeys) * n elements (the zero-mean bias of gen.py)."""
+    st = _keys_tensor(skeys, out.device)
+    bt = _keys_tensor(bkeys, out.device)
+    rc = lib().qgen_zero_mean_bias(st.data_ptr(), bt.data_ptr(), len(bkeys), n, float(sigma_scale),
+                                   float(sigma_bias), int(bits), out.data_ptr(), _stream())
+    if rc != 0:
+        raise RuntimeError(f"qgen_zero_mean_bias failed: hipError {rc}")
+    return (st, bt)
+
+
 def experts_canonical(spec, seed, layer, experts, codes, scales, biases):
     """Fill canonical tensors for the listed experts: codes uint8 [n][3][H*I],
     scales/biases int16 [n][3][H*I/64] (bf16 bits)."""
@@ -85,8 +100,11 @@ def experts_canonical(spec, seed, layer, experts, codes, scales, biases):
     sk = [gen.stream_key(seed, gen.KIND_SCALE, layer, e, m) for e in experts for m in range(3)]
     bk = [gen.stream_key(seed, gen.KIND_BIAS, layer, e, m) for e in experts for m in range(3)]
     keep = [fill_codes(ck, n_el, spec.bits, codes),
-            fill_normal(sk, n_el // 64, spec.sigma_scale, scales, absolute=True),
-            fill_normal(bk, n_el // 64, spec.sigma_bias, biases)]
+            fill_normal(sk, n_el // 64, spec.sigma_scale, scales, absolute=True)]
+    if getattr(spec, "zero_mean", False):
+        keep.append(fill_zero_mean_bias(sk, bk, n_el // 64, spec.sigma_scale, spec.sigma_bias, spec.bits, biases))
+    else:
+        keep.append(fill_normal(bk, n_el // 64, spec.sigma_bias, biases))
     return keep
 
 

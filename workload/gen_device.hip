@@ -73,6 +73,24 @@ __global__ void normal_kernel(const uint64_t* keys, int nkeys, long long n, doub
   }
 }
 
+// Zero-mean bias (definition in workload/gen.py): b = -mid * s + sigma_b * n_b in
+// float64, each operation rounded once (no contraction), then float32, then bf16;
+// s is the group's bf16 scale, regenerated here from its own stream.
+__global__ void zero_mean_bias_kernel(const uint64_t* skeys, const uint64_t* bkeys, int nkeys, long long n,
+                                      double sigma_s, double sigma_b, double mid, uint16_t* out) {
+  const long long total = n * nkeys;
+  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
+       t += (long long)gridDim.x * blockDim.x) {
+    const int k = (int)(t / n);
+    const long long i = t % n;
+    const float sf = (float)(sigma_s * fabs(normal(skeys[k], (uint64_t)i)));
+    const uint16_t sb = f32_to_bf16_bits(sf);
+    const double sd = (double)__uint_as_float((uint32_t)sb << 16);
+    const double v = __dadd_rn(__dmul_rn(-mid, sd), __dmul_rn(sigma_b, normal(bkeys[k], (uint64_t)i)));
+    out[t] = f32_to_bf16_bits((float)v);
+  }
+}
+
 unsigned grid_for(long long total) {
   long long b = (total + 255) / 256;
   if (b > 65536) b = 65536;
@@ -96,6 +114,13 @@ int qgen_normal(const uint64_t* keys, int nkeys, long long n, double sigma, int 
                 void* out, void* stream) {
   hipLaunchKernelGGL(normal_kernel, dim3(grid_for(n * nkeys)), dim3(256), 0, (hipStream_t)stream, keys,
                      nkeys, n, sigma, absolute, as_bf16, out);
+  return (int)hipGetLastError();
+}
+
+int qgen_zero_mean_bias(const uint64_t* skeys, const uint64_t* bkeys, int nkeys, long long n, double sigma_s,
+                        double sigma_b, int bits, void* out, void* stream) {
+  hipLaunchKernelGGL(zero_mean_bias_kernel, dim3(grid_for(n * nkeys)), dim3(256), 0, (hipStream_t)stream, skeys,
+                     bkeys, nkeys, n, sigma_s, sigma_b, ((1 << bits) - 1) / 2.0, static_cast<uint16_t*>(out));
   return (int)hipGetLastError();
 }
 
