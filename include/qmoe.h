@@ -25,11 +25,15 @@
  *    MOE_ERR_HIP with the HIP error text.
  *  - Two calls may run concurrently only on different streams with disjoint
  *    workspaces and outputs. The decode entry points run one persistent grid of
- *    one workgroup per compute unit; the library orders these grids one after
- *    another on the device, whatever the streams, so overlapping calls never
- *    share the compute units. A grid that still cannot get every unit (other
+ *    at most one workgroup per compute unit; the library orders these grids one
+ *    after another on each device, whatever the streams, so overlapping calls
+ *    never share the compute units. A grid that still cannot get its units (other
  *    work holding them for longer than the 2 s bound of each wait) ends with
  *    MOE_ERR_DEVICE from moe_device_status, never a hang.
+ *  - State: besides its loaded code objects the library keeps, per device and
+ *    created on first use, the compute-unit count, which kernels have had their
+ *    LDS limit raised, and one HIP event that orders the persistent grids. It
+ *    holds no device memory; the event lives until the process ends.
  *  - Supported shapes: hidden and inter are 64 * 2^k (64 .. 4096); group 64;
  *    bits 4, 3 or 2; 1 <= top_k <= 16, top_k <= n_experts <= 1024; n_shared 0..2.
  */
@@ -135,7 +139,10 @@ moe_status moe_pack_weights(const moe_config* cfg, int32_t n, const uint8_t* cod
                             const uint16_t* scales, const uint16_t* biases, void* packed,
                             size_t packed_bytes, void* ws, size_t ws_bytes, void* stream);
 
-/* Routing for T tokens.
+/* Routing for T tokens: the router of "Flash-MoE - Chạy mô hình 397 tỷ tham số
+ * trên laptop" (vi.news.hada.io), section "Kiến trúc mô hình" (K of 512 experts
+ * per token, K = 4 there): logits = W_r x_n, the K experts of highest score, and
+ * their weights renormalised over the selected K.
  *   x        dev [T][H] float32 input (normalised here when MOE_F_RMSNORM is set)
  *   router_w dev [E][H] float32;  gamma dev [H] or NULL
  *   sel_bias dev [T][E] float32 or NULL: added to the logit for selection only
@@ -153,13 +160,18 @@ moe_status moe_route(const moe_config* cfg, int32_t T, const float* x, const flo
                      size_t ws_bytes, void* stream);
 
 /* One expert on T tokens: y[t] = Wd (silu(Wg x[t]) * (Wu x[t])) in float32
- * (no norm, no routing weight, no residual).
+ * (no norm, no routing weight, no residual): the dequant mat-vecs and SwiGLU of the
+ * Flash-MoE page, sections "Metal Compute Shaders" and "Kernel dequant tối ưu FMA"
+ * (w = q * scale + bias per 64-element group).
  *   packed_expert dev, one packed expert;  x dev [T][H];  y dev [T][H]. */
 moe_status moe_expert_forward(const moe_config* cfg, const void* packed_expert, int32_t T,
                               const float* x, float* y, void* ws, size_t ws_bytes,
                               void* stream);
 
-/* One MoE layer on T tokens:
+/* One MoE layer on T tokens, the per-layer step of the Flash-MoE page (section
+ * "Deferred GPU Expert Compute": routed experts, shared expert, weighted combine,
+ * residual); the batched path is the cold prefill of "LOOM" (alessandroviola.dev,
+ * 1155 tokens) as an expert-grouped GEMM:
  *   y = [x if MOE_F_RESIDUAL] + sum_k w_k * expert_{idx_k}(x_n) + sum_s shared_s(x_n),
  *   x_n = RMSNorm(x) if MOE_F_RMSNORM else x.
  * Decode path (default): float32 activations, tokens processed one after another.
@@ -174,12 +186,18 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_layer_weights* lay
                              size_t ws_bytes, void* stream);
 
 /* L-layer decode stack for T tokens, strictly in order, entirely on the device
- * (one launch unless MOE_F_PHASED). Between MoE blocks the rest of the model is
+ * (one launch unless MOE_F_PHASED): the 60-layer decode of the Flash-MoE page
+ * (section "Kiến trúc mô hình"). Between MoE blocks the rest of the model is
  * the identity, so token t enters layer 0 with x0[t] and layer l+1 receives
- * layer l's output. Temporal routing correlation: at token t > 0 and layer l,
- * slot j of token t-1's selected set at layer l (sorted by expert index) is
- * ranked in the tier above all others when boost_mask[t][l][j] != 0.
- *   layers     host [L] layer weights (copied into the workspace)
+ * layer l's output. Temporal routing correlation ("Autoresearch impulsa a
+ * Qwen3.5-397B a 20.34 tok/s en M5 Max mediante transmision SSD",
+ * openclawradar.com, section "Optimizaciones Efectivas": 27% of a token's experts
+ * repeat the previous token's): at token t > 0 and layer l, slot j of token t-1's
+ * selected set at layer l (sorted by expert index) is ranked in the tier above
+ * all others when boost_mask[t][l][j] != 0.
+ *   layers     host [L] layer weights, all validated before anything is enqueued;
+ *              the table reaches the device in kernel arguments, so the array
+ *              may be reused as soon as the call returns
  *   x0         dev [T][H];  y dev [T][H] (output of the last layer)
  *   boost_mask dev [T][L][K] uint8 or NULL
  *   idx_trace  dev [T][L][K] int32 or NULL (selected experts, key order)

@@ -105,21 +105,14 @@ moe_status layer_ptrs(const moe_config& c, const moe_layer_weights& w, int l, La
   return MOE_OK;
 }
 
-moe_status upload_layers(const moe_config& c, int L, const moe_layer_weights* layers, uint8_t* ws,
-                         const WsLayout& wl, hipStream_t st) {
-  LayerPtrs tmp[64];
-  LayerPtrs* dev = reinterpret_cast<LayerPtrs*>(ws + wl.layers);
-  for (int l0 = 0; l0 < L; l0 += 64) {
-    const int n = L - l0 < 64 ? L - l0 : 64;
-    for (int i = 0; i < n; ++i) {
-      const moe_status s = layer_ptrs(c, layers[l0 + i], l0 + i, tmp[i]);
-      if (s != MOE_OK) return s;
-    }
-    hipError_t e = hipMemcpyAsync(dev + l0, tmp, sizeof(LayerPtrs) * n, hipMemcpyHostToDevice, st);
-    if (e != hipSuccess) return hip_fail(e, "uploading the layer table");
-    // the staging array is reused by the next chunk: make the copy complete first
-    e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e, "uploading the layer table");
+// Validates every layer before anything is enqueued; the table then travels to
+// the device in kernel arguments (see launch_decode), so the call never blocks.
+moe_status validate_layers(const moe_config& c, int L, const moe_layer_weights* layers,
+                           std::vector<LayerPtrs>& out) {
+  out.resize((size_t)L);
+  for (int l = 0; l < L; ++l) {
+    const moe_status s = layer_ptrs(c, layers[l], l, out[(size_t)l]);
+    if (s != MOE_OK) return s;
   }
   return MOE_OK;
 }
@@ -200,7 +193,7 @@ moe_status moe_route(const moe_config* cfg, int32_t T, const float* x, const flo
   r.cfg = c1;
   r.L = 1;
   r.T = T;
-  r.layers_dev = nullptr;
+  r.layers_host = nullptr;
   r.x0 = x;
   r.sel_bias = sel_bias;
   r.boosted = boosted;
@@ -279,7 +272,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_layer_weights* lay
   r.cfg = *cfg;
   r.L = 1;
   r.T = T;
-  r.layers_dev = nullptr;
+  r.layers_host = nullptr;
   r.x0 = x;
   r.y = y;
   r.sel_bias = sel_bias;
@@ -310,14 +303,15 @@ moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_layer_we
   hipStream_t st = (hipStream_t)stream;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   const WsLayout wl = ws_layout(*cfg, T, L);
-  s = upload_layers(*cfg, L, layers, w8, wl, st);
+  std::vector<LayerPtrs> table;
+  s = validate_layers(*cfg, L, layers, table);
   if (s != MOE_OK) return s;
   DecodeRequest r = {};
   r.mode = 0;
   r.cfg = *cfg;
   r.L = L;
   r.T = T;
-  r.layers_dev = reinterpret_cast<const LayerPtrs*>(w8 + wl.layers);
+  r.layers_host = table.data();
   r.x0 = x0;
   r.y = y;
   r.boost_mask = boost_mask;
@@ -378,14 +372,15 @@ moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe
   hipStream_t st = (hipStream_t)stream;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   const WsLayout wl = ws_layout(*cfg, T, L);
-  s = upload_layers(*cfg, L, lw.data(), w8, wl, st);
+  std::vector<LayerPtrs> table;
+  s = validate_layers(*cfg, L, lw.data(), table);
   if (s != MOE_OK) return s;
   DecodeRequest r = {};
   r.mode = 0;
   r.cfg = *cfg;
   r.L = L;
   r.T = T;
-  r.layers_dev = reinterpret_cast<const LayerPtrs*>(w8 + wl.layers);
+  r.layers_host = table.data();
   r.x0 = x0;
   r.y = y;
   r.boost_mask = boost_mask;

@@ -16,19 +16,81 @@ __global__ void zero_u64(unsigned long long* p, size_t n) {
     p[i] = 0ull;
 }
 
-// Clears the abort flag, the error word and every exchange slot (epoch 0 never
-// matches a live epoch, which start at 1).
-__global__ void zero_words(unsigned* sync, unsigned* err, unsigned long long* xch, size_t nx) {
+// Layer-table entries carried in kernel arguments: the table reaches the device
+// in the launch itself, so a call never waits for a host-to-device copy.
+constexpr int kTableChunk = 64;
+struct TableChunk {
+  int first, n;
+  LayerPtrs p[kTableChunk];
+};
+
+// Start of a decode call: clears the abort flag, the error word and every exchange
+// slot (epoch 0 never matches a live epoch, which start at 1), and writes the
+// first chunk of the layer table.
+__global__ void prologue_kernel(unsigned* sync, unsigned* err, unsigned long long* xch, size_t nx,
+                                LayerPtrs* table, TableChunk chunk) {
   const size_t i0 = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
   if (i0 == 0) {
     sync[0] = 0u;
     err[0] = 0u;
   }
   for (size_t i = i0; i < nx; i += (size_t)gridDim.x * blockDim.x) xch[i] = 0ull;
+  if (blockIdx.x == 0 && (int)threadIdx.x < chunk.n) table[chunk.first + threadIdx.x] = chunk.p[threadIdx.x];
+}
+
+// Further chunks of the layer table (stacks of more than kTableChunk layers).
+__global__ void table_kernel(LayerPtrs* table, TableChunk chunk) {
+  if ((int)threadIdx.x < chunk.n) table[chunk.first + threadIdx.x] = chunk.p[threadIdx.x];
 }
 
 // ------------------------------------------------------------ host side
-static int g_num_cu = -1;
+// Per-device state, created on first use on a device: its compute-unit count and
+// wall-clock rate, which kernel variants have their LDS limit raised, and the
+// ordering of persistent launches. This is the library's only state beyond its
+// loaded code objects; it holds no device memory.
+constexpr int kMaxDevices = 64;
+struct DevState {
+  std::mutex mu;
+  bool ready = false;
+  int num_cu = 0;
+  long long wall_khz = 0;
+  bool lds_attr[3][4] = {};
+  // Persistent launches are put in one order on each device: a launch on another
+  // stream than the previous one waits for the event that launch signalled on
+  // completion (a launch on the same stream is ordered by the stream). So two
+  // persistent grids never hold compute units at the same time, however the
+  // callers' streams overlap, and a grid launched on a stream allowed to use every
+  // unit finds all of them free of this library's persistent work.
+  hipEvent_t order_ev = nullptr;
+  hipStream_t order_last = nullptr;
+  bool order_any = false;
+};
+static DevState g_dev[kMaxDevices];
+
+// The state of the device `stream` belongs to, initialised on first use.
+static hipError_t device_state(hipStream_t stream, DevState** out, const char** why) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *why = "device ordinal beyond the library's limit";
+    return hipErrorInvalidDevice;
+  }
+  DevState& d = g_dev[dev];
+  std::lock_guard<std::mutex> lock(d.mu);
+  if (!d.ready) {
+    int cu = 0, khz = 0;
+    e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess || khz <= 0) khz = 100000;
+    d.num_cu = cu;
+    d.wall_khz = khz;
+    d.ready = true;
+  }
+  *out = &d;
+  return hipSuccess;
+}
 
 // Compute units a stream may dispatch to (its CU mask); 0 if the mask cannot be read.
 static int stream_units(hipStream_t stream) {
@@ -41,52 +103,41 @@ static int stream_units(hipStream_t stream) {
   for (uint32_t m : mask) n += __builtin_popcount(m);
   return n;
 }
-// Persistent launches are put in one order on the device: a launch on another
-// stream than the previous one waits for the event that launch signalled on
-// completion (a launch on the same stream is ordered by the stream). So two
-// persistent grids never hold compute units at the same time, however the
-// callers' streams overlap, and a grid launched on a stream allowed to use every
-// unit finds all of them free of this library's persistent work.
-static std::mutex g_order_mu;
-static hipEvent_t g_order_ev = nullptr;
-static hipStream_t g_order_last = nullptr;
-static bool g_order_any = false;
 
 // Launches the persistent grid in that order (plain launch when the stream may use
 // every unit, else cooperative, whose residency the runtime checks).
-static hipError_t launch_ordered(const void* kern, int nwg, size_t lds, hipStream_t stream, void** args,
-                                 bool plain) {
-  std::lock_guard<std::mutex> lock(g_order_mu);
+static hipError_t launch_ordered(DevState& d, const void* kern, int nwg, size_t lds, hipStream_t stream,
+                                 void** args, bool plain) {
+  std::lock_guard<std::mutex> lock(d.mu);
   hipError_t e;
-  if (!g_order_ev) {
-    e = hipEventCreate(&g_order_ev);
+  if (!d.order_ev) {
+    e = hipEventCreate(&d.order_ev);
     if (e != hipSuccess) {
-      g_order_ev = nullptr;
+      d.order_ev = nullptr;
       return e;
     }
   }
-  if (g_order_any && stream != g_order_last) {
-    e = hipStreamWaitEvent(stream, g_order_ev, 0);
+  if (d.order_any && stream != d.order_last) {
+    e = hipStreamWaitEvent(stream, d.order_ev, 0);
     if (e != hipSuccess) return e;
   }
   if (plain) {
     // the dispatch itself signals the event when the grid completes
-    e = hipExtLaunchKernel(kern, dim3(nwg), dim3(kThreads), args, lds, stream, nullptr, g_order_ev, 0);
+    e = hipExtLaunchKernel(kern, dim3(nwg), dim3(kThreads), args, lds, stream, nullptr, d.order_ev, 0);
     if (e != hipSuccess) return e;
   } else {
     e = hipLaunchCooperativeKernel(kern, dim3(nwg), dim3(kThreads), args, (unsigned)lds, stream);
     if (e != hipSuccess) return e;
-    e = hipEventRecord(g_order_ev, stream);
+    e = hipEventRecord(d.order_ev, stream);
     if (e != hipSuccess) return e;
   }
-  g_order_last = stream;
-  g_order_any = true;
+  d.order_last = stream;
+  d.order_any = true;
   return hipSuccess;
 }
 
 unsigned long long* g_trace = nullptr;     // set only by instrumented builds
 unsigned long long* g_trace_wg = nullptr;  // set only by instrumented builds
-static long long g_wall_khz = -1;
 // Register-prefetch paths in use when a shape allows them: router rows (bit 0),
 // shared gate/up slots (bit 1), down slots (bit 2); bit 3 allows the specialised
 // kernel. Instrumented builds change it to compare the paths; the results are
@@ -94,24 +145,11 @@ static long long g_wall_khz = -1;
 int g_pre_mask = 15;  // bit 3: the specialised kernel
 int g_poll_sleep = 0;
 
-static hipError_t device_info() {
-  if (g_num_cu > 0) return hipSuccess;
-  int dev;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  int cu = 0, khz = 0;
-  e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
-  if (e != hipSuccess || khz <= 0) khz = 100000;
-  g_num_cu = cu;
-  g_wall_khz = khz;
-  return hipSuccess;
-}
-
 hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char** why) {
-  hipError_t e = device_info();
+  DevState* dsp = nullptr;
+  hipError_t e = device_state(stream, &dsp, why);
   if (e != hipSuccess) return e;
+  DevState& ds = *dsp;
   const moe_config& c = r.cfg;
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
@@ -124,7 +162,9 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.eps = c.eps;
   a.L = r.L;
   a.T = r.T;
-  a.layers = r.layers_dev;
+  uint8_t* ws = r.ws;
+  LayerPtrs* table = r.layers_host ? reinterpret_cast<LayerPtrs*>(ws + r.wl.layers) : nullptr;
+  a.layers = table;
   if (r.inline_layer) a.layer0 = r.layer0;
   a.single_expert = r.single_expert;
   a.x0 = r.x0;
@@ -135,16 +175,16 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.idx_out = r.idx_out;
   a.w_out = r.w_out;
   a.logits_out = r.logits_out;
-  uint8_t* ws = r.ws;
   a.xx = reinterpret_cast<unsigned long long*>(ws + r.wl.xbuf);
   a.lx = reinterpret_cast<unsigned long long*>(ws + r.wl.logits);
   a.hx = reinterpret_cast<unsigned long long*>(ws + r.wl.hbuf);
-  a.e_pad = (a.E + 1) & ~1;
+  a.lx_c = lx_per_lane(a.E);
+  a.e_pad = kWave * a.lx_c;
   a.sel = reinterpret_cast<int*>(ws + r.wl.sel);
   a.prev = reinterpret_cast<unsigned long long*>(ws + r.wl.prev);
   a.sync = reinterpret_cast<unsigned*>(ws + r.wl.sync);
   a.err = reinterpret_cast<unsigned*>(ws + r.wl.err);
-  a.timeout_ticks = (unsigned long long)g_wall_khz * 2000ull;  // 2 seconds per barrier wait
+  a.timeout_ticks = (unsigned long long)ds.wall_khz * 2000ull;  // 2 seconds per wait
   a.poll_sleep = g_poll_sleep;
   a.trace = g_trace;
   a.trace_wg = g_trace_wg;
@@ -184,14 +224,23 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   int maxP = 1;
   for (int i = 0; i < np; ++i) maxP = std::max(maxP, kWave / (a.pass_count[i] * Gi));
 
-  // one workgroup per compute unit; phase C rows per workgroup stay <= 64
-  const int nwg = g_num_cu;
+  // One workgroup per compute unit, and no more workgroups than there are router
+  // rows or routed gate/up items (the mode's exchange work), so that every
+  // workgroup produces some of the logits or of the routed h at every epoch: that
+  // is what keeps a slot from being rewritten before every workgroup has read it
+  // (see the exchange buffers). Phase C rows per workgroup stay <= 64: the routed
+  // items alone are at least hidden / 64 for every supported shape.
+  const int items = r.mode == MODE_ROUTE    ? a.E
+                    : r.mode == MODE_EXPERT ? a.geo.nblk_gu
+                                            : std::max(a.E, r.stream ? a.geo.nblk_gu : a.K * a.geo.nblk_gu);
+  const int nwg = std::min(ds.num_cu, items);
   if (nwg > kMaxNwg) {
     *why = "more compute units than the decode kernel supports";
     return hipErrorInvalidValue;
   }
   int rpw = (c.hidden + nwg - 1) / nwg;
   rpw = ((rpw + maxP - 1) / maxP) * maxP;
+  if (r.mode == MODE_ROUTE) rpw = std::min(rpw, 64);  // no phase C: the rows are not used
   if (rpw > 64) {
     *why = "hidden too large for the phase-C row split";
     return hipErrorInvalidValue;
@@ -218,7 +267,7 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   a.lds_xres = words; words = up4(words + rpw);
   a.n_lds_layers = r.mode == MODE_EXPERT ? 0
                    : r.inline_layer ? 1
-                   : r.layers_dev   ? std::min(r.L, kLdsLayers)
+                   : table          ? std::min(r.L, kLdsLayers)
                                     : 0;
   a.lds_layers = (words + 1) & ~1;  // 8-byte aligned
   words = up4(a.lds_layers + a.n_lds_layers * (int)(sizeof(LayerPtrs) / 4));
@@ -258,22 +307,47 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
                     (g_pre_mask & 8);
   const bool gate = spec && r.any_sgate;
   // variant: general, specialised, specialised with the shared-expert gate, streamed
-  static bool attr_set[3][4] = {};
   const int kv = r.stream ? 3 : spec ? (gate ? 2 : 1) : 0;
   const DecodeKernel kern = c.bits == 4 ? decode_kernel_b4(kv) : c.bits == 3 ? decode_kernel_b3(kv)
                                                                               : decode_kernel_b2(kv);
-  if (lds > 64 * 1024 && !attr_set[c.bits - 2][kv]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set[c.bits - 2][kv] = true;
+  {
+    std::lock_guard<std::mutex> lock(ds.mu);
+    if (lds > 64 * 1024 && !ds.lds_attr[c.bits - 2][kv]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
+      if (e != hipSuccess) return e;
+      ds.lds_attr[c.bits - 2][kv] = true;
+    }
   }
-  // every exchange slot, the selection words and the epoch-tagged previous sets
-  // start at epoch 0
+  if (!r.phased) {
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern), kThreads, lds);
+    if (e != hipSuccess) return e;
+    if (occ < 1) {
+      *why = "decode kernel does not fit on a compute unit";
+      return hipErrorInvalidConfiguration;
+    }
+  }
+  // Every check is done: from here on the call only enqueues. Every exchange slot,
+  // the selection words and the epoch-tagged previous sets start at epoch 0; the
+  // layer table travels in the clearing kernel's arguments.
   const size_t nx = (size_t)(r.wl.layers - r.wl.xbuf) / sizeof(unsigned long long);
-  hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, stream, a.sync, a.err, a.xx, nx);
+  TableChunk chunk;
+  memset(&chunk, 0, sizeof(chunk));
+  const int nt = table ? r.L : 0;
+  chunk.n = std::min(nt, kTableChunk);
+  for (int i = 0; i < chunk.n; ++i) chunk.p[i] = r.layers_host[i];
+  hipLaunchKernelGGL(prologue_kernel, dim3(256), dim3(256), 0, stream, a.sync, a.err, a.xx, nx, table, chunk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  for (int first = kTableChunk; first < nt; first += kTableChunk) {
+    chunk.first = first;
+    chunk.n = std::min(nt - first, kTableChunk);
+    for (int i = 0; i < chunk.n; ++i) chunk.p[i] = r.layers_host[first + i];
+    hipLaunchKernelGGL(table_kernel, dim3(1), dim3(kTableChunk), 0, stream, table, chunk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (r.stream) {
     // every workgroup's cache tables start empty: nothing cached by an earlier call is used
     hipLaunchKernelGGL(zero_u64, dim3(256), dim3(256), 0, stream, a.ctab, (size_t)nwg * r.L * r.cslots);
@@ -292,16 +366,8 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
         }
     return hipSuccess;
   }
-  int occ = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern),
-                                                   kThreads, lds);
-  if (e != hipSuccess) return e;
-  if (occ < 1) {
-    *why = "decode kernel does not fit on a compute unit";
-    return hipErrorInvalidConfiguration;
-  }
-  // The grid is one workgroup per compute unit and a workgroup fits on a unit
-  // (checked above), so on a stream allowed to use every unit all workgroups are
+  // The grid is at most one workgroup per compute unit and a workgroup fits on a
+  // unit (checked above), so on a stream allowed to use every unit all workgroups are
   // resident together under a plain launch, which starts about 18 us sooner than a
   // cooperative one; persistent launches are ordered (launch_ordered), so no other
   // persistent grid of this library competes for the units. A stream restricted to
@@ -310,14 +376,17 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
   // outcome is DEV_SYNC_TIMEOUT, never a hang.
   int only = -1, zero = 0;
   void* args[] = {&a, &only, &zero, &zero};
-  return launch_ordered(reinterpret_cast<const void*>(kern), nwg, lds, stream, args,
+  return launch_ordered(ds, reinterpret_cast<const void*>(kern), nwg, lds, stream, args,
                         stream_units(stream) >= nwg);
 }
 
 hipError_t launch_qkv(const moe_qkv_config& c, const uint8_t* w, const float* gamma, int T, const float* x,
                       float* q, float* k, float* v, hipStream_t stream) {
-  hipError_t e = device_info();
+  DevState* dsp = nullptr;
+  const char* why = nullptr;
+  hipError_t e = device_state(stream, &dsp, &why);
   if (e != hipSuccess) return e;
+  const int num_cu = dsp->num_cu;
   QkvArgs a;
   memset(&a, 0, sizeof(a));
   a.R = c.q_rows + c.k_rows + c.v_rows;
@@ -336,7 +405,7 @@ hipError_t launch_qkv(const moe_qkv_config& c, const uint8_t* w, const float* ga
   // two workgroups per compute unit (every unit the same load), at least one block
   // per wave: on 5120 rows of hidden 4096 this beats one block batch per wave (320
   // workgroups, some units holding two and some one) by 5% and 640 workgroups by 25%
-  const int per = std::max(kNW, (a.geo.nblk_gu + 2 * g_num_cu - 1) / (2 * g_num_cu));
+  const int per = std::max(kNW, (a.geo.nblk_gu + 2 * num_cu - 1) / (2 * num_cu));
   a.nwg = std::max(1, (a.geo.nblk_gu + per - 1) / per);
   const QkvKernel kern = c.bits == 4 ? qkv_kernel_b4() : c.bits == 3 ? qkv_kernel_b3() : qkv_kernel_b2();
   hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kThreads), 0, stream, a);

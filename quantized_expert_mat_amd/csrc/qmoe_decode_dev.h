@@ -83,7 +83,8 @@ struct DecodeArgs {
   unsigned long long* xx;        // [kRep][H] (value, epoch) pairs: next layer's input
   unsigned long long* lx;        // [kRep][E_pad] router logits
   unsigned long long* hx;        // [kRep][(K+S)*I] expert intermediates
-  int e_pad;                     // E rounded up to even
+  int e_pad;                     // pairs per replica of the logits exchange: kWave * lx_c
+  int lx_c;                      // experts per lane in top-K (lx_per_lane(E))
   int* sel;                      // [2*kMaxK]
   unsigned long long* prev;      // [2][L][kMaxK] (expert, epoch) pairs: the sorted set of the
                                  // token before, per layer (temporal tier)
@@ -710,11 +711,34 @@ __device__ inline bool wg_all(Small* sm, bool ok) {
 __device__ inline unsigned epoch_of(const DecodeArgs& a, int t, int l) {
   return (unsigned)(t * a.L + l + 1);
 }
-__device__ inline Xv xv_x(const DecodeArgs& a) { return Xv{a.xx, a.geo.H, a.geo.H}; }
-__device__ inline Xv xv_logits(const DecodeArgs& a) { return Xv{a.lx, a.E, a.e_pad}; }
-__device__ inline Xv xv_h(const DecodeArgs& a) {
+// Every exchanged vector has two buffers, used by epochs of alternating parity: a
+// producer's next write to a buffer (epoch e + 2) comes after its logits or h poll
+// of epoch e + 1, and every workgroup produces logits rows or routed h items at
+// every epoch only after it has read all of epoch e, so no slot of epoch e is
+// overwritten before every workgroup has read it (launch_decode sizes the grid so
+// that every workgroup has such rows or items).
+__device__ inline unsigned long long* xbuf_of(unsigned long long* base, int n_pad, unsigned epoch) {
+  return base + (size_t)(epoch & 1u) * kRep * n_pad;
+}
+// Position of expert e's (logit, epoch) pair in one replica of the logits
+// exchange. The top-K wave holds experts C*lane .. C*lane + C - 1 in each lane (C
+// even), so that the lowest expert index among equal scores is the first slot of
+// the lowest lane holding them; the pairs are stored as [C/2][64 lanes][2], which
+// makes each of a lane's C/2 16-byte loads coalesced across the wave.
+__device__ inline int lx_pos(int e, int C) {
+  const int lane = e / C, j = e - lane * C;
+  return ((j >> 1) * kWave + lane) * 2 + (j & 1);
+}
+
+__device__ inline Xv xv_x(const DecodeArgs& a, unsigned epoch) {
+  return Xv{xbuf_of(a.xx, a.geo.H, epoch), a.geo.H, a.geo.H};
+}
+__device__ inline Xv xv_logits(const DecodeArgs& a, unsigned epoch) {
+  return Xv{xbuf_of(a.lx, a.e_pad, epoch), a.E, a.e_pad};
+}
+__device__ inline Xv xv_h(const DecodeArgs& a, unsigned epoch) {
   const int n = (kMaxK + kMaxShared) * a.geo.I;
-  return Xv{a.hx, n, n};
+  return Xv{xbuf_of(a.hx, n, epoch), n, n};
 }
 
 // x -> LDS (normalised if requested) -> digits for the gate/up mat-vecs. The raw
@@ -725,7 +749,7 @@ __device__ __forceinline__ bool prepare_x(const DecodeArgs& a, const Lds& s, int
   const bool norm = a.mode != MODE_EXPERT && (a.flags & MOE_F_RMSNORM);
   bool ok = true;
   if (a.mode == MODE_LAYER && l > 0) {
-    ok = xget(a, xv_x(a), s.xn, epoch_of(a, t, l));
+    ok = xget(a, xv_x(a, epoch_of(a, t, l)), s.xn, epoch_of(a, t, l));
   } else {
     const float* x = a.x0 + (size_t)t * H;
     for (int i = threadIdx.x * 4; i < H; i += kThreads * 4)
@@ -778,7 +802,7 @@ __device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, 
     issue_order();
     return;
   }
-  const Xv hxv = xv_h(a);
+  const Xv hxv = xv_h(a, epoch);
   const int p = lane >> g.lGh, grp = lane & (g.Gh - 1);
   Dig D;
   load_dig(D, s.xdig, s.xsum, grp);
@@ -858,9 +882,10 @@ __device__ __forceinline__ void router_rows(const DecodeArgs& a, const Lds& s, i
     }
     acc = wave_sum(acc);
     if (lane < kRep) {
-      const unsigned long long pv = ((unsigned long long)epoch_of(a, t, l) << 32) | __float_as_uint(acc);
-      __hip_atomic_store(a.lx + (size_t)lane * a.e_pad + e, pv, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned ep = epoch_of(a, t, l);
+      const unsigned long long pv = ((unsigned long long)ep << 32) | __float_as_uint(acc);
+      __hip_atomic_store(xbuf_of(a.lx, a.e_pad, ep) + (size_t)lane * a.e_pad + lx_pos(e, a.lx_c), pv,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (lane == 0 && a.logits_out) a.logits_out[(size_t)t * E + e] = acc;
   }
@@ -970,9 +995,10 @@ __device__ __forceinline__ void router_from_regs(const DecodeArgs& a, const Lds&
     float v = 0.f;
     for (int i = 0; i < kNW; ++i) v += s.sm->redf[i][j];
     const int e = e0 + j;
-    const unsigned long long pv = ((unsigned long long)epoch_of(a, t, l) << 32) | __float_as_uint(v);
-    __hip_atomic_store(a.lx + (size_t)rep * a.e_pad + e, pv, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned ep = epoch_of(a, t, l);
+    const unsigned long long pv = ((unsigned long long)ep << 32) | __float_as_uint(v);
+    __hip_atomic_store(xbuf_of(a.lx, a.e_pad, ep) + (size_t)rep * a.e_pad + lx_pos(e, a.lx_c), pv,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (rep == 0 && a.logits_out) a.logits_out[(size_t)t * a.E + e] = v;
   }
 }
@@ -987,11 +1013,11 @@ __device__ __forceinline__ void shared_from_regs(const DecodeArgs& a, const Lds&
   split_range(a.S * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   if (i0 + w >= i1) return;
-  const Xv hxv = xv_h(a);
+  const unsigned epoch = epoch_of(a, t, l);
+  const Xv hxv = xv_h(a, epoch);
   const int p = lane >> g.lGh, grp = lane & (g.Gh - 1);
   Dig D;
   load_dig(D, s.xdig, s.xsum, grp);
-  const unsigned epoch = epoch_of(a, t, l);
 #pragma unroll
   for (int j = 0; j < kShPre; ++j) {
     const int i = i0 + w + j * kNW;
@@ -1156,14 +1182,62 @@ __device__ __forceinline__ void cache_decide(const DecodeArgs& a, const Lds& s, 
   }
 }
 
+// A uniform value moved to a vector register: comparisons against it become
+// per-lane selects instead of branches.
+__device__ inline int fj_of(int v) { return launder_v(v); }
+
+__device__ inline float ord_to_f32(unsigned u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Wave-wide maximum of an unsigned value, returned uniform.
+__device__ inline unsigned wave_max_u32(unsigned v) {
+  v = max(v, (unsigned)dpp_i<kQuad1032>((int)v));
+  v = max(v, (unsigned)dpp_i<kQuad2301>((int)v));
+  v = max(v, (unsigned)dpp_i<kRowHalfMirror>((int)v));
+  v = max(v, (unsigned)dpp_i<kRowMirror>((int)v));
+  const unsigned r0 = (unsigned)__builtin_amdgcn_readlane((int)v, 0), r1 = (unsigned)__builtin_amdgcn_readlane((int)v, 16);
+  const unsigned r2 = (unsigned)__builtin_amdgcn_readlane((int)v, 32), r3 = (unsigned)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// One selection round over the keys A (larger wins, 0 = none; at least one key is
+// non-zero): the winner is the largest key, and among equal keys the lowest
+// expert index, i.e. the lowest lane holding it and there its first slot. The
+// winner's key is cleared. Returns the expert; *key_out is its key.
+template <int kC>
+__device__ __forceinline__ int select_round(unsigned (&A)[kC], int C, int lane, unsigned* key_out, int* slot_out,
+                                            int* lane_out) {
+  unsigned m = 0;
+#pragma unroll
+  for (int j = 0; j < kC; ++j) m = max(m, A[j]);
+  const unsigned W = wave_max_u32(m);
+  const int L0 = __builtin_ctzll(__ballot(m == W));
+  int fj = 0;
+#pragma unroll
+  for (int j = kC - 1; j >= 0; --j) fj = A[j] == m ? j : fj;
+  const int slot = __builtin_amdgcn_readlane(fj, L0);
+  // clear the winner without indexing the register array by a variable: every
+  // slot keeps its key unless its bit is set in the winner lane's mask
+  const unsigned keep = ~(lane == L0 ? (1u << slot) : 0u);
+#pragma unroll
+  for (int j = 0; j < kC; ++j) A[j] &= (unsigned)((int)(keep << (31 - j)) >> 31);
+  *key_out = W;
+  *slot_out = slot;
+  *lane_out = L0;
+  return C * L0 + slot;
+}
+
 // Top-K with the temporal tier, then softmax over the selected logits. Runs on
-// wave 0 (kCh chunks of 4 logits per lane); the result is left in LDS (sel_idx,
-// sel_w, and for the streamed stack sel_slot, sel_hit).
-template <int kCh, bool STREAM = false>
+// wave 0; lane l holds experts C*l .. C*l + C - 1 (C = a.lx_c <= kC). The boosted
+// experts (the tier) are selected first, each round taking the largest remaining
+// key, then the rest. The result is left in LDS (sel_idx, sel_w, and for the
+// streamed stack sel_slot, sel_hit).
+template <int kC, bool STREAM = false>
 __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, int t, int l) {
   if (threadIdx.x >= kWave) return;
-  const int E = a.E, K = a.K, lane = threadIdx.x;
-  // boosted experts (at most K), kept in fixed registers
+  const int E = a.E, K = a.K, lane = threadIdx.x, C = a.lx_c;
+  // boosted experts (at most K), uniform across the wave
   int bst[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) bst[j] = -1;
@@ -1197,31 +1271,25 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
   }
   const bool by_bias = (a.flags & MOE_F_SELECT_BY_BIAS) != 0;
   const float* sb = a.sel_bias ? a.sel_bias + (size_t)t * E : nullptr;
-  constexpr int kPer = 4 * kCh;
-  unsigned long long key[kPer];
-  float lgv[kPer];
+  v4u raw[kC / 2];  // raw[k]: experts C*lane + 2k, C*lane + 2k + 1
   {
     // poll this workgroup's replica of the logits until they carry this epoch
     const unsigned epoch = epoch_of(a, t, l);
-    const unsigned long long* src = a.lx + (size_t)(blockIdx.x % kRep) * a.e_pad;
+    const unsigned long long* src = xbuf_of(a.lx, a.e_pad, epoch) + (size_t)(blockIdx.x % kRep) * a.e_pad;
     const __amdgpu_buffer_rsrc_t r = coh_rsrc(src, a.e_pad * 8);
-    v4u raw[2 * kCh];  // chunk c covers experts 4*(lane + 64c) .. +3 as two 16-byte halves
     const unsigned long long t0 = wall_clock64();
     for (unsigned it = 0;; ++it) {
 #pragma unroll
-      for (int c = 0; c < kCh; ++c) {
-        raw[2 * c] = ld_coh4(r, (lane + kWave * c) * 32);
-        raw[2 * c + 1] = ld_coh4(r, (lane + kWave * c) * 32 + 16);
-      }
+      for (int k = 0; k < kC / 2; ++k)
+        if (2 * k < C) raw[k] = ld_coh4(r, (k * kWave + lane) * 16);
       int good = 1;
 #pragma unroll
-      for (int c = 0; c < kCh; ++c)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = 4 * (lane + kWave * c) + q;
-          const unsigned ep = (q & 1) ? raw[2 * c + q / 2].w : raw[2 * c + q / 2].y;
-          good &= (e >= E || ep == epoch) ? 1 : 0;
+      for (int k = 0; k < kC / 2; ++k) {
+        if (2 * k < C) {
+          const int e0 = C * lane + 2 * k;
+          good &= (e0 >= E || raw[k].y == epoch) && (e0 + 1 >= E || raw[k].w == epoch) ? 1 : 0;
         }
+      }
       if (__all(good)) break;
       poll_pause(a);
       if ((it & 31u) == 31u) {
@@ -1233,84 +1301,95 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
         }
       }
     }
-    SUBSTAMP(15);
-    if (tier_prev) {
-      const unsigned pep = epoch_of(a, t - 1, l);
-      const unsigned long long t1 = wall_clock64();
-      for (unsigned it = 0;; ++it) {
-        bool good = true;
+  }
+  SUBSTAMP(15);
+  if (tier_prev) {
+    const unsigned pep = epoch_of(a, t - 1, l);
+    const unsigned long long t1 = wall_clock64();
+    for (unsigned it = 0;; ++it) {
+      bool good = true;
 #pragma unroll
-        for (int q = 0; q < kMaxK / 2; ++q)
-          good = good && (2 * q >= K || pp[q].y == pep) && (2 * q + 1 >= K || pp[q].w == pep);
-        if (good) break;
-        if ((it & 31u) == 31u) {
-          bool go = true;
-          if (lane == 0) go = poll_abort(a, t1, 1);
-          if (!__builtin_amdgcn_readlane(go ? 1 : 0, 0)) {
-            s.sm->ok = 0;
-            return;
-          }
+      for (int q = 0; q < kMaxK / 2; ++q)
+        good = good && (2 * q >= K || pp[q].y == pep) && (2 * q + 1 >= K || pp[q].w == pep);
+      if (good) break;
+      if ((it & 31u) == 31u) {
+        bool go = true;
+        if (lane == 0) go = poll_abort(a, t1, 1);
+        if (!__builtin_amdgcn_readlane(go ? 1 : 0, 0)) {
+          s.sm->ok = 0;
+          return;
         }
-#pragma unroll
-        for (int q = 0; q < kMaxK / 2; ++q)
-          if (2 * q < K) pp[q] = ld_coh4(rp, 16 * q);
       }
 #pragma unroll
-      for (int q = 0; q < kMaxK / 2; ++q) {
-        if (2 * q < K && mk[2 * q]) bst[2 * q] = (int)pp[q].x;
-        if (2 * q + 1 < K && mk[2 * q + 1]) bst[2 * q + 1] = (int)pp[q].z;
-      }
+      for (int q = 0; q < kMaxK / 2; ++q)
+        if (2 * q < K) pp[q] = ld_coh4(rp, 16 * q);
     }
 #pragma unroll
-    for (int c = 0; c < kCh; ++c) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r4 = 4 * c + q;
-        const int e = 4 * (lane + kWave * c) + q;
-        const unsigned bits = (q & 1) ? raw[2 * c + q / 2].z : raw[2 * c + q / 2].x;
-        const float lg = __uint_as_float(bits);
-        lgv[r4] = lg;
-        float sc = lg;
-        if (sb) sc = by_bias ? sb[min(e, E - 1)] : lg + sb[min(e, E - 1)];
-        unsigned tier = 0;
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) tier |= (j < K && bst[j] == e) ? 1u : 0u;
-        key[r4] = e < E ? ((unsigned long long)(tier + 1u) << 42) |
-                              ((unsigned long long)ord_f32(sc) << 10) |
-                              (unsigned long long)(kMaxE - 1 - e)
-                        : 0ull;
-      }
+    for (int q = 0; q < kMaxK / 2; ++q) {
+      if (2 * q < K && mk[2 * q]) bst[2 * q] = (int)pp[q].x;
+      if (2 * q + 1 < K && mk[2 * q + 1]) bst[2 * q + 1] = (int)pp[q].z;
     }
   }
-  // K rounds of a wave-wide argmax; winners land in lane k of isel/lsel
+  // keys: the score in an order-preserving unsigned form (a NaN ranks as -inf),
+  // 0 for slots past E; the boosted slots of this lane move to their own keys
+  unsigned key[kC], kb[kC];
+  float lgv[kC];
+  unsigned bmask = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    const int b = bst[j];
+    if (j < K && b >= 0 && b / C == lane) bmask |= 1u << (b - lane * C);
+  }
+#pragma unroll
+  for (int j = 0; j < kC; ++j) {
+    const int e = C * lane + j;
+    const unsigned bits = (j & 1) ? raw[j >> 1].z : raw[j >> 1].x;
+    const float lg = __uint_as_float(bits);
+    lgv[j] = lg;
+    float sc = lg;
+    if (sb) sc = by_bias ? sb[min(e, E - 1)] : lg + sb[min(e, E - 1)];
+    if (sc != sc) sc = -INFINITY;
+    const unsigned kk = (j < C && e < E) ? ord_f32(sc) : 0u;
+    const bool boosted = (bmask >> j) & 1u;
+    kb[j] = boosted ? kk : 0u;
+    key[j] = boosted ? 0u : kk;
+  }
+  // distinct boosted experts (every expert sits in exactly one lane and slot)
+  int nbd = __popc(bmask);
+  nbd += dpp_i<kQuad1032>(nbd);
+  nbd += dpp_i<kQuad2301>(nbd);
+  nbd += dpp_i<kRowHalfMirror>(nbd);
+  nbd += dpp_i<kRowMirror>(nbd);
+  nbd = __builtin_amdgcn_readlane(nbd, 0) + __builtin_amdgcn_readlane(nbd, 16) +
+        __builtin_amdgcn_readlane(nbd, 32) + __builtin_amdgcn_readlane(nbd, 48);
+  SUBSTAMP(6);
+  // K rounds; the winner of round k lands in lane k (my_idx, my_lg)
   int my_idx = 0;
   float my_lg = 0.f;
   for (int k = 0; k < K; ++k) {
-    unsigned long long best = 0;
-    float bl = 0.f;
+    unsigned w;
+    int slot, wl;
+    const int e = k < nbd ? select_round<kC>(kb, C, lane, &w, &slot, &wl) : select_round<kC>(key, C, lane, &w, &slot, &wl);
+    float lw;
+    if (!sb) {
+      lw = ord_to_f32(w);  // the score is the logit
+    } else {
+      float v = lgv[0];
 #pragma unroll
-    for (int r = 0; r < kPer; ++r)
-      if (key[r] > best) {
-        best = key[r];
-        bl = lgv[r];
-      }
-    const unsigned long long wbest = wave_max_u64(best);
-    const int e = kMaxE - 1 - (int)(wbest & 1023ull);
-#pragma unroll
-    for (int r = 0; r < kPer; ++r)
-      if (key[r] == wbest) key[r] = 0;
-    const float lw = readlane_f(bl, (e / 4) % kWave);  // the owner lane holds the winner's logit
+      for (int j = 1; j < kC; ++j) v = j == fj_of(slot) ? lgv[j] : v;
+      lw = readlane_f(v, wl);
+    }
     if (lane == k) {
       my_idx = e;
       my_lg = lw;
     }
   }
-  // softmax over the K selected logits (lanes 0..K-1)
+  SUBSTAMP(7);
+  // softmax over the K selected logits (lanes 0..K-1, K <= 16: the first row)
   const bool mine = lane < K;
-  float m = mine ? my_lg : -INFINITY;
-  m = wave_max(m);
-  float ex = mine ? expf(my_lg - m) : 0.f;
-  const float z = wave_sum(ex);
+  const float m = readlane_f(seg_max(mine ? my_lg : -INFINITY, 16), 0);
+  const float ex = mine ? expf(my_lg - m) : 0.f;
+  const float z = readlane_f(seg_sum(ex, 16), 0);
   const float wk = ex / z;
   if (mine) {
     s.sm->sel_idx[lane] = my_idx;
@@ -1515,8 +1594,8 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
 #pragma unroll
   for (int q = 0; q < kDnPre; ++q) dp.d[q] = ld_slot<BITS>(db[q], ds[q], false);
   issue_order();
-  const Xv hxv = xv_h(a);
   const unsigned epoch = epoch_of(a, t, l);
+  const Xv hxv = xv_h(a, epoch);
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) {
     const float pg = seg_sum(slot_dot<BITS>(G[j], D), kWave);
@@ -1547,9 +1626,9 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   if (threadIdx.x == 0) s.sm->ok = 1;
   __syncthreads();
   if constexpr (SPEC)
-    select_topk<(kSpecE + 4 * kWave - 1) / (4 * kWave)>(a, s, t, l);
+    select_topk<kSpecE / kWave>(a, s, t, l);
   else
-    select_topk<kMaxE / (4 * kWave), STREAM>(a, s, t, l);
+    select_topk<kMaxE / kWave, STREAM>(a, s, t, l);
   __syncthreads();
   if (!s.sm->ok) return false;
   SUBSTAMP(10);
@@ -1624,7 +1703,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
     // experts' h: its digits and its down pass (pass 1) are done first, while the
     // routed h is still arriving; then the routed h and pass 0. (The general
     // kernel keeps one poll: there the split measured slower.)
-    const Xv hv = xv_h(a);
+    const Xv hv = xv_h(a, epoch_of(a, t, l));
     const int K = a.K, Gi = g.Gi;
     const Xv sh{hv.base + (size_t)K * I, a.S * I, hv.n_pad};
     if (!wg_all(s.sm, xget<kSpecShHPer>(a, sh, hs + K * I, epoch_of(a, t, l)))) return false;
@@ -1639,7 +1718,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
     __syncthreads();
   } else {
     {
-      const Xv hv = xv_h(a);
+      const Xv hv = xv_h(a, epoch_of(a, t, l));
       const Xv part{hv.base, nlist * I, hv.n_pad};
       if (!wg_all(s.sm, xget(a, part, hs, epoch_of(a, t, l)))) return false;
     }
@@ -1707,10 +1786,13 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
     float v = res ? s.xres[threadIdx.x] : 0.f;
     for (int pi = 0; pi < npass; ++pi) v += s.acc[pi * rpw + (rr - r0)];
     if (expert_mode || l == a.L - 1) a.y[(size_t)t * H + rr] = v;
-    else xput(xv_x(a), rr, v, epoch_of(a, t, l + 1));
+    else xput(xv_x(a, epoch_of(a, t, l + 1)), rr, v, epoch_of(a, t, l + 1));
   }
-  // the next layer's router rows and shared slots land while x is being exchanged
+  // the next layer's router rows and shared slots land while x is being exchanged;
+  // they are requested once the x rows above are out, so that the stores the other
+  // workgroups wait for do not queue behind this workgroup's prefetch loads
   if (prefetch_static) {
+    __syncthreads();
     issue_order();
     load_static<BITS, SPEC>(a, s, l == a.L - 1 ? 0 : l + 1, sp);
     issue_order();
@@ -1765,7 +1847,8 @@ __device__ __forceinline__ void specialise(DecodeArgs& a, bool gate) {
   a.K = kSpecK;
   a.S = kSpecS;
   a.mode = MODE_LAYER;
-  a.e_pad = kSpecE;
+  a.lx_c = lx_per_lane(kSpecE);
+  a.e_pad = kWave * a.lx_c;
   a.nwg = kSpecNwg;
   a.rpw = kSpecH / kSpecNwg;
   a.exact_rows = 1;
@@ -1838,7 +1921,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
           if ((int)threadIdx.x < a.rpw && r0 + (int)threadIdx.x < a.geo.H) {
             const int r = r0 + threadIdx.x;
             s.xres[threadIdx.x] = l == 0 ? a.x0[(size_t)t * a.geo.H + r]
-                                         : __uint_as_float((unsigned)a.xx[r]);
+                                         : __uint_as_float((unsigned)xv_x(a, epoch_of(a, t, l)).base[r]);
           }
           if ((int)threadIdx.x < a.K) {
             s.sm->sel_idx[threadIdx.x] = ld_coh(a.sel + threadIdx.x);

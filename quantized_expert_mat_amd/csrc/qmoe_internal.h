@@ -128,6 +128,9 @@ struct WsLayout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Router logits per lane of the top-K wave: ceil(E / 64) rounded up to even.
+__host__ __device__ constexpr int lx_per_lane(int E) { return (((E + kWave - 1) / kWave) + 1) & ~1; }
+
 inline WsLayout ws_layout(const moe_config& c, int T, int L) {
   (void)T;
   WsLayout w;
@@ -135,10 +138,11 @@ inline WsLayout ws_layout(const moe_config& c, int T, int L) {
   w.err = o; o += 256;
   w.sync = o; o = align256(o + sizeof(unsigned) * (64 + kMaxNwg));
   w.pack_err = o; o += 256;
-  // exchanged vectors: kRep replicas of (value, epoch) pairs
-  w.xbuf = o; o = align256(o + kRep * sizeof(uint64_t) * c.hidden);
-  w.logits = o; o = align256(o + kRep * sizeof(uint64_t) * c.n_experts);
-  w.hbuf = o; o = align256(o + kRep * sizeof(uint64_t) * (size_t)(kMaxK + kMaxShared) * c.inter);
+  // exchanged vectors: two buffers (epoch parity) of kRep replicas of (value,
+  // epoch) pairs
+  w.xbuf = o; o = align256(o + 2 * kRep * sizeof(uint64_t) * c.hidden);
+  w.logits = o; o = align256(o + 2 * kRep * sizeof(uint64_t) * (size_t)kWave * lx_per_lane(c.n_experts));
+  w.hbuf = o; o = align256(o + 2 * kRep * sizeof(uint64_t) * (size_t)(kMaxK + kMaxShared) * c.inter);
   // selection words: [kMaxK] indices, [kMaxK] weights, [kMaxShared] shared-gate factors
   w.sel = o; o = align256(o + sizeof(int) * (2 * kMaxK + kMaxShared));
   w.prev = o; o = align256(o + sizeof(uint64_t) * 2 * (size_t)(L > 0 ? L : 1) * kMaxK);
@@ -154,7 +158,8 @@ struct DecodeRequest {
   int mode;  // 0 layer/stack, 1 route only, 2 single expert
   moe_config cfg;
   int L, T;
-  const LayerPtrs* layers_dev;
+  const LayerPtrs* layers_host;  // [L] validated layer table in host memory (stack calls), or NULL;
+                                 // read during the call only (it travels in kernel arguments)
   const uint8_t* single_expert;
   const float* x0;
   float* y;
@@ -173,8 +178,8 @@ struct DecodeRequest {
   uint8_t* cache;
   int cslots;
   uint8_t* hit_out;
-  // one-layer calls: the layer's pointers travel in the kernel arguments
-  // (layers_dev == NULL), so no table is copied to the device first
+  // one-layer calls: the layer's pointers travel in the decode kernel's arguments
+  // (layers_host == NULL), so no table is written to the workspace
   bool inline_layer;
   LayerPtrs layer0;
 };

@@ -92,6 +92,35 @@ def test_null_misaligned_and_small_workspace_rejected():
     assert L.moe_device_status(None, 0, None) == q.MOE_ERR_ARG
 
 
+def test_stack_validates_every_layer_before_any_device_call():
+    """moe_stack_decode checks all L layers before it enqueues anything: a bad layer
+    70 of 100 is an argument error naming that layer. On a host without a GPU any
+    enqueue would fail with MOE_ERR_HIP first, so an argument error here shows
+    that nothing was enqueued; with every layer valid the call gets as far as the
+    device (and fails there only because there is none)."""
+    L = q.lib()
+    cfg = q.Config.make(1024, 256, 64, flags=q.MOE_F_RMSNORM | q.MOE_F_RESIDUAL)
+    p = ctypes.c_void_p(1 << 20)
+    n = 100
+    big = q.moe_workspace_bytes(cfg, 2, n)
+    good = [q.LayerWeights(1 << 20, 1 << 21, 1 << 22, None) for _ in range(n)]
+    bad = list(good)
+    bad[70] = q.LayerWeights(None, 1 << 21, 1 << 22, None)
+    arr = (q.LayerWeights * n)(*bad)
+    assert L.moe_stack_decode(ctypes.byref(cfg), n, arr, 2, p, None, p, None, None, p, big, None) == q.MOE_ERR_ARG
+    assert b"layer 70" in L.moe_last_error()
+    misaligned = list(good)
+    misaligned[99] = q.LayerWeights(1 << 20, 1 << 21, (1 << 22) + 64, None)
+    arr = (q.LayerWeights * n)(*misaligned)
+    assert L.moe_stack_decode(ctypes.byref(cfg), n, arr, 2, p, None, p, None, None, p, big, None) == q.MOE_ERR_ALIGN
+    assert b"layer 99" in L.moe_last_error()
+    arr = (q.LayerWeights * n)(*good)
+    import torch
+    if not torch.cuda.is_available():
+        assert L.moe_stack_decode(ctypes.byref(cfg), n, arr, 2, p, None, p, None, None, p, big,
+                                  None) == q.MOE_ERR_HIP
+
+
 def test_binding_raises_with_message():
     cfg = q.Config.make(1024, 256, 64, bits=5)
     with pytest.raises(q.MoeError) as ei:

@@ -114,20 +114,23 @@ def test_expert_forward_integer_exact():
 
 # ------------------------------------------------------------------ routing
 
-@pytest.mark.parametrize("phased", [False, True])
-def test_route_parity(phased):
-    w = small(n_experts=100, top_k=6, hidden=1024)
+@pytest.mark.parametrize("phased,E,T", [(False, 100, 8), (True, 100, 8), (False, 7, 16), (False, 300, 12)])
+def test_route_parity(phased, E, T):
+    """Routing alone, several tokens per call, with fewer router rows than compute
+    units (7, 100) and more (300): the grid is sized so that every workgroup owns a
+    router row, and the exchange buffers alternate by epoch parity, so no
+    workgroup can find a slot already rewritten by the next token."""
+    w = small(n_experts=E, top_k=6, hidden=1024)
     cfg = config_for(w, q.MOE_F_PHASED if phased else 0)
     hl = HostLayer(w, 0)
-    T = 8
     x = xs(w, T)
     router = torch.from_numpy(hl.router).cuda()
     idx = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
     logits = torch.empty((T, w.n_experts), dtype=torch.float32, device="cuda")
     boosted = np.full((T, w.top_k), -1, np.int32)
-    boosted[2, :2] = [99, 3]
-    boosted[5, 0] = 50
+    boosted[2, :2] = [E - 1, 3]
+    boosted[5, 0] = E // 2
     ws = ws_for(cfg, T)
     q.moe_route(cfg, T, torch.from_numpy(x).cuda(), router, idx, wts, ws,
                 boosted=torch.from_numpy(boosted).cuda(), logits_out=logits)
