@@ -293,19 +293,18 @@ hipError_t launch_decode(const DecodeRequest& r, hipStream_t stream, const char*
     a.pre_shared = a.pre_shared && (g_pre_mask & 2);
     a.pre_down = a.pre_down && (g_pre_mask & 4);
   }
-  a.lds_words = words;
-  const size_t lds = (size_t)words * 4;
-  if (lds > (size_t)kMaxLdsBytes) {
-    *why = "shape needs more LDS than a workgroup has";
-    return hipErrorInvalidValue;
-  }
-
   // the specialised kernel when the call is exactly the flash-moe stack shape
   const bool spec = !r.stream && r.mode == MODE_LAYER && !r.phased && c.hidden == kSpecH && c.inter == kSpecI &&
                     a.E == kSpecE && a.K == kSpecK && a.S == kSpecS && nwg == kSpecNwg &&
                     a.pre_router && a.pre_shared && a.pre_down && a.n_lds_layers == r.L &&
                     (g_pre_mask & 8);
   const bool gate = spec && r.any_sgate;
+  a.lds_words = words;
+  const size_t lds = (size_t)words * 4;
+  if (lds > (size_t)kMaxLdsBytes) {
+    *why = "shape needs more LDS than a workgroup has";
+    return hipErrorInvalidValue;
+  }
   // variant: general, specialised, specialised with the shared-expert gate, streamed
   const int kv = r.stream ? 3 : spec ? (gate ? 2 : 1) : 0;
   const DecodeKernel kern = c.bits == 4 ? decode_kernel_b4(kv) : c.bits == 3 ? decode_kernel_b3(kv)

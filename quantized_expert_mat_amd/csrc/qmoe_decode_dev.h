@@ -490,6 +490,34 @@ __device__ inline int encode_chunk(const float v[8], float sc, unsigned out[6]) 
   return isum;
 }
 
+// One lane's chunk of 8 values (chunk dw of group gi, the 8 chunks of a group in 8
+// consecutive lanes of one wave, all active or all inactive) -> its 6 digit dwords
+// in dig[gi * kDigitStride + dw * 6 ..], and for dw == 0 the group's sums
+// sum[4 * gi + {0, 1, 2}] = 8 * sum(ints), float sum of the values, 1/scale.
+__device__ __forceinline__ void encode_chunk8(const float v[8], unsigned* dig, float* sum, int gi, int dw,
+                                              bool active) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = seg_max(m, 8);
+  float sc, xs;
+  digit_scale(m, &sc, &xs);
+  unsigned o[6];
+  int isum = encode_chunk(v, sc, o);
+  float fsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fsum += v[i];
+  if (active) {
+    uint2* dst = reinterpret_cast<uint2*>(dig + (size_t)gi * kDigitStride + dw * 6);
+    dst[0] = make_uint2(o[0], o[1]);
+    dst[1] = make_uint2(o[2], o[3]);
+    dst[2] = make_uint2(o[4], o[5]);
+  }
+  isum = seg_sum8_i(isum);  // |sum of 64 ints| <= 2^28: exact in int32
+  fsum = seg_sum(fsum, 8);
+  if (active && dw == 0) *reinterpret_cast<float4*>(sum + 4 * gi) = make_float4(8.f * (float)isum, fsum, xs, 0.f);
+}
+
 // Encode nvec vectors of length n (multiple of 64) held in LDS at src + j*n, each
 // value first multiplied by gamma[i] (if given) and then by mul, the product
 // written back when NORM_BACK. Every group of 64
@@ -532,28 +560,7 @@ __device__ __forceinline__ void encode_vectors(float* src, int nvec, int n, floa
       v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
       v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
     }
-    float m = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = seg_max(m, 8);
-    float sc, xs;
-    digit_scale(m, &sc, &xs);
-    unsigned o[6];
-    int isum = encode_chunk(v, sc, o);
-    float fsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) fsum += v[i];
-    const int g = cc / 8, dw = cc % 8;
-    if (active) {
-      uint2* dst = reinterpret_cast<uint2*>(dig + (size_t)(j * G + g) * kDigitStride + dw * 6);
-      dst[0] = make_uint2(o[0], o[1]);
-      dst[1] = make_uint2(o[2], o[3]);
-      dst[2] = make_uint2(o[4], o[5]);
-    }
-    isum = seg_sum8_i(isum);  // |sum of 64 ints| <= 2^28: exact in int32
-    fsum = seg_sum(fsum, 8);
-    if (active && dw == 0)
-      *reinterpret_cast<float4*>(sum + 4 * (j * G + g)) = make_float4(8.f * (float)isum, fsum, xs, 0.f);
+    encode_chunk8(v, dig, sum, j * G + cc / 8, cc % 8, active);
   }
 }
 
@@ -905,11 +912,20 @@ constexpr int kDnPre = 5;      // down slots per lane
 
 constexpr int kGatePre = kSpecH / (4 * kThreads);  // float4 of the shared-expert gate per thread
 
+// Column of float4 number q (0..3) of thread t's values in the specialised kernel:
+// [8t, 8t + 4), [8t + 4, 8t + 8), [H/2 + 8t, ...), [H/2 + 8t + 4, ...).
+__device__ inline int spec_col(int q) {
+  return (q >> 1) * (kSpecH / 2) + 8 * (int)threadIdx.x + 4 * (q & 1);
+}
+static_assert(kSpecH == 16 * kThreads, "16 x values per thread");
+static_assert(kRouterPre == 4 * (kSpecE / kSpecNwg), "two router rows of 4 float4 per thread");
+
 struct StaticPre {
   float4 r[kRouterPre];
   Slot g[kShPre], u[kShPre];
   float4 sg[kGatePre];  // specialised kernel with a gate: this thread's share of g_0
 };
+
 
 struct DownPre {
   Slot d[kDnPre];
@@ -922,14 +938,20 @@ __device__ __forceinline__ void load_static(const DecodeArgs& a, const Lds& s, i
   const Geo& g = a.geo;
   const LayerPtrs lp = get_layer(a, s, l);
   if constexpr (SPEC) {
+    // The specialised kernel's layout: thread t takes the columns of the x values
+    // it polls and encodes, [8t, 8t + 8) and [H/2 + 8t, H/2 + 8t + 8), of each of
+    // its workgroup's two router rows (and of the gate vector), so that phase A
+    // forms the dot products in registers.
     if (a.any_sgate) {
       // the gate vector (a layer without one re-reads router row 0, not used)
       const float* G = lp.sgate ? lp.sgate : lp.router;
 #pragma unroll
-      for (int i = 0; i < kGatePre; ++i) sp.sg[i] = ldg_f4(G + ((int)threadIdx.x + kThreads * i) * 4);
+      for (int i = 0; i < kGatePre; ++i) sp.sg[i] = ldg_f4(G + spec_col(i));
     }
-  }
-  if (a.pre_router) {
+    const float* W = lp.router + (size_t)blockIdx.x * (kSpecE / kSpecNwg) * kSpecH;
+#pragma unroll
+    for (int i = 0; i < kRouterPre; ++i) sp.r[i] = ldg_f4(W + (i >> 2) * kSpecH + spec_col(i & 3));
+  } else if (a.pre_router) {
     int e0, e1;
     split_range(a.E, a.nwg, blockIdx.x, e0, e1);
     const int nq = (e1 - e0) * (g.H / 4);
@@ -1064,6 +1086,160 @@ __device__ __forceinline__ void shared_gate_factors(const DecodeArgs& a, const L
     s.sm->sgc[threadIdx.x] = c;
     if (blockIdx.x == 0) st_coh(a.sel + 2 * kMaxK + threadIdx.x, __float_as_int(c));
   }
+}
+
+// Phase A of the specialised kernel. Thread t holds the 16 x values [8t, 8t + 8)
+// and [H/2 + 8t, H/2 + 8t + 8): polled straight into registers (layer 0: read from
+// x0), squared and summed for the RMSNorm, normalised, dotted with its columns of
+// the workgroup's two router rows (and of the shared-expert gate) and encoded into
+// digits, with two workgroup barriers in all; the chunks a thread encodes are the
+// ones encode_vectors gives it, so the digits and sums land where the general
+// path puts them. The logits are published before the digits are formed: the
+// encoding then overlaps the logits exchange (nothing reads the digits before
+// phase B), and the shared expert's gate/up items are reduced in phase B, under
+// the routed experts' loads.
+template <int BITS>
+__device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, int t, int l, const StaticPre& sp) {
+  constexpr int H = kSpecH;
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const unsigned epoch = epoch_of(a, t, l);
+  float v[16];
+  bool ok = true;
+  if (l == 0) {
+    const float* x = a.x0 + (size_t)t * H;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = ldg_f4(x + spec_col(q));
+      v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    }
+  } else {
+    // pairs chunk c = values 2c, 2c + 1; this thread's chunks are 4t .. 4t + 3 and
+    // H/4 + 4t .. H/4 + 4t + 3
+    const Xv xv = xv_x(a, epoch);
+    const __amdgpu_buffer_rsrc_t r = coh_rsrc(xv.base + (size_t)(blockIdx.x % kRep) * xv.n_pad, xv.n_pad * 8);
+    v4u raw[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) raw[k] = ld_coh4(r, ((k >> 2) * (H / 4) + 4 * tid + (k & 3)) * 16);
+    const unsigned long long t0 = wall_clock64();
+    for (unsigned it = 0;; ++it) {
+      unsigned pending = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (!(raw[k].y == epoch && raw[k].w == epoch)) pending |= 1u << k;
+      if (!pending) break;
+      if ((it & 31u) == 31u && !poll_abort(a, t0, 1)) {
+        ok = false;
+        break;
+      }
+      poll_pause(a);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (pending & (1u << k)) raw[k] = ld_coh4(r, ((k >> 2) * (H / 4) + 4 * tid + (k & 3)) * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[2 * k] = __uint_as_float(raw[k].x);
+      v[2 * k + 1] = __uint_as_float(raw[k].z);
+    }
+  }
+  // this workgroup's rows of the (pre-norm) input, for the residual in phase C
+  const int r0 = blockIdx.x * (H / kSpecNwg);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int base = h * (H / 2) + 8 * tid;
+    if (base >= r0 && base < r0 + H / kSpecNwg) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s.xres[base - r0 + i] = v[8 * h + i];
+    }
+  }
+  const bool norm = (a.flags & MOE_F_RMSNORM) != 0;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ss = fmaf(v[i], v[i], ss);
+  ss = wave_sum(ss);
+  if (lane == 0) s.sm->redf[w][0] = ss;
+  if (!ok) s.sm->ok = 0;
+  __syncthreads();
+  if (!s.sm->ok) return false;
+  SUBSTAMP(14);
+  float rinv = 1.f;
+  if (norm) {
+    ss = 0.f;
+    for (int i = 0; i < kNW; ++i) ss += s.sm->redf[i][0];
+    rinv = 1.f / sqrtf(ss / (float)H + a.eps);
+  }
+  // x_n = (x * gamma) * rinv
+  const float* gamma = get_layer(a, s, l).gamma;
+  if (gamma) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 g4 = ldg_f4(gamma + spec_col(q));
+      v[4 * q] *= g4.x; v[4 * q + 1] *= g4.y; v[4 * q + 2] *= g4.z; v[4 * q + 3] *= g4.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] *= rinv;
+  // the router rows (and gate) prefetched at the end of the previous phase C, this
+  // thread's columns
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 r0 = sp.r[q];
+    const float4 r1 = sp.r[4 + q];
+    acc0 = fmaf(r0.x, v[4 * q], acc0);
+    acc0 = fmaf(r0.y, v[4 * q + 1], acc0);
+    acc0 = fmaf(r0.z, v[4 * q + 2], acc0);
+    acc0 = fmaf(r0.w, v[4 * q + 3], acc0);
+    acc1 = fmaf(r1.x, v[4 * q], acc1);
+    acc1 = fmaf(r1.y, v[4 * q + 1], acc1);
+    acc1 = fmaf(r1.z, v[4 * q + 2], acc1);
+    acc1 = fmaf(r1.w, v[4 * q + 3], acc1);
+  }
+  acc0 = wave_sum(acc0);
+  acc1 = wave_sum(acc1);
+  if (lane == 0) {
+    s.sm->redf[w][1] = acc0;
+    s.sm->redf[w][2] = acc1;
+  }
+  if (a.any_sgate) {
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 g4 = sp.sg[q];
+      part = fmaf(g4.x, v[4 * q], part);
+      part = fmaf(g4.y, v[4 * q + 1], part);
+      part = fmaf(g4.z, v[4 * q + 2], part);
+      part = fmaf(g4.w, v[4 * q + 3], part);
+    }
+    part = wave_sum(part);
+    if (lane == 0) s.sm->sgp[w][0] = part;
+  }
+  __syncthreads();
+  SUBSTAMP(8);
+  // publish this workgroup's two logits
+  if (tid < 2 * kRep) {
+    const int j = tid / kRep, rp = tid % kRep;
+    float lg = 0.f;
+    for (int i = 0; i < kNW; ++i) lg += s.sm->redf[i][1 + j];
+    const int e = blockIdx.x * (kSpecE / kSpecNwg) + j;
+    const unsigned long long pv = ((unsigned long long)epoch << 32) | __float_as_uint(lg);
+    __hip_atomic_store(xbuf_of(a.lx, a.e_pad, epoch) + (size_t)rp * a.e_pad + lx_pos(e, a.lx_c), pv,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (rp == 0 && a.logits_out) a.logits_out[(size_t)t * a.E + e] = lg;
+  }
+  if (a.any_sgate && tid == 0) {
+    float z = 0.f;
+    for (int i = 0; i < kNW; ++i) z += s.sm->sgp[i][0];
+    s.sm->sgc[0] = get_layer(a, s, l).sgate ? 1.f / (1.f + expf(-z)) : 1.f;
+  }
+  SUBSTAMP(9);
+  // digits of the two chunks (read in phase B, after the top-K barrier)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = h * kThreads + tid;  // chunk of 8 values
+    encode_chunk8(v + 8 * h, s.xdig, s.xsum, c / 8, c % 8, true);
+  }
+  return true;
 }
 
 template <int BITS, bool SPEC = false>
@@ -1560,7 +1736,7 @@ static_assert(kSpecK * kSpecI / kSpecNwg == kNW * kBatch, "one batch per wave");
 static_assert(kSpecI % (kNW * kBatch) == 0, "a workgroup's rows lie in one expert");
 template <int BITS>
 __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds& s, int t, int l,
-                                                 DownPre& dp) {
+                                                 DownPre& dp, const StaticPre& sp) {
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int i0 = blockIdx.x * (kNW * kBatch);
@@ -1596,12 +1772,35 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
   issue_order();
   const unsigned epoch = epoch_of(a, t, l);
   const Xv hxv = xv_h(a, epoch);
+  {
+    // the shared expert's gate/up item of this wave (prefetched at the end of the
+    // previous phase C) while the routed loads are in flight
+    static_assert(kSpecS * kSpecI / kSpecNwg == kNW * kShPre, "one shared gate/up item per wave");
+    const int i = blockIdx.x * kNW + w;  // one block of one row per item in this shape
+    const float pg = seg_sum(slot_dot<BITS>(sp.g[0], D), kWave);
+    const float pu = seg_sum(slot_dot<BITS>(sp.u[0], D), kWave);
+    if (lane == 0) xput(hxv, kSpecK * g.I + i, silu(pg) * pu, epoch);
+  }
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) {
     const float pg = seg_sum(slot_dot<BITS>(G[j], D), kWave);
     const float pu = seg_sum(slot_dot<BITS>(U[j], D), kWave);
     if (lane == 0) xput(hxv, k * g.I + row[j], silu(pg) * pu, epoch);
   }
+}
+
+// Phase B of the specialised kernel: top-K on wave 0 (the ok flag is 1 here: phase
+// A's barrier checked it), then the gate/up work of the routed and shared experts.
+template <int BITS>
+__device__ __forceinline__ bool phase_b_spec(const DecodeArgs& a, const Lds& s, int t, int l, DownPre& dp,
+                                             const StaticPre& sp) {
+  select_topk<kSpecE / kWave>(a, s, t, l);
+  __syncthreads();
+  if (!s.sm->ok) return false;
+  SUBSTAMP(10);
+  if (a.trace_wg && t == 2 && threadIdx.x == 0) s.sm->twl[1] = wall_clock64();
+  gateup_down_spec<BITS>(a, s, t, l, dp, sp);
+  return true;
 }
 
 template <int BITS, bool SPEC = false, bool STREAM = false>
@@ -1634,10 +1833,7 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   SUBSTAMP(10);
   if (a.trace_wg && t == 2 && threadIdx.x == 0) s.sm->twl[1] = wall_clock64();
   if (a.mode != MODE_LAYER) return true;
-  if constexpr (SPEC) {
-    gateup_down_spec<BITS>(a, s, t, l, dp);
-    return true;
-  }
+
   if constexpr (STREAM) {
     // a workgroup owns whole gate/up blocks (all K entries of each), so a cached
     // expert's block is always read by the workgroup that copied it in
@@ -1820,10 +2016,18 @@ __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) 
       unsigned long long* twg = (a.trace_wg && t == 2 && threadIdx.x == 0)
                                     ? a.trace_wg + ((size_t)l * a.nwg + blockIdx.x) * 4
                                     : nullptr;
-      if (!phase_a<BITS, SPEC>(a, s, t, l, sp, true)) return;
+      if constexpr (SPEC) {
+        if (!phase_a_spec<BITS>(a, s, t, l, sp)) return;
+      } else {
+        if (!phase_a<BITS, SPEC>(a, s, t, l, sp, true)) return;
+      }
       if (tr) s.sm->trl[1] = wall_clock64();
       if (twg) s.sm->twl[0] = wall_clock64();
-      if (!phase_b<BITS, SPEC, STREAM>(a, s, t, l, dp, true)) return;
+      if constexpr (SPEC) {
+        if (!phase_b_spec<BITS>(a, s, t, l, dp, sp)) return;
+      } else {
+        if (!phase_b<BITS, SPEC, STREAM>(a, s, t, l, dp, true)) return;
+      }
       if (tr) s.sm->trl[3] = wall_clock64();
       if (twg) s.sm->twl[2] = wall_clock64();
       const bool more = !(t == a.T - 1 && l == a.L - 1);
@@ -1888,6 +2092,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, unsigned* lds_r
     dst->gamma = a.layer0.gamma;
     dst->sgate = a.layer0.sgate;
   }
+  if (threadIdx.x == 0) s.sm->ok = 1;
   __syncthreads();
   if constexpr (SPEC) {
     decode_chain<BITS, true>(a, s);
