@@ -962,7 +962,7 @@ __device__ __forceinline__ void load_static(const DecodeArgs& a, const Lds& s, i
       sp.r[i] = ldg_f4(W + (q < nq ? q : 0));  // unconditional: exact wait counts
     }
   }
-  if (a.pre_shared) {
+  if (a.pre_shared && !SPEC) {  // the specialised kernel loads them in phase A
     int i0, i1;
     split_range(a.S * g.nblk_gu, a.nwg, blockIdx.x, i0, i1);
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -1088,6 +1088,28 @@ __device__ __forceinline__ void shared_gate_factors(const DecodeArgs& a, const L
   }
 }
 
+// The specialised kernel's shared-expert gate/up slots (four items per workgroup):
+// loaded by waves 1..3 in phase A, which do not poll the logits (wave w takes item
+// w - 1, wave 1 also item 3), and reduced by them in phase B.
+struct SharedSpec {
+  Slot g[2], u[2];
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_shared_spec(const DecodeArgs& a, const Lds& s, int l, SharedSpec& sh) {
+  const Geo& g = a.geo;
+  const int w = (int)threadIdx.x / kWave, lane = (int)threadIdx.x % kWave;
+  const uint8_t* base = get_layer(a, s, l).shared + (size_t)blockIdx.x * kNW * g.blk;
+  const uint8_t* b0 = base + (size_t)(w - 1) * g.blk;
+  const uint8_t* b1 = base + (size_t)3 * g.blk;
+  sh.g[0] = ld_slot<BITS>(b0, lane, false);
+  sh.u[0] = ld_slot<BITS>(b0 + g.off_up, lane, false);
+  if (w == 1) {
+    sh.g[1] = ld_slot<BITS>(b1, lane, false);
+    sh.u[1] = ld_slot<BITS>(b1 + g.off_up, lane, false);
+  }
+}
+
 // Phase A of the specialised kernel. Thread t holds the 16 x values [8t, 8t + 8)
 // and [H/2 + 8t, H/2 + 8t + 8): polled straight into registers (layer 0: read from
 // x0), squared and summed for the RMSNorm, normalised, dotted with its columns of
@@ -1099,7 +1121,8 @@ __device__ __forceinline__ void shared_gate_factors(const DecodeArgs& a, const L
 // phase B), and the shared expert's gate/up items are reduced in phase B, under
 // the routed experts' loads.
 template <int BITS>
-__device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, int t, int l, const StaticPre& sp) {
+__device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, int t, int l, const StaticPre& sp,
+                                             SharedSpec& sh) {
   constexpr int H = kSpecH;
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   const unsigned epoch = epoch_of(a, t, l);
@@ -1162,6 +1185,7 @@ __device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, 
   __syncthreads();
   if (!s.sm->ok) return false;
   SUBSTAMP(14);
+  if (w > 0) load_shared_spec<BITS>(a, s, l, sh);
   float rinv = 1.f;
   if (norm) {
     ss = 0.f;
@@ -1736,7 +1760,7 @@ static_assert(kSpecK * kSpecI / kSpecNwg == kNW * kBatch, "one batch per wave");
 static_assert(kSpecI % (kNW * kBatch) == 0, "a workgroup's rows lie in one expert");
 template <int BITS>
 __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds& s, int t, int l,
-                                                 DownPre& dp, const StaticPre& sp) {
+                                                 DownPre& dp, const SharedSpec& sh) {
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int i0 = blockIdx.x * (kNW * kBatch);
@@ -1772,14 +1796,19 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
   issue_order();
   const unsigned epoch = epoch_of(a, t, l);
   const Xv hxv = xv_h(a, epoch);
-  {
-    // the shared expert's gate/up item of this wave (prefetched at the end of the
-    // previous phase C) while the routed loads are in flight
-    static_assert(kSpecS * kSpecI / kSpecNwg == kNW * kShPre, "one shared gate/up item per wave");
-    const int i = blockIdx.x * kNW + w;  // one block of one row per item in this shape
-    const float pg = seg_sum(slot_dot<BITS>(sp.g[0], D), kWave);
-    const float pu = seg_sum(slot_dot<BITS>(sp.u[0], D), kWave);
-    if (lane == 0) xput(hxv, kSpecK * g.I + i, silu(pg) * pu, epoch);
+  if (w > 0) {
+    // the shared expert's gate/up items (loaded in phase A) while the routed loads
+    // are in flight; one block of one row per item in this shape
+    static_assert(kSpecS * kSpecI / kSpecNwg == kNW, "four shared gate/up items per workgroup");
+    const int i0 = blockIdx.x * kNW;
+    float pg = seg_sum(slot_dot<BITS>(sh.g[0], D), kWave);
+    float pu = seg_sum(slot_dot<BITS>(sh.u[0], D), kWave);
+    if (lane == 0) xput(hxv, kSpecK * g.I + i0 + w - 1, silu(pg) * pu, epoch);
+    if (w == 1) {
+      pg = seg_sum(slot_dot<BITS>(sh.g[1], D), kWave);
+      pu = seg_sum(slot_dot<BITS>(sh.u[1], D), kWave);
+      if (lane == 0) xput(hxv, kSpecK * g.I + i0 + 3, silu(pg) * pu, epoch);
+    }
   }
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) {
@@ -1793,13 +1822,13 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
 // A's barrier checked it), then the gate/up work of the routed and shared experts.
 template <int BITS>
 __device__ __forceinline__ bool phase_b_spec(const DecodeArgs& a, const Lds& s, int t, int l, DownPre& dp,
-                                             const StaticPre& sp) {
+                                             const SharedSpec& sh) {
   select_topk<kSpecE / kWave>(a, s, t, l);
   __syncthreads();
   if (!s.sm->ok) return false;
   SUBSTAMP(10);
   if (a.trace_wg && t == 2 && threadIdx.x == 0) s.sm->twl[1] = wall_clock64();
-  gateup_down_spec<BITS>(a, s, t, l, dp, sp);
+  gateup_down_spec<BITS>(a, s, t, l, dp, sh);
   return true;
 }
 
@@ -2005,6 +2034,7 @@ template <int BITS, bool SPEC, bool STREAM = false>
 __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) {
   StaticPre sp;
   DownPre dp;
+  SharedSpec sh;
   load_static<BITS, SPEC>(a, s, 0, sp);
   for (int t = 0; t < a.T; ++t) {
     for (int l = 0; l < a.L; ++l) {
@@ -2017,14 +2047,14 @@ __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) 
                                     ? a.trace_wg + ((size_t)l * a.nwg + blockIdx.x) * 4
                                     : nullptr;
       if constexpr (SPEC) {
-        if (!phase_a_spec<BITS>(a, s, t, l, sp)) return;
+        if (!phase_a_spec<BITS>(a, s, t, l, sp, sh)) return;
       } else {
         if (!phase_a<BITS, SPEC>(a, s, t, l, sp, true)) return;
       }
       if (tr) s.sm->trl[1] = wall_clock64();
       if (twg) s.sm->twl[0] = wall_clock64();
       if constexpr (SPEC) {
-        if (!phase_b_spec<BITS>(a, s, t, l, dp, sp)) return;
+        if (!phase_b_spec<BITS>(a, s, t, l, dp, sh)) return;
       } else {
         if (!phase_b<BITS, SPEC, STREAM>(a, s, t, l, dp, true)) return;
       }
