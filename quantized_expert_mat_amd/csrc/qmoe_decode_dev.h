@@ -126,6 +126,10 @@ struct Small {
   float sel_w[kMaxK];
   int sel_slot[kMaxK];  // streamed stack: cache slot of each selected expert
   int sel_hit[kMaxK];   // and whether the slot already held it
+  // specialised kernel: each wave's top-K candidates (key, tier << 16 | expert, logit)
+  unsigned cand_key[kNW * kSpecK];
+  int cand_te[kNW * kSpecK];
+  float cand_lg[kNW * kSpecK];
   int ok;
   float sgc[kMaxShared];       // shared-expert gate factors of the current layer
   float sgp[kNW][kMaxShared];  // their per-wave partial dot products
@@ -1620,6 +1624,216 @@ __device__ __forceinline__ void select_topk(const DecodeArgs& a, const Lds& s, i
   }
 }
 
+// Top-K of the specialised kernel (512 experts, K = 4), on all four waves. Wave w
+// polls the logits of experts [128 w, 128 w + 128), two per lane (the specialised
+// logits exchange stores expert e at pair e), and selects its own top K in the
+// order (tier, score, lower index); the 16 candidates go through LDS, and every
+// wave merges them (a candidate's lane order is its expert order, so the lowest
+// lane among equal keys is the lowest expert). Every wave thus knows the set
+// without a second barrier and requests its gate/up slots at once; the routing
+// weights are formed afterwards (spec_weights). Lanes 0..K-1 return the selected
+// expert and its logit. Returns false if the kernel is aborting.
+__device__ __forceinline__ bool select_topk_spec(const DecodeArgs& a, const Lds& s, int t, int l, int& my_idx,
+                                                 float& my_lg) {
+  constexpr int K = kSpecK, E = kSpecE;
+  const int lane = (int)threadIdx.x % kWave, w = (int)threadIdx.x / kWave;
+  const int e0 = w * (E / kNW) + 2 * lane;  // this lane's two experts
+  // boosted experts (at most K), uniform across the workgroup
+  int bst[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) bst[j] = -1;
+  const bool tier_prev = a.boost_mask && t > 0;
+  unsigned mk[K];
+  v4u pp[K / 2];
+  const __amdgpu_buffer_rsrc_t rp = coh_rsrc(a.prev + ((size_t)((t + 1) & 1) * a.L + l) * kMaxK, kMaxK * 8);
+  if (tier_prev) {
+    const uint8_t* m = a.boost_mask + ((size_t)t * a.L + l) * K;
+#pragma unroll
+    for (int j = 0; j < K; ++j) mk[j] = m[j];
+#pragma unroll
+    for (int q = 0; q < K / 2; ++q) pp[q] = ld_coh4(rp, 16 * q);
+  } else if (a.boosted) {
+    const int* b = a.boosted + (size_t)t * K;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int e = b[j];
+      if (e >= 0 && e < E) bst[j] = e;
+      else if ((e >= E || e < -1) && threadIdx.x == 0) set_dev_err(a.err, DEV_BAD_INDEX);
+    }
+  }
+  const bool by_bias = (a.flags & MOE_F_SELECT_BY_BIAS) != 0;
+  const float* sb = a.sel_bias ? a.sel_bias + (size_t)t * E : nullptr;
+  const unsigned epoch = epoch_of(a, t, l);
+  v4u raw;
+  bool ok = true;
+  {
+    const __amdgpu_buffer_rsrc_t r =
+        coh_rsrc(xbuf_of(a.lx, a.e_pad, epoch) + (size_t)(blockIdx.x % kRep) * a.e_pad, a.e_pad * 8);
+    const unsigned long long t0 = wall_clock64();
+    for (unsigned it = 0;; ++it) {
+      raw = ld_coh4(r, e0 * 8);
+      if (__all(raw.y == epoch && raw.w == epoch)) break;
+      poll_pause(a);
+      if ((it & 31u) == 31u) {
+        bool go = true;
+        if (lane == 0) go = poll_abort(a, t0, 1);
+        if (!__builtin_amdgcn_readlane(go ? 1 : 0, 0)) {
+          ok = false;
+          break;
+        }
+      }
+    }
+  }
+  SUBSTAMP(15);
+  if (ok && tier_prev) {
+    const unsigned pep = epoch_of(a, t - 1, l);
+    const unsigned long long t1 = wall_clock64();
+    for (unsigned it = 0;; ++it) {
+      bool good = true;
+#pragma unroll
+      for (int q = 0; q < K / 2; ++q) good = good && pp[q].y == pep && pp[q].w == pep;
+      if (good) break;
+      if ((it & 31u) == 31u) {
+        bool go = true;
+        if (lane == 0) go = poll_abort(a, t1, 1);
+        if (!__builtin_amdgcn_readlane(go ? 1 : 0, 0)) {
+          ok = false;
+          break;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < K / 2; ++q) pp[q] = ld_coh4(rp, 16 * q);
+    }
+#pragma unroll
+    for (int q = 0; q < K / 2; ++q) {
+      if (mk[2 * q]) bst[2 * q] = (int)pp[q].x;
+      if (mk[2 * q + 1]) bst[2 * q + 1] = (int)pp[q].z;
+    }
+  }
+  // keys (order-preserving unsigned form of the score; a NaN ranks as -inf), the
+  // boosted experts in their own keys; the distinct boosted count (uniform)
+  const float lg0 = __uint_as_float(raw.x), lg1 = __uint_as_float(raw.z);
+  float sc0 = lg0, sc1 = lg1;
+  if (sb) {
+    sc0 = by_bias ? sb[e0] : lg0 + sb[e0];
+    sc1 = by_bias ? sb[e0 + 1] : lg1 + sb[e0 + 1];
+  }
+  if (sc0 != sc0) sc0 = -INFINITY;
+  if (sc1 != sc1) sc1 = -INFINITY;
+  bool b0 = false, b1 = false;
+  int nbd = 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int b = bst[j];
+    bool dup = false;
+#pragma unroll
+    for (int i = 0; i < j; ++i) dup = dup || bst[i] == b;
+    nbd += (b >= 0 && !dup) ? 1 : 0;
+    b0 = b0 || b == e0;
+    b1 = b1 || b == e0 + 1;
+  }
+  unsigned kb0 = b0 ? ord_f32(sc0) : 0u, kb1 = b1 ? ord_f32(sc1) : 0u;
+  unsigned kn0 = b0 ? 0u : ord_f32(sc0), kn1 = b1 ? 0u : ord_f32(sc1);
+  // this wave's boosted count, then its K local rounds: the winner lands in lane k
+  int nbw = __popcll(__ballot(b0)) + __popcll(__ballot(b1));
+  unsigned ck = 0u;
+  int cte = 0;
+  float clg = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const bool tier = k < nbw;
+    unsigned& A0 = tier ? kb0 : kn0;
+    unsigned& A1 = tier ? kb1 : kn1;
+    const unsigned m = max(A0, A1);
+    const unsigned W = wave_max_u32(m);
+    const int L0 = __builtin_ctzll(__ballot(m == W));
+    const int slot = __builtin_amdgcn_readlane(A0 == m ? 0 : 1, L0);
+    if (lane == L0) {
+      if (slot == 0) A0 = 0u;
+      else A1 = 0u;
+    }
+    const float lgw = readlane_f(slot == 0 ? lg0 : lg1, L0);
+    if (lane == k) {
+      ck = W;
+      cte = ((tier ? 1 : 0) << 16) | (w * (E / kNW) + 2 * L0 + slot);
+      clg = lgw;
+    }
+  }
+  if (lane < K) {
+    s.sm->cand_key[w * K + lane] = ck;
+    s.sm->cand_te[w * K + lane] = cte;
+    s.sm->cand_lg[w * K + lane] = clg;
+  }
+  if (!ok) s.sm->ok = 0;
+  __syncthreads();
+  if (!s.sm->ok) return false;
+  // merge the 16 candidates (lanes 0..15 of every wave): the nbd boosted ones
+  // first, then the rest
+  const bool cv = lane < kNW * K;
+  const unsigned key = cv ? s.sm->cand_key[lane] : 0u;
+  const int te = cv ? s.sm->cand_te[lane] : 0;
+  const float lgc = cv ? s.sm->cand_lg[lane] : 0.f;
+  unsigned mt = (te >> 16) ? key : 0u, mn = (te >> 16) ? 0u : key;
+  my_idx = 0;
+  my_lg = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    unsigned& A = k < nbd ? mt : mn;
+    unsigned v = A;
+    v = max(v, (unsigned)dpp_i<kQuad1032>((int)v));
+    v = max(v, (unsigned)dpp_i<kQuad2301>((int)v));
+    v = max(v, (unsigned)dpp_i<kRowHalfMirror>((int)v));
+    v = max(v, (unsigned)dpp_i<kRowMirror>((int)v));
+    const unsigned W = (unsigned)__builtin_amdgcn_readlane((int)v, 0);  // the first row's maximum
+    const int L0 = __builtin_ctzll(__ballot(A == W && cv));
+    const int e = __builtin_amdgcn_readlane(te, L0) & 0xFFFF;
+    const float lw = readlane_f(lgc, L0);
+    if (lane == L0) A = 0u;
+    if (lane == k) {
+      my_idx = e;
+      my_lg = lw;
+    }
+  }
+  return true;
+}
+
+// The routing weights of the specialised top-K (a softmax over the K selected
+// logits in lanes 0..K-1), the LDS selection every wave reads, and (workgroup 0,
+// wave 0) the outputs and the sorted set the next token's temporal tier reads.
+// Every wave writes the same selection to LDS, so no barrier is needed before a
+// wave reads it back.
+__device__ __forceinline__ void spec_weights(const DecodeArgs& a, const Lds& s, int t, int l, int my_idx, float my_lg) {
+  constexpr int K = kSpecK;
+  const int lane = (int)threadIdx.x % kWave;
+  const bool mine = lane < K;
+  const float m = readlane_f(seg_max(mine ? my_lg : -INFINITY, 16), 0);
+  const float ex = mine ? expf(my_lg - m) : 0.f;
+  const float z = readlane_f(seg_sum(ex, 16), 0);
+  const float wk = ex / z;
+  if (mine) {
+    s.sm->sel_idx[lane] = my_idx;
+    s.sm->sel_w[lane] = wk;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < kWave) {
+    if (mine) {
+      st_coh(a.sel + lane, my_idx);
+      st_coh(a.sel + kMaxK + lane, __float_as_int(wk));
+      const size_t o = ((size_t)t * a.L + l) * K;
+      if (a.idx_out) a.idx_out[o + lane] = my_idx;
+      if (a.w_out) a.w_out[o + lane] = wk;
+    }
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int other = __builtin_amdgcn_readlane(my_idx, j);
+      rank += (j != lane && other < my_idx) ? 1 : 0;
+    }
+    unsigned long long* ps = a.prev + ((size_t)(t & 1) * a.L + l) * kMaxK;
+    const unsigned long long pv = ((unsigned long long)epoch_of(a, t, l) << 32) | (unsigned)my_idx;
+    if (mine) __hip_atomic_store(ps + rank, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // The expert-list entry li of phase C: its packed expert and routing weight.
 // Streamed stack: routed entry k is read from its cache slot when the slot already
 // holds it, else from host memory, and then wb names the slot it is copied into.
@@ -1753,19 +1967,22 @@ __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s
 // Phase B of the specialised kernel (hidden 4096, inter 1024, K 4, 256 workgroups):
 // a workgroup owns kNW*kBatch consecutive gate/up rows of one routed expert, so
 // each wave has exactly one batch. Every address (gate/up rows and the phase-C down
-// slots) is formed from LDS first; then all loads go out in one straight run, with
-// no branch or LDS read between them that would make the compiler wait for the
-// loads already issued.
+// slots) is formed from LDS first; the gate/up loads go out in one straight run,
+// with no branch or LDS read between them that would make the compiler wait for
+// the loads already issued. The down slots are requested after the gate/up dot
+// products: phase B then moves only the gate/up bytes, and the down slots land
+// while h is being exchanged (measured 2% faster than requesting them with the
+// gate/up slots).
 static_assert(kSpecK * kSpecI / kSpecNwg == kNW * kBatch, "one batch per wave");
 static_assert(kSpecI % (kNW * kBatch) == 0, "a workgroup's rows lie in one expert");
 template <int BITS>
 __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds& s, int t, int l,
-                                                 DownPre& dp, const SharedSpec& sh) {
+                                                 DownPre& dp, const SharedSpec& sh, int my_idx, float my_lg) {
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int i0 = blockIdx.x * (kNW * kBatch);
   const int k = i0 >> g.lnb;  // the routed expert (list entry) of every row here
-  const uint8_t* ex = get_layer(a, s, l).experts + (size_t)s.sm->sel_idx[k] * g.expert_bytes;
+  const uint8_t* ex = get_layer(a, s, l).experts + (size_t)__builtin_amdgcn_readlane(my_idx, k) * g.expert_bytes;
   const uint8_t* gb[kBatch];
   int row[kBatch];
 #pragma unroll
@@ -1773,14 +1990,6 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
     const int b = (i0 + w + j * kNW) & (g.nblk_gu - 1);
     gb[j] = ex + (size_t)b * g.blk;
     row[j] = b;  // one row per block in this shape
-  }
-  const uint8_t* db[kDnPre];
-  int ds[kDnPre];
-#pragma unroll
-  for (int q = 0; q < kDnPre; ++q) {
-    const DnJob j = down_job(a, s, l, q);
-    db[q] = j.on ? j.blk : ex;
-    ds[q] = j.on ? j.slot : 0;
   }
   Dig D;
   load_dig(D, s.xdig, s.xsum, lane);
@@ -1791,9 +2000,10 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
     G[j] = ld_slot<BITS>(gb[j], lane, false);
     U[j] = ld_slot<BITS>(gb[j] + g.off_up, lane, false);
   }
-#pragma unroll
-  for (int q = 0; q < kDnPre; ++q) dp.d[q] = ld_slot<BITS>(db[q], ds[q], false);
   issue_order();
+  // the routing weights and the LDS selection (read by the down jobs below and in
+  // phase C) while the gate/up loads are in flight
+  spec_weights(a, s, t, l, my_idx, my_lg);
   const unsigned epoch = epoch_of(a, t, l);
   const Xv hxv = xv_h(a, epoch);
   if (w > 0) {
@@ -1815,7 +2025,18 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
     const float pg = seg_sum(slot_dot<BITS>(G[j], D), kWave);
     const float pu = seg_sum(slot_dot<BITS>(U[j], D), kWave);
     if (lane == 0) xput(hxv, k * g.I + row[j], silu(pg) * pu, epoch);
+  }  const uint8_t* db[kDnPre];
+  int ds[kDnPre];
+#pragma unroll
+  for (int q = 0; q < kDnPre; ++q) {
+    const DnJob j = down_job(a, s, l, q);
+    db[q] = j.on ? j.blk : ex;
+    ds[q] = j.on ? j.slot : 0;
   }
+  issue_order();
+#pragma unroll
+  for (int q = 0; q < kDnPre; ++q) dp.d[q] = ld_slot<BITS>(db[q], ds[q], false);
+  issue_order();
 }
 
 // Phase B of the specialised kernel: top-K on wave 0 (the ok flag is 1 here: phase
@@ -1823,12 +2044,12 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
 template <int BITS>
 __device__ __forceinline__ bool phase_b_spec(const DecodeArgs& a, const Lds& s, int t, int l, DownPre& dp,
                                              const SharedSpec& sh) {
-  select_topk<kSpecE / kWave>(a, s, t, l);
-  __syncthreads();
-  if (!s.sm->ok) return false;
+  int my_idx;
+  float my_lg;
+  if (!select_topk_spec(a, s, t, l, my_idx, my_lg)) return false;
   SUBSTAMP(10);
   if (a.trace_wg && t == 2 && threadIdx.x == 0) s.sm->twl[1] = wall_clock64();
-  gateup_down_spec<BITS>(a, s, t, l, dp, sh);
+  gateup_down_spec<BITS>(a, s, t, l, dp, sh, my_idx, my_lg);
   return true;
 }
 
@@ -2081,8 +2302,10 @@ __device__ __forceinline__ void specialise(DecodeArgs& a, bool gate) {
   a.K = kSpecK;
   a.S = kSpecS;
   a.mode = MODE_LAYER;
-  a.lx_c = lx_per_lane(kSpecE);
-  a.e_pad = kWave * a.lx_c;
+  // the specialised logits exchange: expert e at pair e (lx_pos with C = 2 is the
+  // identity); the replica holds all 512 pairs
+  a.lx_c = 2;
+  a.e_pad = kSpecE;
   a.nwg = kSpecNwg;
   a.rpw = kSpecH / kSpecNwg;
   a.exact_rows = 1;
