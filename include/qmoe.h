@@ -15,7 +15,9 @@
  *  - Pointers marked "dev" are device pointers; "host" pointers are host memory.
  *    The caller owns every buffer. The library never allocates or frees device
  *    memory; scratch space is the caller's workspace `ws`, sized by
- *    moe_workspace_bytes(). Workspace contents need no initialisation.
+ *    moe_workspace_bytes(), except for moe_stack_decode_noalloc, which uses a
+ *    fixed 4 MiB array of the library's code object on each device. Workspace
+ *    contents need no initialisation.
  *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
  *    enqueues work on that stream and returns; nothing blocks except
  *    moe_device_status().
@@ -32,8 +34,9 @@
  *    MOE_ERR_DEVICE from moe_device_status, never a hang.
  *  - State: besides its loaded code objects the library keeps, per device and
  *    created on first use, the compute-unit count, which kernels have had their
- *    LDS limit raised, and one HIP event that orders the persistent grids. It
- *    holds no device memory; the event lives until the process ends.
+ *    LDS limit raised, one HIP event that orders the persistent grids, and the
+ *    address of the scratch array of moe_stack_decode_noalloc. The event lives
+ *    until the process ends.
  *  - Supported shapes: hidden and inter are 64 * 2^k (64 .. 4096); group 64;
  *    bits 4, 3 or 2; 1 <= top_k <= 16, top_k <= n_experts <= 1024; n_shared 0..2.
  */
@@ -239,6 +242,30 @@ moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe
                                      int32_t* idx_trace, float* w_trace, uint8_t* hit_trace, void* cache,
                                      size_t cache_bytes, int32_t cache_slots, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* moe_stack_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation). Its scratch space is a fixed 4 MiB array inside the
+ * library, one per device, obtained once per device with hipGetSymbolAddress on
+ * the first call there and held until the process ends; the call itself
+ * allocates nothing, host or device. Same kernels, same results as
+ * moe_stack_decode on the same inputs.
+ *   limits     L <= 128, and the shape's workspace without the streamed tier's
+ *              tables must fit 4 MiB (hidden 4096, inter 1024, any K and E of
+ *              the supported range: about 3 MiB); otherwise MOE_ERR_UNSUPPORTED
+ *              or MOE_ERR_WORKSPACE, before anything is enqueued.
+ *   dev_err    dev uint32 or NULL: after the stack, receives this call's device
+ *              error word (0 none, 1 expert index out of range, 2 a wait timed
+ *              out), copied on `stream`; moe_device_status cannot reach the array.
+ *              Not written when T = 0 (nothing is enqueued).
+ * Every call on a device shares that device's array and leaves its contents
+ * behind; each call clears what must start at zero itself. Two calls on one
+ * device that may overlap (different streams without ordering between them)
+ * race on the array: give them one stream. Other arguments as in
+ * moe_stack_decode. */
+moe_status moe_stack_decode_noalloc(const moe_config* cfg, int32_t L, const moe_layer_weights* layers,
+                                    int32_t T, const float* x0, const uint8_t* boost_mask, float* y,
+                                    int32_t* idx_trace, float* w_trace, uint32_t* dev_err, void* stream);
 
 /* Bytes of the packed fused Q/K/V matrix (Rq + Rk + Rv rows of H columns, the
  * block layout of an expert's gate matrix). 0 if the config is invalid. */

@@ -18,6 +18,7 @@ MOE_F_PREFILL_BF16, MOE_F_PHASED = 8, 16
 
 EXPORTS = ["moe_packed_expert_bytes", "moe_workspace_bytes", "moe_pack_weights", "moe_route",
            "moe_expert_forward", "moe_layer_forward", "moe_stack_decode", "moe_stack_decode_streamed",
+           "moe_stack_decode_noalloc",
            "moe_qkv_packed_bytes", "moe_qkv_pack", "moe_qkv_forward", "moe_last_error", "moe_device_status"]
 
 
@@ -82,6 +83,8 @@ def lib():
         L.moe_layer_forward.argtypes = [C, ctypes.POINTER(LayerWeights), i32, P, P, P, P, P, P, P, sz, P]
         L.moe_stack_decode.restype = st
         L.moe_stack_decode.argtypes = [C, i32, ctypes.POINTER(LayerWeights), i32, P, P, P, P, P, P, sz, P]
+        L.moe_stack_decode_noalloc.restype = st
+        L.moe_stack_decode_noalloc.argtypes = [C, i32, ctypes.POINTER(LayerWeights), i32, P, P, P, P, P, P, P]
         L.moe_stack_decode_streamed.restype = st
         L.moe_stack_decode_streamed.argtypes = [C, i32, ctypes.POINTER(LayerWeights), i32, P, P, P, P, P, P,
                                                 P, sz, i32, P, sz, P]
@@ -166,6 +169,15 @@ def moe_stack_decode(cfg, layers, T, x0, y, ws, boost_mask=None, idx_trace=None,
     return _check(lib().moe_stack_decode(ctypes.byref(cfg), len(layers), arr, T, _ptr(x0), _ptr(boost_mask),
                                          _ptr(y), _ptr(idx_trace), _ptr(w_trace), _ptr(ws),
                                          ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_stack_decode_noalloc(cfg, layers, T, x0, y, boost_mask=None, idx_trace=None, w_trace=None,
+                             dev_err=None, stream=None):
+    """moe_stack_decode on the library's fixed scratch array (no workspace)."""
+    arr = (LayerWeights * len(layers))(*layers)
+    return _check(lib().moe_stack_decode_noalloc(ctypes.byref(cfg), len(layers), arr, T, _ptr(x0),
+                                                 _ptr(boost_mask), _ptr(y), _ptr(idx_trace), _ptr(w_trace),
+                                                 _ptr(dev_err), _stream(stream)))
 
 
 def moe_stack_decode_streamed(cfg, layers, T, x0, y, ws, cache, cache_slots, boost_mask=None, idx_trace=None,

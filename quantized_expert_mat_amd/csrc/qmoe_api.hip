@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include <vector>
@@ -18,6 +19,14 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
 }  // namespace qmoe
 
 using namespace qmoe;
+
+// The workspace of moe_stack_decode_noalloc: one fixed array per device, held
+// until the process ends. In host code `scratch` names a host-side stand-in, not
+// device memory: host code uses only the address hipGetSymbolAddress returns for
+// it (looked up once per device, see scratch_of).
+constexpr size_t kScratchBytes = size_t(4) << 20;
+constexpr int kScratchMaxLayers = 128;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -105,24 +114,88 @@ moe_status layer_ptrs(const moe_config& c, const moe_layer_weights& w, int l, La
   return MOE_OK;
 }
 
-// Validates every layer before anything is enqueued; the table then travels to
-// the device in kernel arguments (see launch_decode), so the call never blocks.
-moe_status validate_layers(const moe_config& c, int L, const moe_layer_weights* layers,
-                           std::vector<LayerPtrs>& out) {
-  out.resize((size_t)L);
-  for (int l = 0; l < L; ++l) {
-    const moe_status s = layer_ptrs(c, layers[l], l, out[(size_t)l]);
-    if (s != MOE_OK) return s;
-  }
-  return MOE_OK;
-}
-
 moe_status run_decode(DecodeRequest& r, hipStream_t st) {
   const char* why = nullptr;
   hipError_t e = launch_decode(r, st, &why);
   if (why) return fail(MOE_ERR_UNSUPPORTED, "%s", why);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return MOE_OK;
+}
+
+// Validates every layer before anything is enqueued; the table then travels to
+// the device in kernel arguments (see launch_decode), so the call never blocks.
+moe_status validate_layers(const moe_config& c, int L, const moe_layer_weights* layers, LayerPtrs* out) {
+  for (int l = 0; l < L; ++l) {
+    const moe_status s = layer_ptrs(c, layers[l], l, out[l]);
+    if (s != MOE_OK) return s;
+  }
+  return MOE_OK;
+}
+
+// Device address of this device's `scratch` array: hipGetSymbolAddress once per
+// device, with that device current, then kept for the life of the process.
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[64] = {};
+
+moe_status scratch_of(hipStream_t st, uint8_t*& out) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  REQUIRE(dev >= 0 && dev < 64, MOE_ERR_UNSUPPORTED, "device %d: at most 64 devices", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (back != hipSuccess) return hip_fail(back, "hipSetDevice");
+    REQUIRE(p && aligned(p, 256), MOE_ERR_HIP, "scratch array at %p is not 256-byte aligned", p);
+    g_scratch[dev] = static_cast<uint8_t*>(p);
+  }
+  out = g_scratch[dev];
+  return MOE_OK;
+}
+
+// Checks shared by both resident-stack entry points (before any workspace check).
+moe_status check_stack(const moe_config* cfg, int L, int T, const moe_layer_weights* layers, const float* x0,
+                       const float* y) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  REQUIRE(L >= 1 && T >= 0, MOE_ERR_ARG, "L=%d T=%d", L, T);
+  REQUIRE(!(cfg->flags & (MOE_F_PREFILL_BF16 | MOE_F_SELECT_BY_BIAS)), MOE_ERR_ARG,
+          "stack decode takes neither MOE_F_PREFILL_BF16 nor MOE_F_SELECT_BY_BIAS");
+  if (T == 0) return MOE_OK;
+  REQUIRE(layers && x0 && y, MOE_ERR_ARG, "NULL pointer");
+  REQUIRE(aligned(x0, 16) && aligned(y, 16), MOE_ERR_ALIGN, "x0/y must be 16-byte aligned");
+  return MOE_OK;
+}
+
+// Enqueues the resident stack on a validated layer table and a workspace of
+// layout wl.
+moe_status run_stack(const moe_config* cfg, int L, const moe_layer_weights* layers, const LayerPtrs* table,
+                     int T, const float* x0, const uint8_t* boost_mask, float* y, int32_t* idx_trace,
+                     float* w_trace, uint8_t* ws, const WsLayout& wl, hipStream_t st) {
+  DecodeRequest r = {};
+  r.mode = 0;
+  r.cfg = *cfg;
+  r.L = L;
+  r.T = T;
+  r.layers_host = table;
+  r.x0 = x0;
+  r.y = y;
+  r.boost_mask = boost_mask;
+  r.idx_out = idx_trace;
+  r.w_out = w_trace;
+  r.ws = ws;
+  r.wl = wl;
+  r.phased = (cfg->flags & MOE_F_PHASED) != 0;
+  r.any_sgate = false;
+  for (int l = 0; l < L; ++l) r.any_sgate = r.any_sgate || (cfg->n_shared > 0 && layers[l].shared_gate);
+  return run_decode(r, st);
 }
 
 }  // namespace
@@ -290,39 +363,15 @@ moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_layer_we
                             int32_t T, const float* x0, const uint8_t* boost_mask, float* y,
                             int32_t* idx_trace, float* w_trace, void* ws, size_t ws_bytes,
                             void* stream) {
-  moe_status s = check_config(cfg);
-  if (s != MOE_OK) return s;
-  REQUIRE(L >= 1 && T >= 0, MOE_ERR_ARG, "L=%d T=%d", L, T);
-  if (T == 0) return MOE_OK;
-  REQUIRE(!(cfg->flags & (MOE_F_PREFILL_BF16 | MOE_F_SELECT_BY_BIAS)), MOE_ERR_ARG,
-          "stack decode takes neither MOE_F_PREFILL_BF16 nor MOE_F_SELECT_BY_BIAS");
-  REQUIRE(layers && x0 && y, MOE_ERR_ARG, "NULL pointer");
-  REQUIRE(aligned(x0, 16) && aligned(y, 16), MOE_ERR_ALIGN, "x0/y must be 16-byte aligned");
+  moe_status s = check_stack(cfg, L, T, layers, x0, y);
+  if (s != MOE_OK || T == 0) return s;
   s = check_ws(cfg, T, L, ws, ws_bytes);
   if (s != MOE_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
-  uint8_t* w8 = static_cast<uint8_t*>(ws);
-  const WsLayout wl = ws_layout(*cfg, T, L);
-  std::vector<LayerPtrs> table;
-  s = validate_layers(*cfg, L, layers, table);
+  std::vector<LayerPtrs> table((size_t)L);
+  s = validate_layers(*cfg, L, layers, table.data());
   if (s != MOE_OK) return s;
-  DecodeRequest r = {};
-  r.mode = 0;
-  r.cfg = *cfg;
-  r.L = L;
-  r.T = T;
-  r.layers_host = table.data();
-  r.x0 = x0;
-  r.y = y;
-  r.boost_mask = boost_mask;
-  r.idx_out = idx_trace;
-  r.w_out = w_trace;
-  r.ws = w8;
-  r.wl = wl;
-  r.phased = (cfg->flags & MOE_F_PHASED) != 0;
-  r.any_sgate = false;
-  for (int l = 0; l < L; ++l) r.any_sgate = r.any_sgate || (cfg->n_shared > 0 && layers[l].shared_gate);
-  return run_decode(r, st);
+  return run_stack(cfg, L, layers, table.data(), T, x0, boost_mask, y, idx_trace, w_trace,
+                   static_cast<uint8_t*>(ws), ws_layout(*cfg, T, L), (hipStream_t)stream);
 }
 
 moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe_layer_weights* layers,
@@ -372,8 +421,8 @@ moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe
   hipStream_t st = (hipStream_t)stream;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   const WsLayout wl = ws_layout(*cfg, T, L);
-  std::vector<LayerPtrs> table;
-  s = validate_layers(*cfg, L, lw.data(), table);
+  std::vector<LayerPtrs> table((size_t)L);
+  s = validate_layers(*cfg, L, lw.data(), table.data());
   if (s != MOE_OK) return s;
   DecodeRequest r = {};
   r.mode = 0;
@@ -396,6 +445,33 @@ moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe
   r.cslots = cache_slots;
   r.hit_out = hit_trace;
   return run_decode(r, st);
+}
+
+moe_status moe_stack_decode_noalloc(const moe_config* cfg, int32_t L, const moe_layer_weights* layers,
+                                    int32_t T, const float* x0, const uint8_t* boost_mask, float* y,
+                                    int32_t* idx_trace, float* w_trace, uint32_t* dev_err, void* stream) {
+  moe_status s = check_stack(cfg, L, T, layers, x0, y);
+  if (s != MOE_OK || T == 0) return s;
+  REQUIRE(L <= kScratchMaxLayers, MOE_ERR_UNSUPPORTED, "L=%d: at most %d layers", L, kScratchMaxLayers);
+  REQUIRE(!dev_err || aligned(dev_err, 4), MOE_ERR_ALIGN, "dev_err must be 4-byte aligned");
+  const WsLayout wl = ws_layout(*cfg, T, L, false);
+  REQUIRE(wl.total <= kScratchBytes, MOE_ERR_WORKSPACE,
+          "this shape needs %zu bytes of scratch; the library's fixed array holds %zu", wl.total,
+          kScratchBytes);
+  LayerPtrs table[kScratchMaxLayers];
+  s = validate_layers(*cfg, L, layers, table);
+  if (s != MOE_OK) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = nullptr;
+  s = scratch_of(st, ws);
+  if (s != MOE_OK) return s;
+  s = run_stack(cfg, L, layers, table, T, x0, boost_mask, y, idx_trace, w_trace, ws, wl, st);
+  if (s != MOE_OK) return s;
+  if (dev_err) {
+    const hipError_t e = hipMemcpyAsync(dev_err, ws + wl.err, sizeof(uint32_t), hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "copying the device error word");
+  }
+  return MOE_OK;
 }
 
 size_t moe_qkv_packed_bytes(const moe_qkv_config* cfg) {

@@ -131,7 +131,9 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Router logits per lane of the top-K wave: ceil(E / 64) rounded up to even.
 __host__ __device__ constexpr int lx_per_lane(int E) { return (((E + kWave - 1) / kWave) + 1) & ~1; }
 
-inline WsLayout ws_layout(const moe_config& c, int T, int L) {
+// with_ctab = false leaves out the streamed stack's cache tables (calls that do
+// not stream never touch them)
+inline WsLayout ws_layout(const moe_config& c, int T, int L, bool with_ctab = true) {
   (void)T;
   WsLayout w;
   size_t o = 0;
@@ -148,7 +150,8 @@ inline WsLayout ws_layout(const moe_config& c, int T, int L) {
   w.prev = o; o = align256(o + sizeof(uint64_t) * 2 * (size_t)(L > 0 ? L : 1) * kMaxK);
   w.layers = o; o = align256(o + sizeof(LayerPtrs) * (size_t)(L > 0 ? L : 1));
   // streamed stack: every workgroup's copy of every layer's expert-cache table
-  w.ctab = o; o = align256(o + sizeof(uint64_t) * (size_t)kMaxNwg * (L > 0 ? L : 1) * kMaxCacheSlots);
+  w.ctab = o;
+  if (with_ctab) o = align256(o + sizeof(uint64_t) * (size_t)kMaxNwg * (L > 0 ? L : 1) * kMaxCacheSlots);
   w.total = o;
   return w;
 }

@@ -203,3 +203,33 @@ int main(void) {
                     "-L", lib_dir, "-lqmoe", f"-Wl,-rpath,{lib_dir}"], check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
     assert out == ["7077888", "11796480", "0"]
+
+
+def test_noalloc_stack_limits_checked_before_any_device_call():
+    """moe_stack_decode_noalloc rejects what its fixed 4 MiB scratch array cannot
+    hold (more than 128 layers; a shape whose workspace exceeds it) and bad layers,
+    all before any HIP call; the pages' shape (hidden 4096, inter 1024, 512 experts)
+    fits."""
+    L = q.lib()
+    p = ctypes.c_void_p(1 << 20)
+    lw = q.LayerWeights(1 << 20, 1 << 21, 1 << 22, None)
+    arr = (q.LayerWeights * 129)(*([lw] * 129))
+    cfg = q.Config.make(4096, 1024, 512, flags=q.MOE_F_RMSNORM | q.MOE_F_RESIDUAL)
+    assert L.moe_stack_decode_noalloc(ctypes.byref(cfg), 129, arr, 2, p, None, p, None, None, None,
+                                      None) == q.MOE_ERR_UNSUPPORTED
+    wide = q.Config.make(4096, 4096, 512, flags=q.MOE_F_RMSNORM | q.MOE_F_RESIDUAL)
+    assert L.moe_stack_decode_noalloc(ctypes.byref(wide), 60, arr, 2, p, None, p, None, None, None,
+                                      None) == q.MOE_ERR_WORKSPACE
+    assert b"scratch" in L.moe_last_error()
+    bad = (q.LayerWeights * 60)(*([lw] * 59 + [q.LayerWeights(None, 1 << 21, 1 << 22, None)]))
+    assert L.moe_stack_decode_noalloc(ctypes.byref(cfg), 60, bad, 256, p, None, p, None, None, None,
+                                      None) == q.MOE_ERR_ARG
+    assert b"layer 59" in L.moe_last_error()
+    assert L.moe_stack_decode_noalloc(ctypes.byref(cfg), 60, arr, 256, p, None, p, None, None,
+                                      ctypes.c_void_p((1 << 20) + 2), None) == q.MOE_ERR_ALIGN
+    assert L.moe_stack_decode_noalloc(ctypes.byref(cfg), 60, arr, 0, p, None, p, None, None, None,
+                                      None) == q.MOE_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert L.moe_stack_decode_noalloc(ctypes.byref(cfg), 60, arr, 256, p, None, p, None, None, None,
+                                          None) == q.MOE_ERR_HIP
