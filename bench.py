@@ -3,8 +3,14 @@
 
 One step = one moe_stack_decode call: 256 sequential decode tokens through 60
 MoE layers (RMSNorm -> router -> top-4 + shared expert -> SwiGLU experts ->
-weighted combine + residual), all expert weights resident in HBM, 27% of each
-token's routed experts repeating the previous token's (temporal tier).
+weighted combine + residual), all expert weights resident in HBM. A temporal tier
+promotes a seeded 27% of the previous token's experts at every layer. On the
+default workload (unsigned codes, positive scales: weights with a positive mean)
+the realised repeat fraction is higher, about 0.58: after layer 0 every token's
+residual stream falls into one of two basins whose routing no longer depends on
+the token. `--zero-mean` keeps the shapes and bytes but makes the dequantised
+weights zero-mean, so routing stays token-dependent and the realised repeat is
+the tier's share plus a small natural overlap (both reported).
 
 Prints one JSON line. `value` is decode tokens/s; `roofline` prices the decode
 kernel's algorithmic bytes (weights touched per token, the per-token figure
@@ -27,6 +33,7 @@ FETCH_SIZE / WRITE_SIZE counters, calibrated against a plain copy):
                        profiles/decode_stack60_traffic.json that later runs report
 """
 import argparse
+import contextlib
 import json
 import os
 import sys
@@ -40,6 +47,22 @@ PEAK_HBM_GBS = 8000.0
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+@contextlib.contextmanager
+def one_core():
+    """The CPU baseline runs on one core: while the oracle runs, the process is
+    pinned to the first core it may use and the BLAS thread pools are held to one
+    thread; both are restored afterwards."""
+    from threadpoolctl import threadpool_limits
+    prev = os.sched_getaffinity(0)
+    core = min(prev)
+    os.sched_setaffinity(0, {core})
+    try:
+        with threadpool_limits(limits=1):
+            yield core
+    finally:
+        os.sched_setaffinity(0, prev)
 
 
 def per_token_bytes(w, gated=False):
@@ -83,6 +106,45 @@ def copy_rate_gbs(nbytes=1 << 31, reps=5):
     torch.cuda.synchronize()
     rate = 2 * nbytes * reps / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9
     del src, dst
+    torch.cuda.empty_cache()
+    return rate
+
+
+def repeat_fractions(ih, mask):
+    """Share of each token's routed experts (tokens after the first) that the
+    previous token also used at the same layer, split into the tier's part (experts
+    the boost mask promoted, which always repeat) and the natural overlap of the
+    rest; the two add up to the realised repeat fraction."""
+    T, L, K = ih.shape
+    tier = natural = 0
+    for t in range(1, T):
+        for l in range(L):
+            prev = sorted(int(e) for e in ih[t - 1, l])
+            cur = {int(e) for e in ih[t, l]}
+            promoted = {prev[j] for j in range(K) if mask[t, l, j]}
+            tier += len(promoted & cur)
+            natural += len((cur & set(prev)) - promoted)
+    n = max(1, (T - 1) * L * K)
+    return tier / n, natural / n
+
+
+def read_rate_gbs(nbytes=1 << 31, reps=5):
+    """Read-only HBM stream rate (bytes read per second) of a plain load kernel: the
+    practical ceiling of a kernel that only reads, as the decode kernel nearly does."""
+    import torch
+    from workload import device as wdev
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wdev.read_probe(buf, sink)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        wdev.read_probe(buf, sink)
+    ev[1].record()
+    torch.cuda.synchronize()
+    rate = nbytes * reps / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9
+    del buf
     torch.cuda.empty_cache()
     return rate
 
@@ -244,19 +306,20 @@ def prefill_bench(args, w):
         toks = [int(t) for t in np.linspace(0, T - 1, n)]
         dt = 0.0
         worst = (0.0, 0.0)
-        for t in toks:
-            for e in ih[t]:  # generate this token's experts outside the timed region
-                cl.expert(int(e))
-            g0 = cl.gen_seconds
-            t1 = time.perf_counter()
-            r = ref.prefill_token(xh[t], cl.router, cl.expert, cl.shared(), K, sel_h[t])
-            dt += time.perf_counter() - t1 - (cl.gen_seconds - g0)
-            assert np.array_equal(np.asarray(r.idx), ih[t]), f"token {t}: experts differ"
-            rm, rl = parity(yh[t], r.y, f"prefill token {t}")
-            worst = (max(worst[0], rm), max(worst[1], rl))
+        with one_core() as core:
+            for t in toks:
+                for e in ih[t]:  # generate this token's experts outside the timed region
+                    cl.expert(int(e))
+                g0 = cl.gen_seconds
+                t1 = time.perf_counter()
+                r = ref.prefill_token(xh[t], cl.router, cl.expert, cl.shared(), K, sel_h[t])
+                dt += time.perf_counter() - t1 - (cl.gen_seconds - g0)
+                assert np.array_equal(np.asarray(r.idx), ih[t]), f"token {t}: experts differ"
+                rm, rl = parity(yh[t], r.y, f"prefill token {t}")
+                worst = (max(worst[0], rm), max(worst[1], rl))
         cpu = {"value": round(n / dt, 4), "unit": "tok/s", "cores": 1, "kind": "oracle",
                "sample": f"{n} of the {T} tokens (evenly spaced), one layer each, {dt:.1f} s of "
-                         f"single-threaded fp64 oracle arithmetic"}
+                         f"fp64 oracle arithmetic on one pinned core"}
         par = {"tokens": n, "max_rel_err": float(worst[0]), "rel_l2": float(worst[1]),
                "experts_equal": True}
         log(f"cpu oracle: {dt:.1f} s for {n} tokens -> {cpu['value']} tok/s")
@@ -378,7 +441,8 @@ def stream_bench(args, w):
     pcie_bytes = misses * eb  # routed experts read from host memory per step
     pcie_gbs = pcie_bytes / avg_s / 1e9
     ih = idx.cpu().numpy()
-    rep = np.mean([len(set(ih[t, l]) & set(ih[t - 1, l])) / K for t in range(1, T) for l in range(L)])
+    rep_tier, rep_nat = repeat_fractions(ih, mask.cpu().numpy())
+    rep = rep_tier + rep_nat
     h2d = h2d_rate(pins[0])
     log(f"streamed: {T * args.steps / elapsed:.1f} tok/s ({L} layers), launch avg {avg_s * 1e3:.2f} ms, "
         f"hit rate {hit_rate:.3f}, {pcie_gbs:.1f} GB/s from host memory (copy engine {h2d:.1f} GB/s)")
@@ -386,10 +450,11 @@ def stream_bench(args, w):
     cpu, par = None, None
     if not args.no_cpu:
         n = min(args.cpu_tokens, T)
-        dt, par = cpu_baseline_and_parity(w.replace(n_tokens=T), x0.cpu().numpy(), y.cpu().numpy(), ih, n)
+        with one_core() as core:
+            dt, par = cpu_baseline_and_parity(w.replace(n_tokens=T), x0.cpu().numpy(), y.cpu().numpy(), ih, n)
         cpu = {"value": round(n / dt, 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
                "sample": f"tokens 0-{n - 1} through all {L} layers (temporal tier replayed), "
-                         f"{dt:.1f} s of single-threaded fp64 oracle arithmetic"}
+                         f"{dt:.1f} s of fp64 oracle arithmetic on one pinned core"}
     out = {
         "metric": f"streamed decode tok/s, {L}-layer {w.bits}-bit MoE stack, routed experts in host memory",
         "value": round(T * args.steps / elapsed, 2),
@@ -406,7 +471,9 @@ def stream_bench(args, w):
         "config": {"workload": f"{w.name}-streamed", "layers": L, "tokens_per_step": T, "hidden": H,
                    "inter": w.inter, "experts": w.n_experts, "top_k": K, "shared": w.n_shared, "bits": w.bits,
                    "cache_slots": C, "temporal_repeat_target": w.temporal_p,
-                   "temporal_repeat_realised": round(float(rep), 4), "cache_hit_rate": round(hit_rate, 4),
+                   "temporal_repeat_realised": round(float(rep), 4),
+                   "temporal_repeat_tier": round(rep_tier, 4), "temporal_repeat_natural": round(rep_nat, 4),
+                   "cache_hit_rate": round(hit_rate, 4),
                    "host_bytes_per_step": pcie_bytes},
         "roofline": {"bound": "pcie", "achieved": round(pcie_gbs, 2), "peak": PCIE5_X16_GBS, "unit": "GB/s",
                      "frac": round(pcie_gbs / PCIE5_X16_GBS, 4), "traffic": None,
@@ -479,15 +546,16 @@ def qkv_bench(args):
             r0 += r
         got = [o.cpu().numpy() for o in outs]
         worst = (0.0, 0.0)
-        t1 = time.perf_counter()
-        for t in range(T):
-            want = ref.qkv(mats, x_h[t], gamma=gamma_h, norm=True)
-            for g_, w_ in zip(got, want):
-                rm, rl = parity(g_[t], w_, f"qkv token {t}")
-                worst = (max(worst[0], rm), max(worst[1], rl))
-        dt = time.perf_counter() - t1
+        with one_core() as core:
+            t1 = time.perf_counter()
+            for t in range(T):
+                want = ref.qkv(mats, x_h[t], gamma=gamma_h, norm=True)
+                for g_, w_ in zip(got, want):
+                    rm, rl = parity(g_[t], w_, f"qkv token {t}")
+                    worst = (max(worst[0], rm), max(worst[1], rl))
+            dt = time.perf_counter() - t1
         cpu = {"value": round(T / dt, 3), "unit": "calls/s" if T == 1 else "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"all {T} token(s) of one call, {dt:.2f} s of single-threaded fp64 oracle arithmetic"}
+               "sample": f"all {T} token(s) of one call, {dt:.2f} s of fp64 oracle arithmetic on one pinned core"}
         par = {"tokens": T, "max_rel_err": float(worst[0]), "rel_l2": float(worst[1])}
     out = {
         "metric": f"fused Q/K/V projection calls/s, hidden 4096 -> 4096+512+512, {bits}-bit, {T} token(s)",
@@ -561,18 +629,19 @@ def layer_bench(args):
         ih = idx.cpu().numpy()
         worst = (0.0, 0.0)
         dt = 0.0
-        for t in range(T):
-            for e in ih[t]:
-                cl.expert(int(e))
-            cl.shared()
-            t1 = time.perf_counter()
-            r = ref.layer_decode(x_h[t], cl.router, cl.expert, cl.shared(), w.top_k)
-            dt += time.perf_counter() - t1
-            if not same_set(r.idx, ih[t]):
-                assert r.gap < NEAR_TIE
-                r = ref.layer_decode(x_h[t], cl.router, cl.expert, cl.shared(), w.top_k, force_idx=ih[t])
-            rm, rl = parity(y.cpu().numpy()[t], r.y, f"layer token {t}")
-            worst = (max(worst[0], rm), max(worst[1], rl))
+        with one_core() as core:
+            for t in range(T):
+                for e in ih[t]:
+                    cl.expert(int(e))
+                cl.shared()
+                t1 = time.perf_counter()
+                r = ref.layer_decode(x_h[t], cl.router, cl.expert, cl.shared(), w.top_k)
+                dt += time.perf_counter() - t1
+                if not same_set(r.idx, ih[t]):
+                    assert r.gap < NEAR_TIE
+                    r = ref.layer_decode(x_h[t], cl.router, cl.expert, cl.shared(), w.top_k, force_idx=ih[t])
+                rm, rl = parity(y.cpu().numpy()[t], r.y, f"layer token {t}")
+                worst = (max(worst[0], rm), max(worst[1], rl))
         cpu = {"value": round(T / dt, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
                "sample": f"the call's {T} token(s) through the layer, {dt:.2f} s of single-threaded fp64 oracle "
                          f"arithmetic"}
@@ -620,6 +689,9 @@ def main():
                          "streamed: the stack with routed experts in pinned host memory "
                          "(default 16 layers, 64 tokens)")
     ap.add_argument("--cache-slots", type=int, default=16, help="streamed: HBM cache slots per layer")
+    ap.add_argument("--zero-mean", action="store_true",
+                    help="decode/streamed: the same shapes and bytes with zero-mean dequantised weights "
+                         "(bias = -(2^bits-1)/2 * scale + noise), where routing stays token-dependent")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     args = ap.parse_args()
@@ -649,6 +721,8 @@ def main():
     if args.workload == "streamed":
         w = wl.STACK60_3BIT if args.bits == 3 else wl.WORKLOADS[args.config]
         w = w.replace(n_layers=args.layers or 16, n_tokens=args.tokens or 64)
+        if args.zero_mean:
+            w = w.replace(name=w.name + "-zero-mean", zero_mean=True)
         return stream_bench(args, w)
 
     import numpy as np
@@ -660,6 +734,8 @@ def main():
     w = wl.STACK60_3BIT if args.bits == 3 else wl.WORKLOADS[args.config]
     if args.layers or args.tokens:
         w = w.replace(n_layers=args.layers or w.n_layers, n_tokens=args.tokens or w.n_tokens)
+    if args.zero_mean:
+        w = w.replace(name=w.name + "-zero-mean", zero_mean=True)
     L, T, K, H = w.n_layers, w.n_tokens, w.top_k, w.hidden
     flags = q.MOE_F_PHASED if args.phased else 0
     cfg = config_for(w, flags)
@@ -714,21 +790,24 @@ def main():
         f"{achieved:.0f} GB/s")
 
     copy_gbs = copy_rate_gbs()
-    log(f"device copy {copy_gbs:.0f} GB/s (read + write)")
+    read_gbs = read_rate_gbs()
+    log(f"device copy {copy_gbs:.0f} GB/s (read + write), read-only stream {read_gbs:.0f} GB/s")
 
     # realised temporal repeat fraction (routing workload check)
     ih = idx.cpu().numpy()
-    rep = np.mean([len(set(ih[t, l]) & set(ih[t - 1, l])) / K for t in range(1, T) for l in range(L)])
+    rep_tier, rep_nat = repeat_fractions(ih, mask.cpu().numpy())
+    rep = rep_tier + rep_nat
 
     cpu = None
     par = None
     if not args.no_cpu:
         n = min(args.cpu_tokens, T)
-        dt, par = cpu_baseline_and_parity(w, x0.cpu().numpy(), y.cpu().numpy(), ih, n, gated=args.shared_gate)
+        with one_core() as core:
+            dt, par = cpu_baseline_and_parity(w, x0.cpu().numpy(), y.cpu().numpy(), ih, n, gated=args.shared_gate)
         cpu = {"value": round(n / dt, 6), "unit": "tok/s", "cores": 1, "kind": "oracle",
                "sample": f"tokens 0-{n - 1} through all {L} layers (temporal tier replayed), "
-                         f"{dt:.1f} s of single-threaded fp64 oracle arithmetic",
-               "host": f"{host_cpu()}, {os.cpu_count()} logical CPUs visible, 1 used"}
+                         f"{dt:.1f} s of fp64 oracle arithmetic on one pinned core",
+               "host": f"{host_cpu()}, {os.cpu_count()} logical CPUs visible, pinned to core {core}"}
         log(f"cpu oracle: {dt:.1f} s for {n} tokens x {L} layers -> {cpu['value']:.4f} tok/s")
 
     traffic = None
@@ -759,11 +838,12 @@ def main():
         "config": {"workload": w.name, "layers": L, "tokens_per_step": T, "hidden": H, "inter": w.inter,
                    "experts": w.n_experts, "top_k": K, "shared": w.n_shared, "bits": w.bits,
                    "temporal_repeat_target": w.temporal_p, "temporal_repeat_realised": round(float(rep), 4),
+                   "temporal_repeat_tier": round(rep_tier, 4), "temporal_repeat_natural": round(rep_nat, 4),
                    "bytes_per_token": ptb, "mode": "phased" if args.phased else "persistent",
                    "shared_gate": bool(args.shared_gate)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "device_copy_gbs": round(copy_gbs, 1)},
+                     "device_copy_gbs": round(copy_gbs, 1), "device_read_gbs": round(read_gbs, 1)},
         "cpu_baseline": cpu,
         "parity": par,
         "effective_hbm_gbs": round(ptb * tok_s / 1e9, 1),

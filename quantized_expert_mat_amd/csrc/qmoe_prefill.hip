@@ -17,20 +17,20 @@
 //   router   (only when the selection needs all logits) logits = x_n W^T, float32
 //   select   one wave per token: top-K by (tier, score, lower index), softmax of the
 //            selected router logits (computed here when selection is by sel_bias)
-//   group    one workgroup: stable counting of (token, slot) pairs by expert via a
-//            bitonic sort of (expert, pair) keys; per-expert row runs; m-tile table
+//   group    one workgroup: counting sort of the (token, slot) pairs by expert
+//            (counts, exclusive scan, row claims); per-expert row runs; m-tile table
 //   gateup   grouped GEMM: rows of one expert x 64 intermediate columns per
 //            workgroup, gate and up fused, h = bf16(silu(g) * u)
 //   down     grouped GEMM: rows x 128 output columns per workgroup -> float32 rows
 //   combine  y = x_b + sum_k w_k o_k + sum_s o_s, fixed order per token
 //
 // Weights are dequantised in registers by the lane that feeds them to the MFMA (no
-// LDS round trip for B); activations are staged through LDS per 128-wide reduction
-// chunk. Inside a chunk the reduction index is permuted identically for the A and B
-// operands (the MFMA sums over it, so any common permutation is exact): lane group
-// kk = lane/16 covers chunk positions [32kk, 32kk+32) and MFMA step i the octet
-// [32kk+8i, 32kk+8i+8), which is exactly one 16-byte code chunk of the packed layout
-// for 4-bit codes (half a slot for 2-bit codes).
+// LDS round trip for B); activations are staged through LDS per 256-wide reduction
+// chunk (four 64-groups). Inside a chunk the reduction index is permuted identically
+// for the A and B operands (the MFMA sums over it, so any common permutation is
+// exact): lane group kk = lane/16 covers group kk of the chunk, positions
+// [64kk, 64kk+64), and MFMA step i (i = 0..7) the octet [64kk+8i, 64kk+8i+8) of it,
+// so each lane dequantises whole groups of one packed slot.
 #include <string>
 
 #include "qmoe_internal.h"

@@ -1,7 +1,8 @@
 """Device-side fill of the synthetic workload (same bits as ``workload.gen``).
 
 Used by the GPU tests and the benchmark to materialise large weight sets in
-HBM directly. Generation only; no MoE arithmetic.
+HBM directly, and the read-only HBM stream probe of the benchmark. Generation and
+measurement only; no MoE arithmetic.
 """
 import ctypes
 import os
@@ -45,6 +46,8 @@ def lib():
         L.qgen_zero_mean_bias.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong,
                                           ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.c_void_p]
+        L.qgen_read_probe.restype = ctypes.c_int
+        L.qgen_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -90,6 +93,14 @@ def fill_zero_mean_bias(skeys, bkeys, n, sigma_scale, sigma_bias, bits, out):
     if rc != 0:
         raise RuntimeError(f"qgen_zero_mean_bias failed: hipError {rc}")
     return (st, bt)
+
+
+def read_probe(buf, sink):
+    """Launch the read-only stream probe over the device tensor buf (its bytes a
+    multiple of 16) on torch's current stream; sink is a device int32 tensor."""
+    rc = lib().qgen_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), _stream())
+    if rc != 0:
+        raise RuntimeError(f"qgen_read_probe failed: hipError {rc}")
 
 
 def experts_canonical(spec, seed, layer, experts, codes, scales, biases):

@@ -1,6 +1,7 @@
 // gen_device.hip -- device implementation of the counter-based workload generator
-// (the definition is in workload/gen.py; both produce identical bits). Input
-// generation only: no part of the MoE computation lives here.
+// (the definition is in workload/gen.py; both produce identical bits), plus the
+// read-only HBM stream probe the benchmark calibrates against. Input generation and
+// measurement only: no part of the MoE computation lives here.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -91,6 +92,25 @@ __global__ void zero_mean_bias_kernel(const uint64_t* skeys, const uint64_t* bke
   }
 }
 
+// Read-only stream: every 16-byte word of p is loaded once, four loads in flight per
+// thread. The xor of the words reaches memory only under a test the data never
+// meets (the caller fills the buffer with one repeated byte), so the loads stay and
+// nothing is written.
+__global__ void __launch_bounds__(256) read_probe_kernel(const uint4* p, long long n16, unsigned* sink) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 unsigned grid_for(long long total) {
   long long b = (total + 255) / 256;
   if (b > 65536) b = 65536;
@@ -121,6 +141,14 @@ int qgen_zero_mean_bias(const uint64_t* skeys, const uint64_t* bkeys, int nkeys,
                         double sigma_b, int bits, void* out, void* stream) {
   hipLaunchKernelGGL(zero_mean_bias_kernel, dim3(grid_for(n * nkeys)), dim3(256), 0, (hipStream_t)stream, skeys,
                      bkeys, nkeys, n, sigma_s, sigma_b, ((1 << bits) - 1) / 2.0, static_cast<uint16_t*>(out));
+  return (int)hipGetLastError();
+}
+
+// bytes: a multiple of 16; p 16-byte aligned; sink: one writable device word.
+int qgen_read_probe(const void* p, long long bytes, unsigned* sink, void* stream) {
+  if (bytes % 16 != 0 || (uintptr_t)p % 16 != 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_probe_kernel, dim3(8192), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint4*>(p), bytes / 16, sink);
   return (int)hipGetLastError();
 }
 
