@@ -314,6 +314,48 @@ __device__ inline void poll_pause(const DecodeArgs& a) {
   for (int i = 0; i < a.poll_sleep; ++i) __builtin_amdgcn_s_sleep(1);
 }
 
+// Request this thread's chunks base + tid + k*kThreads (k < kPer) of this
+// workgroup's replica of x.
+template <int kPer>
+__device__ __forceinline__ void xissue(const Xv& x, int base, v4u (&v)[kPer]) {
+  const unsigned long long* src = x.base + (size_t)(blockIdx.x % kRep) * x.n_pad;
+  const __amdgpu_buffer_rsrc_t r = coh_rsrc(src, x.n_pad * 8);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) v[k] = ld_coh4(r, (base + (int)threadIdx.x + k * kThreads) * 16);
+}
+
+// Given the chunks xissue requested, poll until every one of them carries `epoch`
+// and copy the values into LDS (dst[i]). Returns false if the kernel is aborting.
+template <int kPer>
+__device__ __forceinline__ bool xwait(const DecodeArgs& a, const Xv& x, int base, float* dst, unsigned epoch,
+                                      v4u (&v)[kPer]) {
+  const unsigned long long* src = x.base + (size_t)(blockIdx.x % kRep) * x.n_pad;
+  const __amdgpu_buffer_rsrc_t r = coh_rsrc(src, x.n_pad * 8);
+  const int nch = (x.n + 1) / 2;  // only the n produced values are awaited
+  const unsigned long long t0 = wall_clock64();
+  for (unsigned it = 0;; ++it) {
+    unsigned pending = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int c = base + (int)threadIdx.x + k * kThreads;
+      if (c >= nch) continue;
+      const bool ok0 = v[k].y == epoch, ok1 = v[k].w == epoch || 2 * c + 1 >= x.n;
+      if (ok0 && ok1) {
+        dst[2 * c] = __uint_as_float(v[k].x);
+        if (2 * c + 1 < x.n) dst[2 * c + 1] = __uint_as_float(v[k].z);
+      } else {
+        pending |= 1u << k;
+      }
+    }
+    if (!pending) return true;
+    if ((it & 31u) == 31u && !poll_abort(a, t0, 1)) return false;
+    poll_pause(a);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (pending & (1u << k)) v[k] = ld_coh4(r, (base + (int)threadIdx.x + k * kThreads) * 16);
+  }
+}
+
 // Wait until every pair of this workgroup's replica carries `epoch` and copy the
 // values into LDS (dst[i]). All threads take part; each polls its own chunks,
 // kPer 16-byte chunks per thread in flight at once (a vector of up to
@@ -321,43 +363,13 @@ __device__ inline void poll_pause(const DecodeArgs& a) {
 // Returns false if the kernel is aborting.
 template <int kPer = 8>
 __device__ __forceinline__ bool xget(const DecodeArgs& a, const Xv& x, float* dst, unsigned epoch) {
-  const unsigned long long* src = x.base + (size_t)(blockIdx.x % kRep) * x.n_pad;
-  const __amdgpu_buffer_rsrc_t r = coh_rsrc(src, x.n_pad * 8);
-  const int nch = (x.n + 1) / 2;  // only the n produced values are awaited
-  bool ok = true;
+  const int nch = (x.n + 1) / 2;
   for (int base = 0; base < nch; base += kThreads * kPer) {
     v4u v[kPer];
-    unsigned pending = 0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) v[k] = ld_coh4(r, (base + (int)threadIdx.x + k * kThreads) * 16);
-    const unsigned long long t0 = wall_clock64();
-    for (unsigned it = 0;; ++it) {
-      pending = 0;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int c = base + (int)threadIdx.x + k * kThreads;
-        if (c >= nch) continue;
-        const bool ok0 = v[k].y == epoch, ok1 = v[k].w == epoch || 2 * c + 1 >= x.n;
-        if (ok0 && ok1) {
-          dst[2 * c] = __uint_as_float(v[k].x);
-          if (2 * c + 1 < x.n) dst[2 * c + 1] = __uint_as_float(v[k].z);
-        } else {
-          pending |= 1u << k;
-        }
-      }
-      if (!pending) break;
-      if ((it & 31u) == 31u && !poll_abort(a, t0, 1)) {
-        ok = false;
-        break;
-      }
-      poll_pause(a);
-#pragma unroll
-      for (int k = 0; k < kPer; ++k)
-        if (pending & (1u << k)) v[k] = ld_coh4(r, (base + (int)threadIdx.x + k * kThreads) * 16);
-    }
-    if (!ok) break;
+    xissue<kPer>(x, base, v);
+    if (!xwait<kPer>(a, x, base, dst, epoch, v)) return false;
   }
-  return ok;
+  return true;
 }
 
 // ---------------------------------------------------------------- reductions (DPP)
@@ -931,8 +943,25 @@ struct StaticPre {
 };
 
 
+// chunks per thread that poll the shared and the routed h of the specialised shape
+constexpr int kSpecShHPer = kSpecS * kSpecI / 2 / kThreads;
+constexpr int kSpecRtHPer = kSpecK * kSpecI / 2 / kThreads;
+
+// Down job k of this lane in phase C (defined with the phase-C code below).
+struct DnJob {
+  bool on;     // this lane has a slot to read (its row lies inside the workgroup's)
+  int pass;    // -1: no job k on this wave
+  int li, row, slot;
+  const uint8_t* blk;
+  uint8_t* wb;  // streamed stack: the cache block the slot is copied to, or NULL
+  float wk;
+};
+template <bool STREAM = false>
+__device__ __forceinline__ DnJob down_job(const DecodeArgs& a, const Lds& s, int l, int k);
+
 struct DownPre {
   Slot d[kDnPre];
+  v4u shp[kSpecShHPer];  // specialised kernel: the shared expert's h, requested at the end of phase B
 };
 
 // Router rows of this workgroup (float4 q = tid + kThreads*i of rows [e0, e1)) and
@@ -1126,7 +1155,7 @@ __device__ __forceinline__ void load_shared_spec(const DecodeArgs& a, const Lds&
 // the routed experts' loads.
 template <int BITS>
 __device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, int t, int l, const StaticPre& sp,
-                                             SharedSpec& sh) {
+                                             SharedSpec& sh, DownPre& dp) {
   constexpr int H = kSpecH;
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   const unsigned epoch = epoch_of(a, t, l);
@@ -1190,6 +1219,12 @@ __device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, 
   if (!s.sm->ok) return false;
   SUBSTAMP(14);
   if (w > 0) load_shared_spec<BITS>(a, s, l, sh);
+  {
+    // this lane's down slot of the shared expert (the last down job): phase C
+    // reduces it while the routed experts' down slots are still arriving
+    const DnJob j = down_job(a, s, l, kDnPre - 1);
+    dp.d[kDnPre - 1] = ld_slot<BITS>(j.on ? j.blk : get_layer(a, s, l).shared, j.on ? j.slot : 0, false);
+  }
   float rinv = 1.f;
   if (norm) {
     ss = 0.f;
@@ -1878,16 +1913,7 @@ __device__ inline const uint8_t* list_expert(const DecodeArgs& a, const Lds& s, 
 // pair that wave w walks, in the order of the direct loop. A pass covers expert-list
 // entries [first, first + n); lane (p, kl, grp) handles row r0 + c*Pp + p, entry
 // first + kl and group grp of chunk c = w + kNW*m.
-struct DnJob {
-  bool on;     // this lane has a slot to read (its row lies inside the workgroup's)
-  int pass;    // -1: no job k on this wave
-  int li, row, slot;
-  const uint8_t* blk;
-  uint8_t* wb;  // streamed stack: the cache block the slot is copied to, or NULL
-  float wk;
-};
-
-template <bool STREAM = false>
+template <bool STREAM>
 __device__ __forceinline__ DnJob down_job(const DecodeArgs& a, const Lds& s, int l, int k) {
   const Geo& g = a.geo;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -2025,17 +2051,24 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
     const float pg = seg_sum(slot_dot<BITS>(G[j], D), kWave);
     const float pu = seg_sum(slot_dot<BITS>(U[j], D), kWave);
     if (lane == 0) xput(hxv, k * g.I + row[j], silu(pg) * pu, epoch);
-  }  const uint8_t* db[kDnPre];
-  int ds[kDnPre];
+  }
+  // the routed experts' down slots of phase C, requested once the gate/up dots are
+  // done, behind a first poll of the shared expert's h (published before the routed
+  // dots by every workgroup): that poll then returns ahead of the down slots, and
+  // phase C starts on the shared expert at once
+  const uint8_t* db[kDnPre - 1];
+  int ds[kDnPre - 1];
 #pragma unroll
-  for (int q = 0; q < kDnPre; ++q) {
+  for (int q = 0; q < kDnPre - 1; ++q) {
     const DnJob j = down_job(a, s, l, q);
     db[q] = j.on ? j.blk : ex;
     ds[q] = j.on ? j.slot : 0;
   }
+  const Xv shx{hxv.base + (size_t)kSpecK * g.I, kSpecS * g.I, hxv.n_pad};
   issue_order();
+  xissue<kSpecShHPer>(shx, 0, dp.shp);
 #pragma unroll
-  for (int q = 0; q < kDnPre; ++q) dp.d[q] = ld_slot<BITS>(db[q], ds[q], false);
+  for (int q = 0; q < kDnPre - 1; ++q) dp.d[q] = ld_slot<BITS>(db[q], ds[q], false);
   issue_order();
 }
 
@@ -2126,10 +2159,6 @@ __device__ __forceinline__ bool phase_b(const DecodeArgs& a, const Lds& s, int t
   return true;
 }
 
-// chunks per thread that poll the shared and the routed h of the specialised shape
-constexpr int kSpecShHPer = kSpecS * kSpecI / 2 / kThreads;
-constexpr int kSpecRtHPer = kSpecK * kSpecI / 2 / kThreads;
-
 template <int BITS, bool SPEC = false, bool STREAM = false>
 __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t, int l,
                                         bool pre_down, DownPre& dp, bool down_loaded,
@@ -2145,14 +2174,17 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   // requested before these polls, so they have landed when the polls complete)
   float* hs = s.hstage;
   if constexpr (SPEC) {
-    // The shared expert's h was published in phase A, long before the routed
-    // experts' h: its digits and its down pass (pass 1) are done first, while the
-    // routed h is still arriving; then the routed h and pass 0. (The general
-    // kernel keeps one poll: there the split measured slower.)
+    // The shared expert's h was published in phase B before the routed dots, and
+    // its poll went out at the end of phase B, ahead of the routed down slots; its
+    // down slot came in phase A. So its digits and its down pass (pass 1) are done
+    // first, while the routed h and the routed down slots are still arriving; then
+    // the routed h and pass 0. (The general kernel keeps one poll: there the split
+    // measured slower.)
     const Xv hv = xv_h(a, epoch_of(a, t, l));
     const int K = a.K, Gi = g.Gi;
     const Xv sh{hv.base + (size_t)K * I, a.S * I, hv.n_pad};
-    if (!wg_all(s.sm, xget<kSpecShHPer>(a, sh, hs + K * I, epoch_of(a, t, l)))) return false;
+    static_assert(kSpecS * kSpecI / 2 == kThreads * kSpecShHPer, "the shared h is one round of chunks");
+    if (!wg_all(s.sm, xwait<kSpecShHPer>(a, sh, 0, hs + K * I, epoch_of(a, t, l), dp.shp))) return false;
     encode_vectors<false>(hs + K * I, a.S, I, 1.f, nullptr, s.hdig + K * Gi * kDigitStride,
                           s.hsum + 4 * K * Gi);
     __syncthreads();
@@ -2268,7 +2300,7 @@ __device__ __forceinline__ void decode_chain(const DecodeArgs& a, const Lds& s) 
                                     ? a.trace_wg + ((size_t)l * a.nwg + blockIdx.x) * 4
                                     : nullptr;
       if constexpr (SPEC) {
-        if (!phase_a_spec<BITS>(a, s, t, l, sp, sh)) return;
+        if (!phase_a_spec<BITS>(a, s, t, l, sp, sh, dp)) return;
       } else {
         if (!phase_a<BITS, SPEC>(a, s, t, l, sp, true)) return;
       }
