@@ -1121,26 +1121,19 @@ __device__ __forceinline__ void shared_gate_factors(const DecodeArgs& a, const L
   }
 }
 
-// The specialised kernel's shared-expert gate/up slots (four items per workgroup):
-// loaded by waves 1..3 in phase A, which do not poll the logits (wave w takes item
-// w - 1, wave 1 also item 3), and reduced by them in phase B.
+// The shared expert's gate/up item of this wave (the workgroup's four items, one
+// per wave), loaded in phase A and reduced in phase B under the routed loads.
 struct SharedSpec {
-  Slot g[2], u[2];
+  Slot g, u;
 };
 
 template <int BITS>
 __device__ __forceinline__ void load_shared_spec(const DecodeArgs& a, const Lds& s, int l, SharedSpec& sh) {
   const Geo& g = a.geo;
   const int w = (int)threadIdx.x / kWave, lane = (int)threadIdx.x % kWave;
-  const uint8_t* base = get_layer(a, s, l).shared + (size_t)blockIdx.x * kNW * g.blk;
-  const uint8_t* b0 = base + (size_t)(w - 1) * g.blk;
-  const uint8_t* b1 = base + (size_t)3 * g.blk;
-  sh.g[0] = ld_slot<BITS>(b0, lane, false);
-  sh.u[0] = ld_slot<BITS>(b0 + g.off_up, lane, false);
-  if (w == 1) {
-    sh.g[1] = ld_slot<BITS>(b1, lane, false);
-    sh.u[1] = ld_slot<BITS>(b1 + g.off_up, lane, false);
-  }
+  const uint8_t* b = get_layer(a, s, l).shared + ((size_t)blockIdx.x * kNW + w) * g.blk;
+  sh.g = ld_slot<BITS>(b, lane, false);
+  sh.u = ld_slot<BITS>(b + g.off_up, lane, false);
 }
 
 // Phase A of the specialised kernel. Thread t holds the 16 x values [8t, 8t + 8)
@@ -1218,7 +1211,7 @@ __device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, 
   __syncthreads();
   if (!s.sm->ok) return false;
   SUBSTAMP(14);
-  if (w > 0) load_shared_spec<BITS>(a, s, l, sh);
+  load_shared_spec<BITS>(a, s, l, sh);
   {
     // this lane's down slot of the shared expert (the last down job): phase C
     // reduces it while the routed experts' down slots are still arriving
@@ -2032,30 +2025,26 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
   spec_weights(a, s, t, l, my_idx, my_lg);
   const unsigned epoch = epoch_of(a, t, l);
   const Xv hxv = xv_h(a, epoch);
-  if (w > 0) {
-    // the shared expert's gate/up items (loaded in phase A) while the routed loads
-    // are in flight; one block of one row per item in this shape
+  {
+    // the shared expert's gate/up item of this wave (loaded in phase A) while the
+    // routed loads are in flight; one block of one row per item in this shape
     static_assert(kSpecS * kSpecI / kSpecNwg == kNW, "four shared gate/up items per workgroup");
-    const int i0 = blockIdx.x * kNW;
-    float pg = seg_sum(slot_dot<BITS>(sh.g[0], D), kWave);
-    float pu = seg_sum(slot_dot<BITS>(sh.u[0], D), kWave);
-    if (lane == 0) xput(hxv, kSpecK * g.I + i0 + w - 1, silu(pg) * pu, epoch);
-    if (w == 1) {
-      pg = seg_sum(slot_dot<BITS>(sh.g[1], D), kWave);
-      pu = seg_sum(slot_dot<BITS>(sh.u[1], D), kWave);
-      if (lane == 0) xput(hxv, kSpecK * g.I + i0 + 3, silu(pg) * pu, epoch);
-    }
+    const float pg = seg_sum(slot_dot<BITS>(sh.g, D), kWave);
+    const float pu = seg_sum(slot_dot<BITS>(sh.u, D), kWave);
+    if (lane == 0) xput(hxv, kSpecK * g.I + blockIdx.x * kNW + w, silu(pg) * pu, epoch);
   }
+  float hj[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) {
     const float pg = seg_sum(slot_dot<BITS>(G[j], D), kWave);
     const float pu = seg_sum(slot_dot<BITS>(U[j], D), kWave);
-    if (lane == 0) xput(hxv, k * g.I + row[j], silu(pg) * pu, epoch);
+    hj[j] = silu(pg) * pu;
   }
-  // the routed experts' down slots of phase C, requested once the gate/up dots are
-  // done, behind a first poll of the shared expert's h (published before the routed
-  // dots by every workgroup): that poll then returns ahead of the down slots, and
-  // phase C starts on the shared expert at once
+  // A first poll of the shared expert's h (published before the routed dots by
+  // every workgroup), then this wave's routed h, then the routed experts' down slots
+  // of phase C. The memory counter retires in issue order, stores included, so the
+  // poll goes out ahead of the stores and the loads: phase C can use it without
+  // waiting for either, and starts on the shared expert at once.
   const uint8_t* db[kDnPre - 1];
   int ds[kDnPre - 1];
 #pragma unroll
@@ -2067,6 +2056,12 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
   const Xv shx{hxv.base + (size_t)kSpecK * g.I, kSpecS * g.I, hxv.n_pad};
   issue_order();
   xissue<kSpecShHPer>(shx, 0, dp.shp);
+  issue_order();
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) xput(hxv, k * g.I + row[j], hj[j], epoch);
+  }
+  issue_order();
 #pragma unroll
   for (int q = 0; q < kDnPre - 1; ++q) dp.d[q] = ld_slot<BITS>(db[q], ds[q], false);
   issue_order();
