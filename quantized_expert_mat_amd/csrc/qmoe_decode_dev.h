@@ -305,6 +305,15 @@ __device__ inline void xput(const Xv& x, int i, float v, unsigned epoch) {
     __hip_atomic_store(base + (size_t)r * x.n_pad + i, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Replica r of value i, stored by one lane: callers spread the kRep replicas of a
+// value over kRep lanes, so a wave stores them with one instruction instead of kRep.
+__device__ inline void xput_rep(const Xv& x, int r, int i, float v, unsigned epoch) {
+  const unsigned long long pv = ((unsigned long long)epoch << 32) | __float_as_uint(v);
+  __attribute__((address_space(1))) unsigned long long* base =
+      (__attribute__((address_space(1))) unsigned long long*)(uintptr_t)launder_s(x.base);
+  __hip_atomic_store(base + (size_t)r * x.n_pad + i, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ bool poll_abort(const DecodeArgs& a, unsigned long long t0, int lane0);
 
 // Pause between two polls of data that has not arrived: a workgroup that is done
@@ -2031,7 +2040,7 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
     static_assert(kSpecS * kSpecI / kSpecNwg == kNW, "four shared gate/up items per workgroup");
     const float pg = seg_sum(slot_dot<BITS>(sh.g, D), kWave);
     const float pu = seg_sum(slot_dot<BITS>(sh.u, D), kWave);
-    if (lane == 0) xput(hxv, kSpecK * g.I + blockIdx.x * kNW + w, silu(pg) * pu, epoch);
+    if (lane < kRep) xput_rep(hxv, lane, kSpecK * g.I + blockIdx.x * kNW + w, silu(pg) * pu, epoch);
   }
   float hj[kBatch];
 #pragma unroll
@@ -2057,9 +2066,18 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
   issue_order();
   xissue<kSpecShHPer>(shx, 0, dp.shp);
   issue_order();
-  if (lane == 0) {
+  // lane j*kRep + r stores replica r of row j: all of this wave's h in one instruction
+  static_assert(kBatch * kRep <= kWave, "a wave's h replicas fit its lanes");
+  if (lane < kBatch * kRep) {
+    const int j = lane / kRep;
+    float v = hj[0];
+    int rj = row[0];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) xput(hxv, k * g.I + row[j], hj[j], epoch);
+    for (int q = 1; q < kBatch; ++q) {
+      v = j == q ? hj[q] : v;
+      rj = j == q ? row[q] : rj;
+    }
+    xput_rep(hxv, lane % kRep, k * g.I + rj, v, epoch);
   }
   issue_order();
 #pragma unroll
@@ -2253,13 +2271,25 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
   }
   __syncthreads();
   SUBSTAMP(12);
-  const int rr = r0 + (int)threadIdx.x;
-  if (rr < r1 && (int)threadIdx.x < rpw) {
-    const bool res = !expert_mode && (a.flags & MOE_F_RESIDUAL);
-    float v = res ? s.xres[threadIdx.x] : 0.f;
-    for (int pi = 0; pi < npass; ++pi) v += s.acc[pi * rpw + (rr - r0)];
-    if (expert_mode || l == a.L - 1) a.y[(size_t)t * H + rr] = v;
-    else xput(xv_x(a, epoch_of(a, t, l + 1)), rr, v, epoch_of(a, t, l + 1));
+  const bool res = !expert_mode && (a.flags & MOE_F_RESIDUAL);
+  if (expert_mode || l == a.L - 1) {
+    const int rr = r0 + (int)threadIdx.x;
+    if (rr < r1 && (int)threadIdx.x < rpw) {
+      float v = res ? s.xres[threadIdx.x] : 0.f;
+      for (int pi = 0; pi < npass; ++pi) v += s.acc[pi * rpw + (rr - r0)];
+      a.y[(size_t)t * H + rr] = v;
+    }
+  } else {
+    // thread q stores replica q % kRep of row q / kRep: the replicas of 32 rows per
+    // store instruction, each thread forming its row's sum from LDS
+    const Xv xo = xv_x(a, epoch_of(a, t, l + 1));
+    for (int q = (int)threadIdx.x; q < rpw * kRep; q += kThreads) {
+      const int i = q / kRep, rr = r0 + i;
+      if (rr >= r1) continue;
+      float v = res ? s.xres[i] : 0.f;
+      for (int pi = 0; pi < npass; ++pi) v += s.acc[pi * rpw + i];
+      xput_rep(xo, q % kRep, rr, v, epoch_of(a, t, l + 1));
+    }
   }
   // the next layer's router rows and shared slots land while x is being exchanged;
   // they are requested once the x rows above are out, so that the stores the other
