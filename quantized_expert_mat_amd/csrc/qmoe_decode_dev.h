@@ -314,6 +314,16 @@ __device__ inline void xput_rep(const Xv& x, int r, int i, float v, unsigned epo
   __hip_atomic_store(base + (size_t)r * x.n_pad + i, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A value held by all seg lanes of a segment (lane grp of it): with at least kRep
+// lanes, lane r < kRep stores replica r; otherwise lane 0 stores all of them.
+__device__ inline void xput_seg(const Xv& x, int grp, int seg, int i, float v, unsigned epoch) {
+  if (seg >= kRep) {
+    if (grp < kRep) xput_rep(x, grp, i, v, epoch);
+  } else if (grp == 0) {
+    xput(x, i, v, epoch);
+  }
+}
+
 __device__ __forceinline__ bool poll_abort(const DecodeArgs& a, unsigned long long t0, int lane0);
 
 // Pause between two polls of data that has not arrived: a workgroup that is done
@@ -877,7 +887,7 @@ __device__ __forceinline__ void gateup_items(const DecodeArgs& a, const Lds& s, 
       }
       const float pg = seg_sum(slot_dot<BITS>(G[j], D), g.Gh);
       const float pu = seg_sum(slot_dot<BITS>(U[j], D), g.Gh);
-      if (grp == 0 && row[j] < g.I) xput(hxv, hv[j] * g.I + row[j], silu(pg) * pu, epoch);
+      if (row[j] < g.I) xput_seg(hxv, grp, g.Gh, hv[j] * g.I + row[j], silu(pg) * pu, epoch);
     }
   }
 }
@@ -1089,7 +1099,7 @@ __device__ __forceinline__ void shared_from_regs(const DecodeArgs& a, const Lds&
       const float pg = seg_sum(slot_dot<BITS>(sp.g[j], D), g.Gh);
       const float pu = seg_sum(slot_dot<BITS>(sp.u[j], D), g.Gh);
       const int row = ((i & (g.nblk_gu - 1)) << g.lPh) + p;
-      if (grp == 0 && row < g.I) xput(hxv, (a.K + (i >> g.lnb)) * g.I + row, silu(pg) * pu, epoch);
+      if (row < g.I) xput_seg(hxv, grp, g.Gh, (a.K + (i >> g.lnb)) * g.I + row, silu(pg) * pu, epoch);
     }
   }
 }
