@@ -2031,27 +2031,39 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
   }
   Dig D;
   load_dig(D, s.xdig, s.xsum, lane);
+  // The gate/up loads go out in two halves. The CU's memory pipeline fills up with
+  // the first half of every wave's requests, and a wave that issues more then
+  // stalls until some drain; so the routing weights and the shared expert's item
+  // are computed between the halves, while the first half streams in.
+  constexpr int kFirst = kBatch / 2;
   Slot G[kBatch], U[kBatch];
   issue_order();
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) {
+  for (int j = 0; j < kFirst; ++j) {
     G[j] = ld_slot<BITS>(gb[j], lane, false);
     U[j] = ld_slot<BITS>(gb[j] + g.off_up, lane, false);
   }
   issue_order();
   // the routing weights and the LDS selection (read by the down jobs below and in
-  // phase C) while the gate/up loads are in flight
+  // phase C)
   spec_weights(a, s, t, l, my_idx, my_lg);
   const unsigned epoch = epoch_of(a, t, l);
   const Xv hxv = xv_h(a, epoch);
   {
-    // the shared expert's gate/up item of this wave (loaded in phase A) while the
-    // routed loads are in flight; one block of one row per item in this shape
+    // the shared expert's gate/up item of this wave (loaded in phase A); one block
+    // of one row per item in this shape
     static_assert(kSpecS * kSpecI / kSpecNwg == kNW, "four shared gate/up items per workgroup");
     const float pg = seg_sum(slot_dot<BITS>(sh.g, D), kWave);
     const float pu = seg_sum(slot_dot<BITS>(sh.u, D), kWave);
     if (lane < kRep) xput_rep(hxv, lane, kSpecK * g.I + blockIdx.x * kNW + w, silu(pg) * pu, epoch);
   }
+  issue_order();
+#pragma unroll
+  for (int j = kFirst; j < kBatch; ++j) {
+    G[j] = ld_slot<BITS>(gb[j], lane, false);
+    U[j] = ld_slot<BITS>(gb[j] + g.off_up, lane, false);
+  }
+  issue_order();
   float hj[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) {
