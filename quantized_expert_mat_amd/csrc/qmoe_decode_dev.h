@@ -5,7 +5,8 @@
 // One token through one layer is three phases; each depends on all of the
 // previous one:
 //   A  RMSNorm of x (every workgroup recomputes it from the 16 KB input), router
-//      logits (float32 mat-vec), shared expert gate/up + SwiGLU -> h_shared.
+//      logits (float32 mat-vec); the general kernel also reduces the shared
+//      expert's gate/up + SwiGLU -> h_shared here (the specialised one in B).
 //   B  top-K over the logits (every workgroup recomputes it from the logits),
 //      routed experts gate/up + SwiGLU -> h_k.
 //   C  down projections of the routed and shared experts, weighted combine and
@@ -41,8 +42,6 @@
 // instruction with exact int32 accumulation. One weight element then costs about
 // one VALU operation instead of two and a half for convert + FMA, which keeps the
 // 4-bit path under the HBM roofline instead of next to it.
-
-
 
 #include <hip/hip_ext.h>
 
