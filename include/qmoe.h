@@ -247,9 +247,11 @@ moe_status moe_stack_decode_streamed(const moe_config* cfg, int32_t L, const moe
  * device memory (code under stream capture, tight serving loops, harnesses that
  * forbid allocation). Its scratch space is a fixed 4 MiB array inside the
  * library, one per device, obtained once per device with hipGetSymbolAddress on
- * the first call there and held until the process ends; the call itself
- * allocates nothing, host or device. Same kernels, same results as
- * moe_stack_decode on the same inputs.
+ * the first call there and held until the process ends. Apart from the library's
+ * one-time per-device set-up (that address, the compute-unit count, the kernels'
+ * LDS limits and the ordering event, which any decode entry point creates on its
+ * first use of a device), a call allocates nothing, host or device. Same kernels,
+ * same results as moe_stack_decode on the same inputs.
  *   limits     L <= 128, and the shape's workspace without the streamed tier's
  *              tables must fit 4 MiB (hidden 4096, inter 1024, any K and E of
  *              the supported range: about 3 MiB); otherwise MOE_ERR_UNSUPPORTED
