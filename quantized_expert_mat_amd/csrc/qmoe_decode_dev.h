@@ -2222,9 +2222,16 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
     encode_vectors<false>(hs + K * I, a.S, I, 1.f, nullptr, s.hdig + K * Gi * kDigitStride,
                           s.hsum + 4 * K * Gi);
     __syncthreads();
-    down_from_regs<BITS, STREAM>(a, s, l, dp, a.npass_routed, a.npass);
+    // the routed h is requested before the shared pass, so its round trip overlaps
+    // that pass; whatever has not arrived by then is polled again
     const Xv rt{hv.base, K * I, hv.n_pad};
-    if (!wg_all(s.sm, xget<kSpecRtHPer>(a, rt, hs, epoch_of(a, t, l)))) return false;
+    static_assert(kSpecK * kSpecI / 2 == kThreads * kSpecRtHPer, "the routed h is one round of chunks");
+    v4u rtp[kSpecRtHPer];
+    issue_order();
+    xissue<kSpecRtHPer>(rt, 0, rtp);
+    issue_order();
+    down_from_regs<BITS, STREAM>(a, s, l, dp, a.npass_routed, a.npass);
+    if (!wg_all(s.sm, xwait<kSpecRtHPer>(a, rt, 0, hs, epoch_of(a, t, l), rtp))) return false;
     SUBSTAMP(13);
     encode_vectors<false>(hs, K, I, 1.f, nullptr, s.hdig, s.hsum);
     __syncthreads();
