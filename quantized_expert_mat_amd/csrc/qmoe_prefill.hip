@@ -486,14 +486,15 @@ __device__ inline bf16x8 deq_octet(const WFrag& f, int i) {
   } else if (BITS == 3) {
     // octets 0..3 come from dwords 0..2, octets 4..7 from dwords 3..5; the fourth
     // octet of each triple is gathered from the top bits of the three dwords
-    const unsigned w[6] = {f.c0[0], f.c0[1], f.c0[2], f.c0[3], f.c1[0], f.c1[1]};
+    // triple t is dwords 3t..3t+2 of the slot (c0[0..2] or c0[3], c1[0], c1[1]),
+    // picked by selects rather than an indexed array, which would live in scratch
     const int t = i >> 2, r = i & 3;
+    const unsigned w0 = t ? f.c0[3] : f.c0[0], w1 = t ? f.c1[0] : f.c0[1], w2 = t ? f.c1[1] : f.c0[2];
     unsigned d;
     if (r < 3) {
-      d = w[3 * t + r];
+      d = r == 0 ? w0 : r == 1 ? w1 : w2;
     } else {
-      d = ((w[3 * t] >> 3) & 0x11111111u) | ((w[3 * t + 1] >> 2) & 0x22222222u) |
-          ((w[3 * t + 2] >> 1) & 0x44444444u);
+      d = ((w0 >> 3) & 0x11111111u) | ((w1 >> 2) & 0x22222222u) | ((w2 >> 1) & 0x44444444u);
     }
     lo = opaque(d & 0x07070707u);
     hi = opaque((d >> 4) & 0x07070707u);
