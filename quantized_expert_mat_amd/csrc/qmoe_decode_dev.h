@@ -22,13 +22,18 @@
 // Cross-workgroup traffic. The 256 workgroups sit on 8 XCDs with separate L2
 // caches, and a grid-wide barrier costs several microseconds there. So there is
 // no barrier: every value one phase hands to the next (x, logits, h) is written
-// as an 8-byte (value, epoch) pair with a device-coherent store, in 8 replicas,
-// and each consumer polls exactly the values it needs until they carry the
-// current epoch. Weights never pass through LDS: they are requested into the
-// registers of the lanes that reduce them, as early as their addresses are known
-// (the next layer's router rows and shared-expert gate/up slots at the end of
-// phase C; the routed gate/up and down slots together once top-K is known), so
-// their latency overlaps the exchanges.
+// as an 8-byte (value, epoch) pair with a device-coherent store, in kRep
+// replicas stored by kRep lanes at once, and each consumer polls exactly the
+// values it needs until they carry the current epoch. Each exchanged vector has
+// two buffers chosen by the epoch's parity; a workgroup rewrites a buffer only
+// after its polls of the next epoch, to which every workgroup contributes, so no
+// slot is overwritten before every consumer has read it (the grid is sized so
+// that every workgroup publishes logits or h at every epoch).
+// Weights never pass through LDS: they are requested into the registers of the
+// lanes that reduce them, as early as their addresses are known, so that their
+// latency overlaps the exchanges. The vector-memory counter retires loads and
+// stores in issue order, and a wave that issues into a full memory pipeline
+// stalls; where a poll, a store or a load is issued is chosen with both in mind.
 //
 // Dequant mat-vec. The page rewrites (nibble*scale + bias)*x as
 // fma(nibble, scale*x, bias*x) ("Kernel dequant tối ưu FMA"). Carried one step

@@ -17,7 +17,7 @@ constexpr int kMaxShared = 2;
 constexpr int kMaxDim = 4096;
 constexpr int kMaxNwg = 1024;     // workgroups a decode launch may use
 constexpr int kMaxCacheSlots = 64;  // HBM expert-cache slots per layer (streamed stack)
-constexpr int kRep = 8;           // replicas of every exchanged vector (spreads polling)
+constexpr int kRep = 4;           // replicas of every exchanged vector (spreads polling)
 constexpr int kDigitStride = 52;  // dwords per (vector, group) in LDS: 48 digit dwords + pad
 
 // ---------------------------------------------------------------------------
