@@ -940,10 +940,12 @@ __device__ __forceinline__ void router_rows(const DecodeArgs& a, const Lds& s, i
 // ------------------------------------------------------------ register prefetch
 // Weights a phase needs are requested early, into the registers of the lanes that
 // will consume them, so their HBM latency overlaps an exchange wait instead of
-// following it: the next layer's router rows and shared gate/up slots right after
-// this layer's combine (they land while x is being exchanged), and the down slots
-// of phase C right after the routed gate/up loads of phase B (they land while h
-// is being exchanged). Plain loads keep the compiler's wait counts exact.
+// following it: the next layer's router rows right after this layer's combine
+// (they land while x is being exchanged; the general kernel also takes its shared
+// gate/up slots there, the specialised one right after the x poll), and the down
+// slots of phase C at the end of phase B (they land while h is being exchanged;
+// the specialised kernel takes the shared expert's down slot in phase A). Plain
+// loads keep the compiler's wait counts exact.
 constexpr int kRouterPre = 8;  // float4 of router rows per thread
 constexpr int kRowsPre = 4;    // router rows per workgroup on the prefetch path
 constexpr int kShPre = 1;      // shared gate/up items per wave
@@ -987,8 +989,10 @@ struct DownPre {
   v4u shp[kSpecShHPer];  // specialised kernel: the shared expert's h, requested at the end of phase B
 };
 
-// Router rows of this workgroup (float4 q = tid + kThreads*i of rows [e0, e1)) and
-// its shared gate/up items (item i0 + w + kNW*j on wave w) for layer l.
+// Router rows of this workgroup (float4 q = tid + kThreads*i of rows [e0, e1)) and,
+// in the general kernel, its shared gate/up items (item i0 + w + kNW*j on wave w)
+// for layer l. The specialised kernel takes its share of the two router rows (and
+// of the shared-expert gate); its shared gate/up items are requested in phase A.
 template <int BITS, bool SPEC = false>
 __device__ __forceinline__ void load_static(const DecodeArgs& a, const Lds& s, int l, StaticPre& sp) {
   const Geo& g = a.geo;
@@ -2008,13 +2012,13 @@ __device__ __forceinline__ void down_from_regs(const DecodeArgs& a, const Lds& s
 
 // Phase B of the specialised kernel (hidden 4096, inter 1024, K 4, 256 workgroups):
 // a workgroup owns kNW*kBatch consecutive gate/up rows of one routed expert, so
-// each wave has exactly one batch. Every address (gate/up rows and the phase-C down
-// slots) is formed from LDS first; the gate/up loads go out in one straight run,
-// with no branch or LDS read between them that would make the compiler wait for
-// the loads already issued. The down slots are requested after the gate/up dot
-// products: phase B then moves only the gate/up bytes, and the down slots land
-// while h is being exchanged (measured 2% faster than requesting them with the
-// gate/up slots).
+// each wave has exactly one batch. Every address is formed from LDS first; the
+// gate/up loads go out in two straight runs (no branch or LDS read among them
+// that would make the compiler wait for the loads already issued), with the
+// routing weights and the shared item computed between them. The routed down
+// slots are requested after the gate/up dot products: phase B then moves only the
+// gate/up bytes, and the down slots land while h is being exchanged (measured 2%
+// faster than requesting them with the gate/up slots).
 static_assert(kSpecK * kSpecI / kSpecNwg == kNW * kBatch, "one batch per wave");
 static_assert(kSpecI % (kNW * kBatch) == 0, "a workgroup's rows lie in one expert");
 template <int BITS>
@@ -2111,8 +2115,9 @@ __device__ __forceinline__ void gateup_down_spec(const DecodeArgs& a, const Lds&
   issue_order();
 }
 
-// Phase B of the specialised kernel: top-K on wave 0 (the ok flag is 1 here: phase
-// A's barrier checked it), then the gate/up work of the routed and shared experts.
+// Phase B of the specialised kernel: top-K on all four waves (the ok flag is 1
+// here: phase A's barrier checked it), then the gate/up work of the routed and
+// shared experts.
 template <int BITS>
 __device__ __forceinline__ bool phase_b_spec(const DecodeArgs& a, const Lds& s, int t, int l, DownPre& dp,
                                              const SharedSpec& sh) {
