@@ -52,3 +52,13 @@ def test_noalloc_matches_workspace_call_twice_second_smaller():
     small = wl.WorkloadConfig(name="small", hidden=512, inter=128, n_experts=24, top_k=4, n_shared=1,
                               n_layers=2, n_tokens=3)
     run_both(small, 2, 3, 1)
+
+
+def test_noalloc_layer_table_past_the_launch_arguments():
+    """70 layers: the first 64 layer-table entries travel in the launch arguments,
+    the rest are written into the scratch array by a second kernel; the result is
+    the workspace call's, bit for bit."""
+    print("noalloc: 70 small layers, T=2", flush=True)
+    w = wl.WorkloadConfig(name="small70", hidden=256, inter=128, n_experts=16, top_k=2, n_shared=1,
+                          n_layers=70, n_tokens=2)
+    run_both(w, 70, 2, 2)
