@@ -118,6 +118,22 @@ def test_streamed_full_layer_shape():
     check_against_oracle(w, hls, x, mask, yh, ih, hh, 8)
 
 
+def test_streamed_full_shape_zero_mean():
+    """The host-memory tier on zero-mean weights, where routing stays token-dependent
+    (the regime of the 27% repeats): three full-shape layers x 4 tokens with the
+    tier, outputs, sets and the per-expert hit pattern against the oracle."""
+    w = wl.STACK60_4BIT_ZM.replace(name="streamed-zm", n_layers=3, n_tokens=4)
+    dls = [DeviceLayer(w, l, chunk=8) for l in range(w.n_layers)]
+    hls = [DeviceCanonicalLayer(w, l) for l in range(w.n_layers)]
+    x = wl.tokens_x(w.seed + 1000, w.n_tokens, w.hidden)
+    mask = wl.boost_mask(w.seed + 7, w.n_tokens, w.n_layers, w.top_k, w.temporal_p)
+    yh, ih, hh = run_streamed(w, dls, x, mask, w.top_k)
+    n_hits = check_against_oracle(w, hls, x, mask, yh, ih, hh, w.top_k)
+    # with C = K a hit is exactly a repeat from the token before; every promoted
+    # expert repeats, so there are at least as many hits as promoted slots
+    assert n_hits >= int(mask[1:].astype(bool).sum())
+
+
 def test_streamed_rejects_pageable_experts():
     w = small(n_layers=1, n_tokens=1)
     d = DeviceLayer(w, 0)
