@@ -54,11 +54,13 @@ def _check_layers_visible(deltas, y_final, what):
         assert d >= 10 * bar, f"{what}: token {t} layer {l}: max|delta| {d:.3e} < 10 x {bar:.3e}"
 
 
-def test_stack_zero_mean_8_layers_full_shape():
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_stack_zero_mean_8_layers_full_shape(bits):
     """The specialised kernel (the benchmark's launch configuration) over 8 layers x 4
-    tokens with the temporal tier: outputs and every layer's expert set against the
-    oracle, every layer visible above the tolerance."""
-    w = wl.STACK60_4BIT_ZM.replace(n_layers=8, n_tokens=4)
+    tokens with the temporal tier, at each code width: outputs and every layer's
+    expert set against the oracle, every layer visible above the tolerance."""
+    base = {4: wl.STACK60_4BIT, 3: wl.STACK60_3BIT, 2: wl.STACK60_2BIT}[bits]
+    w = base.replace(name=base.name + "-zero-mean", zero_mean=True, n_layers=8, n_tokens=4)
     L, T, K = w.n_layers, w.n_tokens, w.top_k
     cfg = config_for(w)
     dls = [DeviceLayer(w, l, chunk=8) for l in range(L)]
