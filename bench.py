@@ -17,7 +17,7 @@ kernel's algorithmic bytes (weights touched per token, the per-token figure
 below) against MI355X's 8 TB/s HBM; `cpu_baseline` is the CPU oracle timed on
 a bounded sample (the first tokens through all layers) and scaled to tokens/s.
 `launch_ms` gives the mean, median and range of the per-launch HIP-event times
-and `device` the device name and compute-unit count.
+and `device` the device name, architecture and compute-unit count.
 
 Other workloads (`--workload`): `prefill` (1155 tokens through one layer as an
 expert-grouped bf16 GEMM) and `streamed` (the stack with every layer's routed
@@ -851,7 +851,8 @@ def main():
         "effective_hbm_gbs": round(ptb * tok_s / 1e9, 1),
         "launch_ms": {"mean": round(avg_launch_s * 1e3, 3), "median": round(float(np.median(launch_ms)), 3),
                       "min": round(min(launch_ms), 3), "max": round(max(launch_ms), 3)},
-        "device": {"name": props.name, "compute_units": props.multi_processor_count},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                   "compute_units": props.multi_processor_count},
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(out), flush=True)
