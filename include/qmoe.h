@@ -66,7 +66,8 @@ typedef enum {
 #define MOE_F_RESIDUAL 2       /* add the (pre-norm) input x to the output */
 #define MOE_F_SELECT_BY_BIAS 4 /* selection score = sel_bias alone (else logit + sel_bias) */
 #define MOE_F_PREFILL_BF16 8   /* moe_layer_forward: bf16 expert-grouped GEMM path */
-#define MOE_F_PHASED 16        /* decode: one kernel launch per phase (no grid barrier) */
+#define MOE_F_PHASED 16        /* decode: one kernel launch per phase and layer instead of the
+                                  persistent grid (kernel boundaries order the phases) */
 
 typedef struct {
   int32_t hidden;    /* H: model width (gate/up input, down output) */
