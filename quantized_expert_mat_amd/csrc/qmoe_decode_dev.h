@@ -2526,7 +2526,6 @@ constexpr int kQkvB = 4;  // blocks per wave in flight together
 
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void qkv_kernel(QkvArgs a) {
-  __shared__ __align__(16) float xn[kMaxDim];
   __shared__ __align__(16) unsigned dig[(kMaxDim / kGroup) * kDigitStride];
   __shared__ __align__(16) float sums[4 * (kMaxDim / kGroup)];
   __shared__ float red[kNW];
@@ -2544,28 +2543,48 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(QkvArgs a) {
 #pragma unroll
     for (int j = 0; j < kQkvB; ++j) S[j] = ld_slot<BITS>(blk_of(b0 + w + j * kNW), lane, false);
     issue_order();
+    // thread t holds chunks t and t + kThreads of 8 input values (the chunks that
+    // encode_chunk8 takes from it), with their gamma, both requested together
     const float* xt = a.x + (size_t)t * H;
-    float ss = 0.f;
-    for (int i = threadIdx.x * 4; i < H; i += kThreads * 4) {
-      const float4 v = *reinterpret_cast<const float4*>(xt + i);
-      *reinterpret_cast<float4*>(xn + i) = v;
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    const int nch = H / 8;
+    float v[16], gm[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = h * kThreads + (int)threadIdx.x;
+      float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0, g0 = make_float4(1.f, 1.f, 1.f, 1.f), g1 = g0;
+      if (c < nch) {
+        v0 = ldg_f4(xt + 8 * c);
+        v1 = ldg_f4(xt + 8 * c + 4);
+        if (a.gamma) {
+          g0 = ldg_f4(a.gamma + 8 * c);
+          g1 = ldg_f4(a.gamma + 8 * c + 4);
+        }
+      }
+      v[8 * h] = v0.x; v[8 * h + 1] = v0.y; v[8 * h + 2] = v0.z; v[8 * h + 3] = v0.w;
+      v[8 * h + 4] = v1.x; v[8 * h + 5] = v1.y; v[8 * h + 6] = v1.z; v[8 * h + 7] = v1.w;
+      gm[8 * h] = g0.x; gm[8 * h + 1] = g0.y; gm[8 * h + 2] = g0.z; gm[8 * h + 3] = g0.w;
+      gm[8 * h + 4] = g1.x; gm[8 * h + 5] = g1.y; gm[8 * h + 6] = g1.z; gm[8 * h + 7] = g1.w;
     }
-    if (a.norm) {
-      ss = wave_sum(ss);
-      if (lane == 0) red[w] = ss;
-    }
-    __syncthreads();
     float rinv = 1.f;
     if (a.norm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = fmaf(v[i], v[i], ss);
+      ss = wave_sum(ss);
+      if (lane == 0) red[w] = ss;
+      __syncthreads();
       ss = 0.f;
       for (int i = 0; i < kNW; ++i) ss += red[i];
       rinv = 1.f / sqrtf(ss / (float)H + a.eps);
     }
-    if (a.norm || a.gamma)
-      encode_vectors<true>(xn, 1, H, rinv, a.gamma, dig, sums);
-    else
-      encode_vectors<false>(xn, 1, H, 1.f, nullptr, dig, sums);
+    // x_n = (x * gamma) * rinv, then its digits
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (v[i] * gm[i]) * rinv;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = h * kThreads + (int)threadIdx.x;
+      encode_chunk8(v + 8 * h, dig, sums, c / 8, c % 8, c < nch);
+    }
     __syncthreads();
     Dig D;
     load_dig(D, dig, sums, grp);
