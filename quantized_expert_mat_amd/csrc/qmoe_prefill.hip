@@ -260,6 +260,18 @@ __global__ __launch_bounds__(256) void select_kernel(PArgs a) {
     }
     bst[j] = b;
   }
+  // selection by sel_bias: the router logits of the selected experts are formed
+  // here; x_n is requested now, under the selection
+  constexpr int kIt = kMaxDim / 256;  // float4 of a row per lane
+  float4 xv[kIt];
+  if (by_sel) {
+    const float* xr = a.xn + (size_t)t * a.H;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int h = lane * 4 + it * 256;
+      xv[it] = h < a.H ? *reinterpret_cast<const float4*>(xr + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
   constexpr int kPer = kMaxE / 64;
   unsigned long long key[kPer];
   for (int i = 0; i < kPer; ++i) {
@@ -290,23 +302,39 @@ __global__ __launch_bounds__(256) void select_kernel(PArgs a) {
     sel[k] = e;
     for (int i = 0; i < kPer; ++i) key[i] = key[i] == m ? 0ull : key[i];
   }
-  // router logits of the selected experts
+  // router logits of the selected experts. By sel_bias: each selected row is
+  // requested whole, the next one while the current one is reduced (one round trip
+  // per row, overlapped); the products run in the same order as a plain loop over h.
   float lg[kMaxK];
-  for (int k = 0; k < kMaxK; ++k) {
-    lg[k] = 0.f;
-    if (k >= a.K) continue;
-    if (!by_sel) {
-      lg[k] = a.logits[(size_t)t * a.E + sel[k]];
-    } else {
-      const float* wr = a.router + (size_t)sel[k] * a.H;
-      const float* xr = a.xn + (size_t)t * a.H;
-      float s = 0.f;
-      for (int h = lane * 4; h < a.H; h += 256) {
-        const float4 w = *reinterpret_cast<const float4*>(wr + h);
-        const float4 v = *reinterpret_cast<const float4*>(xr + h);
-        s = fmaf(w.x, v.x, s); s = fmaf(w.y, v.y, s); s = fmaf(w.z, v.z, s); s = fmaf(w.w, v.w, s);
+  if (!by_sel) {
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) lg[k] = k < a.K ? a.logits[(size_t)t * a.E + sel[k]] : 0.f;
+  } else {
+    float4 wa[kIt], wb[kIt];
+    auto load_row = [&](float4 (&w)[kIt], int e) {
+      const float* wr = a.router + (size_t)e * a.H;
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int h = lane * 4 + it * 256;
+        w[it] = h < a.H ? *reinterpret_cast<const float4*>(wr + h) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      lg[k] = wave_sum_f(s);
+    };
+    load_row(wa, sel[0]);
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      float4(&cur)[kIt] = (k & 1) ? wb : wa;
+      float4(&nxt)[kIt] = (k & 1) ? wa : wb;
+      if (k + 1 < a.K) load_row(nxt, sel[k + 1]);
+      lg[k] = 0.f;
+      if (k < a.K) {
+        float s = 0.f;
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+          const float4 w = cur[it], v = xv[it];
+          s = fmaf(w.x, v.x, s); s = fmaf(w.y, v.y, s); s = fmaf(w.z, v.z, s); s = fmaf(w.w, v.w, s);
+        }
+        lg[k] = wave_sum_f(s);
+      }
     }
   }
   float mx = lg[0];
