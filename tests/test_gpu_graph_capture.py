@@ -1,6 +1,7 @@
 """Entry points captured into a HIP graph (torch.cuda.CUDAGraph) and replayed: the
-resident stack (with a workspace and allocation-free), the single-layer decode
-call, the 1155-token prefill and the fused Q/K/V projection. Every replay, with
+resident stack (with a workspace and allocation-free), the streamed stack (routed
+experts in pinned host memory), the single-layer decode call, the 1155-token
+prefill and the fused Q/K/V projection. Every replay, with
 eager work and a synchronisation between replays, gives the eager call's outputs
 bit for bit, including after the input buffer is rewritten between replays. The
 weight memory stays alive while a graph may replay (a capture made with torch
@@ -199,3 +200,34 @@ def test_qkv_graph_replays():
         q.moe_qkv_forward(cfg, packed, T, xin, *outs, gamma=gamma, stream=s)
 
     graph_vs_eager("qkv", run, xin, xs, outs)
+
+
+def test_streamed_stack_graph_replays():
+    w = wl.WorkloadConfig(name="small-streamed", hidden=512, inter=128, n_experts=16, top_k=4, n_shared=1,
+                          n_layers=3, n_tokens=8, temporal_p=0.27)
+    L, T, K, C = w.n_layers, w.n_tokens, w.top_k, 6
+    cfg = config_for(w)
+    dls = [DeviceLayer(w, l) for l in range(L)]
+    pins, lws = [], []
+    for d in dls:
+        h = torch.empty(d.experts.numel(), dtype=torch.uint8, pin_memory=True)
+        h.copy_(d.experts)
+        pins.append(h)
+        lws.append(q.layer_weights(h, d.shared, d.router))
+    torch.cuda.synchronize()
+    cache = torch.empty(L * C * q.moe_packed_expert_bytes(cfg), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(q.moe_workspace_bytes(cfg, T, L), dtype=torch.uint8, device="cuda")
+    mask = torch.from_numpy(wl.boost_mask(w.seed + 7, T, L, K, 0.27)).cuda()
+    xs = [torch.from_numpy(wl.tokens_x(w.seed + 400 + i, T, w.hidden)).cuda() for i in range(2)]
+    xin = xs[0].clone()
+    y = torch.empty_like(xin)
+    idx = torch.empty((T, L, K), dtype=torch.int32, device="cuda")
+    hit = torch.empty((T, L, K), dtype=torch.uint8, device="cuda")
+
+    def run(s):
+        q.moe_stack_decode_streamed(cfg, lws, T, xin, y, ws, cache, C, boost_mask=mask, idx_trace=idx,
+                                    hit_trace=hit, stream=s)
+
+    graph_vs_eager("streamed stack", run, xin, xs, [y, idx, hit])
+    q.moe_device_status(ws)
+    del pins
