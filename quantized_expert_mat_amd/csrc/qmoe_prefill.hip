@@ -495,22 +495,31 @@ struct WFrag {
   unsigned sb;   // (the packed slot's six dwords); 2-bit: c0 holds all 64
 };
 
-// Hides a value's known bits from the optimiser so that byte-to-float conversions
-// of masked code bytes stay single v_cvt_f32_ubyteN instructions.
-__device__ inline unsigned opaque(unsigned v) {
-  asm("" : "+v"(v));
-  return v;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+// q*s + b rounded once to float32, for the code q in the low bits of one 16-bit
+// half of m (the other bits of that half zero). The half read as a float16 is the
+// denormal q * 2^-24, which converts exactly, and s24 = s * 2^24, so the fused
+// product is q*s exactly and the fma rounds the exact q*s + b once: the same value
+// as fmaf((float)q, s, b). One v_fma_mix_f32 per weight instead of a byte-to-float
+// conversion and an fma. (Exact while |s| < 2^104, where s * 2^24 is finite.)
+__device__ inline float deq_lo(unsigned m, float s24, float b) {
+  return fmaf((float)__builtin_bit_cast(f16x2, m)[0], s24, b);
+}
+__device__ inline float deq_hi(unsigned m, float s24, float b) {
+  return fmaf((float)__builtin_bit_cast(f16x2, m)[1], s24, b);
 }
 
-// bf16(q*s + b) for the 8 codes of octet i of a group, in reduction order.
-// q*s is exact in float32, so the fma rounds the exact q*s + b once.
+// bf16(q*s + b) for the 8 codes of octet i of a group, in reduction order. The
+// octet's codes sit in one dword d as two interleaved sets of four byte lanes:
+// element j < 4 in bits [8j, 8j + bits), element 4 + j in bits [8j + 4, 8j + 4 + bits).
+// Masking d (and d shifted by 4, 8 and 12) with one bits-wide field per 16-bit half
+// leaves two codes per dword, one per half, for deq_lo / deq_hi.
 template <int BITS>
 __device__ inline bf16x8 deq_octet(const WFrag& f, int i) {
-  unsigned lo, hi;
+  unsigned d;
   if (BITS == 4) {
-    const unsigned d = (i < 4 ? f.c0[i & 3] : f.c1[i & 3]) ^ 0x88888888u;  // stored q ^ 8
-    lo = opaque(d & 0x0F0F0F0Fu);
-    hi = opaque((d >> 4) & 0x0F0F0F0Fu);
+    d = i < 4 ? f.c0[i & 3] : f.c1[i & 3];  // stored q ^ 8, flipped back per field below
   } else if (BITS == 3) {
     // octets 0..3 come from dwords 0..2, octets 4..7 from dwords 3..5; the fourth
     // octet of each triple is gathered from the top bits of the three dwords
@@ -518,29 +527,25 @@ __device__ inline bf16x8 deq_octet(const WFrag& f, int i) {
     // picked by selects rather than an indexed array, which would live in scratch
     const int t = i >> 2, r = i & 3;
     const unsigned w0 = t ? f.c0[3] : f.c0[0], w1 = t ? f.c1[0] : f.c0[1], w2 = t ? f.c1[1] : f.c0[2];
-    unsigned d;
     if (r < 3) {
       d = r == 0 ? w0 : r == 1 ? w1 : w2;
     } else {
       d = ((w0 >> 3) & 0x11111111u) | ((w1 >> 2) & 0x22222222u) | ((w2 >> 1) & 0x44444444u);
     }
-    lo = opaque(d & 0x07070707u);
-    hi = opaque((d >> 4) & 0x07070707u);
   } else {
-    const unsigned d = f.c0[i >> 1] >> (2 * (i & 1));
-    lo = opaque(d & 0x03030303u);
-    hi = opaque((d >> 4) & 0x03030303u);
+    d = f.c0[i >> 1] >> (2 * (i & 1));
   }
-  const float s = bf16lo_to_f32(f.sb), b = bf16hi_to_f32(f.sb);
-  const float w0 = fmaf((float)(lo & 0xFFu), s, b);
-  const float w1 = fmaf((float)((lo >> 8) & 0xFFu), s, b);
-  const float w2 = fmaf((float)((lo >> 16) & 0xFFu), s, b);
-  const float w3 = fmaf((float)(lo >> 24), s, b);
-  const float w4 = fmaf((float)(hi & 0xFFu), s, b);
-  const float w5 = fmaf((float)((hi >> 8) & 0xFFu), s, b);
-  const float w6 = fmaf((float)((hi >> 16) & 0xFFu), s, b);
-  const float w7 = fmaf((float)(hi >> 24), s, b);
-  u32x4 r = {pack_bf16(w0, w1), pack_bf16(w2, w3), pack_bf16(w4, w5), pack_bf16(w6, w7)};
+  constexpr unsigned kM = ((1u << BITS) - 1u) * 0x00010001u;  // one field per half
+  constexpr unsigned kX = BITS == 4 ? 0x00080008u : 0u;        // 4-bit codes are stored as q ^ 8
+  const unsigned m02 = (d & kM) ^ kX;          // elements 0 (low half) and 2 (high half)
+  const unsigned m13 = ((d >> 8) & kM) ^ kX;   // elements 1 and 3
+  const unsigned m46 = ((d >> 4) & kM) ^ kX;   // elements 4 and 6
+  const unsigned m57 = ((d >> 12) & kM) ^ kX;  // elements 5 and 7
+  const float s24 = bf16lo_to_f32(f.sb) * 16777216.0f, b = bf16hi_to_f32(f.sb);
+  u32x4 r = {pack_bf16(deq_lo(m02, s24, b), deq_lo(m13, s24, b)),
+             pack_bf16(deq_hi(m02, s24, b), deq_hi(m13, s24, b)),
+             pack_bf16(deq_lo(m46, s24, b), deq_lo(m57, s24, b)),
+             pack_bf16(deq_hi(m46, s24, b), deq_hi(m57, s24, b))};
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -561,13 +566,14 @@ __device__ inline const uint8_t* expert_base(const PArgs& a, int e) {
 }
 
 // One work item as seen by one lane. Chunk ch of a lane's weight row starts 64*ch
-// bytes after wc (code plane 0; plane 1 of 4-bit codes is 1024 bytes further), 32*ch
-// bytes after wc1 (plane 1 of 3-bit codes) and 4*ch words after wsb ((scale, bias)).
+// bytes after wc (code plane 0; plane 1 of 4-bit codes is 1024 bytes further) and
+// 32*ch bytes after wc1 (plane 1 of 3-bit codes); the row's (scale, bias) words,
+// one per 64-group, start at wsb.
 struct Job {
-  int row0, nrows, K, nch;
+  int row0, nrows, K, nch, G;
   const uint8_t* wc[2];    // codes of chunk 0 of this lane's row in each set
   const uint8_t* wc1[2];   // 3-bit: second code plane of chunk 0
-  const unsigned* wsb[2];  // (scale, bias) word of chunk 0
+  const unsigned* wsb[2];  // (scale, bias) word of group 0 of this lane's row
   unsigned sbmask;         // 0 where the lane's group lies beyond K (K < 256)
   int col[2];              // output column of this lane in each set
   bool on[2];              // the set has columns (wave-uniform)
@@ -581,7 +587,7 @@ __device__ inline void job_row(const Geo& g, const uint8_t* mat, int row, int P,
   const int slot = (row % P) * G + grp;
   wc = blk + slot * 16;
   wc1 = blk + kPlane1Offset + slot * 8;
-  wsb = reinterpret_cast<const unsigned*>(blk + sb_offset(BITS)) + slot;
+  wsb = reinterpret_cast<const unsigned*>(blk + sb_offset(BITS)) + (row % P) * G;
 }
 
 template <int BITS, bool DOWN>
@@ -600,6 +606,7 @@ __device__ inline bool make_job(const PArgs& a, const int4* list, Job& jb) {
   jb.K = DOWN ? a.I : a.H;
   jb.nch = (jb.K + kKC2 - 1) / kKC2;
   const int G = DOWN ? g.Gi : g.Gh;
+  jb.G = G;
   jb.sbmask = kk < G ? 0xFFFFFFFFu : 0u;
   if (!DOWN) {
     const int j = nt * kGuCols + wave * 16 + (lane & 15);
@@ -639,8 +646,47 @@ __device__ inline void load_wpair(const Job& jb, int ch, WFrag& f0, WFrag& f1) {
     f0.c1 = u32x4{0u, 0u, 0u, 0u};
     f1.c1 = u32x4{0u, 0u, 0u, 0u};
   }
-  f0.sb = jb.wsb[0][4 * ch];  // masked by the consumer: arithmetic on a prefetched
-  f1.sb = jb.wsb[1][4 * ch];  // value here would make the compiler wait for it early
+}
+
+// (scale, bias) words. A chunk needs one word per lane (its group of the chunk), but
+// one dword load per chunk spends a memory request on 16 bytes of each row, a third
+// of the requests of the whole weight stream. So they are loaded four chunks at a
+// time: for the block of chunks 4q..4q+3, lane (kk, m) loads the 16 bytes of chunk
+// 4q + kk of its row m (all four groups of that chunk), the wave writes the 4 x 4
+// words of each row to its own LDS area, and at chunk 4q + j lane (kk, m) reads
+// word kk of the piece that lane (j, m) loaded. Chunks past the last are clamped
+// (in-bounds loads of values never used). A row of fewer than four groups (K < 256,
+// a single chunk) loads its words one by one, clamped to the row.
+__device__ inline u32x4 load_sbpiece(const Job& jb, int q, int set) {
+  const unsigned* row = set ? jb.wsb[1] : jb.wsb[0];
+  if (jb.G >= 4) {
+    int c = 4 * q + ((threadIdx.x & 63) >> 4);
+    c = c < jb.nch ? c : jb.nch - 1;
+    return *reinterpret_cast<const u32x4*>(row + 4 * c);
+  }
+  u32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = row[e < jb.G ? e : 0];
+  return v;
+}
+
+// Each wave owns 4 KB of LDS: two areas (blocks q even / odd), each with 1 KB per
+// set. Block q is stored one set at a time during chunks 4q - 2 and 4q - 1, while
+// the other area still serves block q - 1; the workgroup barrier at the start of
+// every chunk orders a block's stores before the reads of its first chunk.
+__device__ inline uint8_t* sb_area(uint8_t* lds_sb, int q, int set) {
+  return lds_sb + (threadIdx.x >> 6) * 4096 + (q & 1) * 2048 + set * 1024;
+}
+
+__device__ inline void store_sbpiece(uint8_t* lds_sb, int q, int set, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(sb_area(lds_sb, q, set) + (threadIdx.x & 63) * 16) = v;
+}
+
+__device__ inline void read_sb(uint8_t* lds_sb, int ch, unsigned& sb0, unsigned& sb1) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t* r = sb_area(lds_sb, ch >> 2, 0) + ((ch & 3) * 16 + (lane & 15)) * 16 + (lane >> 4) * 4;
+  sb0 = *reinterpret_cast<const unsigned*>(r);
+  sb1 = *reinterpret_cast<const unsigned*>(r + 1024);
 }
 
 template <bool DOWN>
@@ -729,19 +775,33 @@ __global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
   }
   // activations: LDS stage ch & 1 holds chunk ch, chunk ch + 1 is in registers;
   // weights: chunks ch and ch + 1 in registers, ch + 2 requested during chunk ch
+  uint8_t* lds_sb = lds + 2 * MT * kSubBytes;
   AStage<MT> st;
   WFrag p0, p1, r0, r1;
   load_achunk<MT>(st, rowp, 0, jb.K, mt_valid);
-  load_wpair<BITS>(jb, 0, p0, p1);
-  load_wpair<BITS>(jb, 1, r0, r1);
+  {
+    const u32x4 v0 = load_sbpiece(jb, 0, 0), v1 = load_sbpiece(jb, 0, 1);
+    load_wpair<BITS>(jb, 0, p0, p1);
+    load_wpair<BITS>(jb, 1, r0, r1);
+    store_sbpiece(lds_sb, 0, 0, v0);
+    store_sbpiece(lds_sb, 0, 1, v1);
+  }
   store_achunk<MT>(st, lds, mt_valid);
 
   auto chunk = [&](int ch, WFrag& f0, WFrag& f1) {
     const uint8_t* cur = lds + (ch & 1) * (MT * kSubBytes);
     uint8_t* nxt = lds + ((ch + 1) & 1) * (MT * kSubBytes);
     __syncthreads();  // stage cur is written; stage nxt is no longer read
-    if (ch + 1 < nch) load_achunk<MT>(st, rowp, ch + 1, jb.K, mt_valid);
     WFrag c0 = f0, c1 = f1;
+    read_sb(lds_sb, ch, c0.sb, c1.sb);
+    if (ch + 1 < nch) load_achunk<MT>(st, rowp, ch + 1, jb.K, mt_valid);
+    // one set of the next block's (scale, bias) words: set 0 during chunk 4q - 2,
+    // set 1 during chunk 4q - 1
+    const int bset = ((ch + 2) & 3) == 0 ? 0 : 1;
+    const int bq = (ch + 2 - bset) >> 2;
+    const bool bnext = ((ch + 2 - bset) & 3) == 0 && 4 * bq < nch;
+    u32x4 sbv;
+    if (bnext) sbv = load_sbpiece(jb, bq, bset);
     load_wpair<BITS>(jb, ch + 2, f0, f1);
     c0.sb &= jb.sbmask;
     c1.sb &= jb.sbmask;
@@ -759,6 +819,7 @@ __global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
       }
     }
     if (ch + 1 < nch) store_achunk<MT>(st, nxt, mt_valid);
+    if (bnext) store_sbpiece(lds_sb, bq, bset, sbv);
   };
   for (int ch = 0; ch < nch; ch += 2) {
     chunk(ch, p0, p1);
@@ -811,10 +872,24 @@ __global__ void clear_err(unsigned* err) {
 
 dim3 xcd_grid(int items) { return dim3((unsigned)(8 * ((items + 7) / 8))); }
 
+// Dynamic LDS of a GEMM workgroup: two activation stages, then each wave's 4 KB of
+// (scale, bias) areas. The thick tiles' 80 KB exceed the default 64 KB limit.
+constexpr size_t kLdsThin = 2 * kSubBytes + 16384, kLdsThick = 2 * kThickMT * kSubBytes + 16384;
+
+template <int BITS>
+hipError_t gemm_lds_attrs() {
+  hipError_t e = hipSuccess;
+  const void* k[2] = {reinterpret_cast<const void*>(&gemm_grouped<BITS, false, kThickMT>),
+                      reinterpret_cast<const void*>(&gemm_grouped<BITS, true, kThickMT>)};
+  for (int i = 0; i < 2 && e == hipSuccess; ++i)
+    e = hipFuncSetAttribute(k[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsThick);
+  return e;
+}
+
 // The gate/up and down passes, thin (one m-tile) and thick (kThickMT m-tiles) items.
 template <int BITS>
 void launch_gemms(const PArgs& a, int thin_max, int thick_max, int nt_gu, int nt_dn, hipStream_t stream) {
-  const size_t lds_thin = 2 * kSubBytes, lds_thick = 2 * kThickMT * kSubBytes;
+  const size_t lds_thin = kLdsThin, lds_thick = kLdsThick;
   hipLaunchKernelGGL((gemm_grouped<BITS, false, 1>), xcd_grid(thin_max * nt_gu), dim3(256), lds_thin, stream, a);
   if (thick_max > 0)
     hipLaunchKernelGGL((gemm_grouped<BITS, false, kThickMT>), xcd_grid(thick_max * nt_gu), dim3(256), lds_thick,
@@ -871,6 +946,9 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&group_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)group_lds_max);
+    if (e == hipSuccess) e = gemm_lds_attrs<2>();
+    if (e == hipSuccess) e = gemm_lds_attrs<3>();
+    if (e == hipSuccess) e = gemm_lds_attrs<4>();
     if (e != hipSuccess) {
       *msg = std::string("hipFuncSetAttribute: ") + hipGetErrorString(e);
       return MOE_ERR_HIP;
