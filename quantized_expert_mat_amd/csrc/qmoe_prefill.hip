@@ -497,24 +497,26 @@ struct WFrag {
 
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
-// q*s + b rounded once to float32, for the code q in the low bits of one 16-bit
-// half of m (the other bits of that half zero). The half read as a float16 is the
-// denormal q * 2^-24, which converts exactly, and s24 = s * 2^24, so the fused
+// q*s + b rounded once to float32, for a code q held in one 16-bit half of m as a
+// field at bit 0 or bit 4 of that half (the half's other bits zero). The half read
+// as a float16 is the denormal q * 2^-24 (field at bit 0) or q * 2^-20 (bit 4),
+// which converts exactly, and sc is s * 2^24 or s * 2^20 to match, so the fused
 // product is q*s exactly and the fma rounds the exact q*s + b once: the same value
 // as fmaf((float)q, s, b). One v_fma_mix_f32 per weight instead of a byte-to-float
 // conversion and an fma. (Exact while |s| < 2^104, where s * 2^24 is finite.)
-__device__ inline float deq_lo(unsigned m, float s24, float b) {
-  return fmaf((float)__builtin_bit_cast(f16x2, m)[0], s24, b);
+__device__ inline float deq_lo(unsigned m, float sc, float b) {
+  return fmaf((float)__builtin_bit_cast(f16x2, m)[0], sc, b);
 }
-__device__ inline float deq_hi(unsigned m, float s24, float b) {
-  return fmaf((float)__builtin_bit_cast(f16x2, m)[1], s24, b);
+__device__ inline float deq_hi(unsigned m, float sc, float b) {
+  return fmaf((float)__builtin_bit_cast(f16x2, m)[1], sc, b);
 }
 
 // bf16(q*s + b) for the 8 codes of octet i of a group, in reduction order. The
 // octet's codes sit in one dword d as two interleaved sets of four byte lanes:
 // element j < 4 in bits [8j, 8j + bits), element 4 + j in bits [8j + 4, 8j + 4 + bits).
-// Masking d (and d shifted by 4, 8 and 12) with one bits-wide field per 16-bit half
-// leaves two codes per dword, one per half, for deq_lo / deq_hi.
+// So each 16-bit half of d holds elements at bits 0 and 4 (both inside a float16's
+// mantissa) and at bits 8 and 12; one shift by 8 and four masks leave two codes per
+// dword, one per half, each at bit 0 or bit 4, for deq_lo / deq_hi.
 template <int BITS>
 __device__ inline bf16x8 deq_octet(const WFrag& f, int i) {
   unsigned d;
@@ -535,17 +537,19 @@ __device__ inline bf16x8 deq_octet(const WFrag& f, int i) {
   } else {
     d = f.c0[i >> 1] >> (2 * (i & 1));
   }
-  constexpr unsigned kM = ((1u << BITS) - 1u) * 0x00010001u;  // one field per half
+  constexpr unsigned kM = ((1u << BITS) - 1u) * 0x00010001u;  // a field at bit 0 of each half
   constexpr unsigned kX = BITS == 4 ? 0x00080008u : 0u;        // 4-bit codes are stored as q ^ 8
-  const unsigned m02 = (d & kM) ^ kX;          // elements 0 (low half) and 2 (high half)
-  const unsigned m13 = ((d >> 8) & kM) ^ kX;   // elements 1 and 3
-  const unsigned m46 = ((d >> 4) & kM) ^ kX;   // elements 4 and 6
-  const unsigned m57 = ((d >> 12) & kM) ^ kX;  // elements 5 and 7
-  const float s24 = bf16lo_to_f32(f.sb) * 16777216.0f, b = bf16hi_to_f32(f.sb);
+  const unsigned e = d >> 8;
+  const unsigned m02 = (d & kM) ^ kX;                  // elements 0 (low half) and 2 (high half), bit 0
+  const unsigned m13 = (e & kM) ^ kX;                  // elements 1 and 3, bit 0
+  const unsigned m46 = (d & (kM << 4)) ^ (kX << 4);    // elements 4 and 6, bit 4
+  const unsigned m57 = (e & (kM << 4)) ^ (kX << 4);    // elements 5 and 7, bit 4
+  const float s = bf16lo_to_f32(f.sb), b = bf16hi_to_f32(f.sb);
+  const float s24 = s * 16777216.0f, s20 = s * 1048576.0f;
   u32x4 r = {pack_bf16(deq_lo(m02, s24, b), deq_lo(m13, s24, b)),
              pack_bf16(deq_hi(m02, s24, b), deq_hi(m13, s24, b)),
-             pack_bf16(deq_lo(m46, s24, b), deq_lo(m57, s24, b)),
-             pack_bf16(deq_hi(m46, s24, b), deq_hi(m57, s24, b))};
+             pack_bf16(deq_lo(m46, s20, b), deq_lo(m57, s20, b)),
+             pack_bf16(deq_hi(m46, s20, b), deq_hi(m57, s20, b))};
   return __builtin_bit_cast(bf16x8, r);
 }
 
