@@ -406,7 +406,11 @@ hipError_t launch_qkv(const moe_qkv_config& c, const uint8_t* w, const float* ga
   // workgroups, some units holding two and some one) by 5% and 640 workgroups by 25%
   const int per = std::max(kNW, (a.geo.nblk_gu + 2 * num_cu - 1) / (2 * num_cu));
   a.nwg = std::max(1, (a.geo.nblk_gu + per - 1) / per);
-  const QkvKernel kern = c.bits == 4 ? qkv_kernel_b4() : c.bits == 3 ? qkv_kernel_b3() : qkv_kernel_b2();
+  // one token: the single-token kernel; several: kQkvTB tokens per pass
+  const QkvKernel kern = T == 1 ? (c.bits == 4 ? qkv_kernel_b4() : c.bits == 3 ? qkv_kernel_b3() : qkv_kernel_b2())
+                                : (c.bits == 4   ? qkv_batched_kernel_b4()
+                                   : c.bits == 3 ? qkv_batched_kernel_b3()
+                                                 : qkv_batched_kernel_b2());
   hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -2611,6 +2611,120 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(QkvArgs a) {
   }
 }
 
+// Several tokens per call. The single-token kernel above re-reads every slot and
+// stages, normalises and encodes one input per pass, with a barrier round trip per
+// token. Here a pass takes kQkvTB tokens: their inputs are requested together,
+// normalised with one barrier and encoded into kQkvTB digit sets in LDS, and every
+// slot, once in registers, is reduced against each token's digits in turn.
+constexpr int kQkvTB = 4;
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void qkv_batched_kernel(QkvArgs a) {
+  __shared__ __align__(16) unsigned dig[kQkvTB][(kMaxDim / kGroup) * kDigitStride];
+  __shared__ __align__(16) float sums[kQkvTB][4 * (kMaxDim / kGroup)];
+  __shared__ float red[kQkvTB][kNW];
+  const Geo& g = a.geo;
+  const int H = g.H;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int p = lane >> g.lGh, grp = lane & (g.Gh - 1);
+  int b0, b1;
+  split_range(g.nblk_gu, a.nwg, blockIdx.x, b0, b1);
+  if (b0 >= b1) return;  // whole workgroup: no block here
+  const int first = b0 + w < b1 ? b0 + w : b0;  // a wave without blocks re-reads a valid one
+  auto blk_of = [&](int b) { return a.w + (size_t)(b < b1 ? b : first) * g.blk; };
+  const int nch = H / 8;
+  for (int t0 = 0; t0 < a.T; t0 += kQkvTB) {
+    const int tb = a.T - t0 < kQkvTB ? a.T - t0 : kQkvTB;
+    Slot S[kQkvB];
+#pragma unroll
+    for (int j = 0; j < kQkvB; ++j) S[j] = ld_slot<BITS>(blk_of(b0 + w + j * kNW), lane, false);
+    issue_order();
+    // thread t holds chunks t and t + kThreads of 8 values of every token of the
+    // pass (tokens past the last are zeros and are never reduced)
+    float v[kQkvTB][16], gm[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = h * kThreads + (int)threadIdx.x;
+      float4 g0 = make_float4(1.f, 1.f, 1.f, 1.f), g1 = g0;
+      if (c < nch && a.gamma) {
+        g0 = ldg_f4(a.gamma + 8 * c);
+        g1 = ldg_f4(a.gamma + 8 * c + 4);
+      }
+      gm[8 * h] = g0.x; gm[8 * h + 1] = g0.y; gm[8 * h + 2] = g0.z; gm[8 * h + 3] = g0.w;
+      gm[8 * h + 4] = g1.x; gm[8 * h + 5] = g1.y; gm[8 * h + 6] = g1.z; gm[8 * h + 7] = g1.w;
+#pragma unroll
+      for (int tt = 0; tt < kQkvTB; ++tt) {
+        float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+        if (c < nch && tt < tb) {
+          const float* xt = a.x + (size_t)(t0 + tt) * H;
+          v0 = ldg_f4(xt + 8 * c);
+          v1 = ldg_f4(xt + 8 * c + 4);
+        }
+        v[tt][8 * h] = v0.x; v[tt][8 * h + 1] = v0.y; v[tt][8 * h + 2] = v0.z; v[tt][8 * h + 3] = v0.w;
+        v[tt][8 * h + 4] = v1.x; v[tt][8 * h + 5] = v1.y; v[tt][8 * h + 6] = v1.z; v[tt][8 * h + 7] = v1.w;
+      }
+    }
+    float rinv[kQkvTB];
+#pragma unroll
+    for (int tt = 0; tt < kQkvTB; ++tt) rinv[tt] = 1.f;
+    if (a.norm) {
+#pragma unroll
+      for (int tt = 0; tt < kQkvTB; ++tt) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss = fmaf(v[tt][i], v[tt][i], ss);
+        ss = wave_sum(ss);
+        if (lane == 0) red[tt][w] = ss;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tt = 0; tt < kQkvTB; ++tt) {
+        float ss = 0.f;
+        for (int i = 0; i < kNW; ++i) ss += red[tt][i];
+        rinv[tt] = 1.f / sqrtf(ss / (float)H + a.eps);
+      }
+    }
+    // x_n = (x * gamma) * rinv, then its digits, one set per token
+#pragma unroll
+    for (int tt = 0; tt < kQkvTB; ++tt) {
+      if (tt >= tb) break;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[tt][i] = (v[tt][i] * gm[i]) * rinv[tt];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = h * kThreads + (int)threadIdx.x;
+        encode_chunk8(v[tt] + 8 * h, dig[tt], sums[tt], c / 8, c % 8, c < nch);
+      }
+    }
+    __syncthreads();
+    for (int ib = b0 + w; ib < b1; ib += kQkvB * kNW) {
+      Slot C[kQkvB];
+#pragma unroll
+      for (int j = 0; j < kQkvB; ++j) C[j] = S[j];
+#pragma unroll
+      for (int j = 0; j < kQkvB; ++j) S[j] = ld_slot<BITS>(blk_of(ib + (kQkvB + j) * kNW), lane, false);
+      for (int tt = 0; tt < tb; ++tt) {
+        Dig D;
+        load_dig(D, dig[tt], sums[tt], grp);
+        const int t = t0 + tt;
+#pragma unroll
+        for (int j = 0; j < kQkvB; ++j) {
+          const int b = ib + j * kNW;
+          if (b >= b1) continue;
+          const float r = seg_sum(slot_dot<BITS>(C[j], D), g.Gh);
+          const int row = (b << g.lPh) + p;
+          if (grp == 0 && row < a.R) {
+            if (row < a.rq) a.yq[(size_t)t * a.rq + row] = r;
+            else if (row < a.rq + a.rk) a.yk[(size_t)t * a.rk + (row - a.rq)] = r;
+            else a.yv[(size_t)t * (a.R - a.rq - a.rk) + (row - a.rq - a.rk)] = r;
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next pass overwrites the staged inputs and their digits
+  }
+}
+
 typedef void (*DecodeKernel)(DecodeArgs, int, int, int);
 typedef void (*QkvKernel)(QkvArgs);
 // Kernel tables, one per code width (each defined in its own file so that the
@@ -2622,5 +2736,8 @@ DecodeKernel decode_kernel_b4(int variant);
 QkvKernel qkv_kernel_b2();
 QkvKernel qkv_kernel_b3();
 QkvKernel qkv_kernel_b4();
+QkvKernel qkv_batched_kernel_b2();
+QkvKernel qkv_batched_kernel_b3();
+QkvKernel qkv_batched_kernel_b4();
 
 }  // namespace qmoe

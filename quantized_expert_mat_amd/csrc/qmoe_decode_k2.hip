@@ -13,5 +13,6 @@ DecodeKernel decode_kernel_b2(int variant) {
 }
 
 QkvKernel qkv_kernel_b2() { return qkv_kernel<2>; }
+QkvKernel qkv_batched_kernel_b2() { return qkv_batched_kernel<2>; }
 
 }  // namespace qmoe

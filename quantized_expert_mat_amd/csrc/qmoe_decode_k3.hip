@@ -13,5 +13,6 @@ DecodeKernel decode_kernel_b3(int variant) {
 }
 
 QkvKernel qkv_kernel_b3() { return qkv_kernel<3>; }
+QkvKernel qkv_batched_kernel_b3() { return qkv_batched_kernel<3>; }
 
 }  // namespace qmoe

@@ -13,5 +13,6 @@ DecodeKernel decode_kernel_b4(int variant) {
 }
 
 QkvKernel qkv_kernel_b4() { return qkv_kernel<4>; }
+QkvKernel qkv_batched_kernel_b4() { return qkv_batched_kernel<4>; }
 
 }  // namespace qmoe

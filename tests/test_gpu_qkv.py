@@ -104,3 +104,29 @@ def test_qkv_zero_tokens_and_bad_config():
     assert float(o.max()) == 7.0
     with pytest.raises(q.MoeError):
         q.moe_qkv_forward(q.QkvConfig.make(512, 0, 8, 8), packed, 1, x, o, o, o)
+
+
+@pytest.mark.parametrize("bits,H,rows,T,norm", [
+    (4, 4096, (4096, 512, 512), 9, True),   # two full passes of four tokens and one token
+    (3, 512, (200, 40, 44), 4, True),       # exactly one pass, ragged last block
+    (2, 256, (64, 32, 33), 6, False),       # a full pass and a half pass
+])
+def test_qkv_batched_tokens(bits, H, rows, T, norm):
+    """Several tokens per call (the batched kernel: four tokens per pass, a partial
+    last pass) against the oracle, and every token bit-identical to a call with that
+    token alone (the single-token kernel: the same encoding and reduction order)."""
+    rng = np.random.default_rng(hash((bits, H, rows, T, 7)) % 2**32)
+    cfg = q.QkvConfig.make(H, *rows, bits=bits, flags=q.MOE_F_RMSNORM if norm else 0)
+    codes, sc, bi = canon(rng, H, rows, bits, {4: 0.02, 3: 0.04, 2: 0.06}[bits])
+    packed = pack(cfg, codes, sc, bi)
+    x = wl.tokens_x(int(rng.integers(1 << 30)), T, H)
+    gamma = (1.0 + 0.1 * rng.normal(size=H)).astype(np.float32)
+    outs = run(cfg, packed, x, gamma)
+    mats = split(codes, sc, bi, rows)
+    for t in range(T):
+        want = ref.qkv(mats, x[t], gamma=gamma, norm=norm)
+        for name, got, ref_y in zip("qkv", outs, want):
+            parity(got[t], ref_y, f"{name} token {t}")
+        one = run(cfg, packed, x[t:t + 1], gamma)
+        for name, got, got1 in zip("qkv", outs, one):
+            np.testing.assert_array_equal(got[t], got1[0], err_msg=f"{name} token {t}: batched vs one token")
