@@ -809,16 +809,48 @@ __global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
     load_wpair<BITS>(jb, ch + 2, f0, f1);
     c0.sb &= jb.sbmask;
     c1.sb &= jb.sbmask;
+    if constexpr (MT > 1) {
+      // A fragments one octet ahead: the reads of octet i + 1 (every subtile, also
+      // those without rows: the stage is always in bounds and their products are
+      // never stored) are in flight while octet i is dequantised and multiplied.
+      // (A thin tile keeps one read per octet: four more registers would cost it a
+      // wave per SIMD.)
+      bf16x8 af[MT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x8 b0 = deq_octet<BITS>(c0, i);
-      const bf16x8 b1 = deq_octet<BITS>(c1, i);
+      for (int q = 0; q < MT; ++q) af[q] = lds_afrag(cur, q, 0);
 #pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        if (q < mt_valid) {
-          const bf16x8 af = lds_afrag(cur, q, i);
-          acc0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b0, acc0[q], 0, 0, 0);
-          acc1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b1, acc1[q], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        bf16x8 an[MT];
+        if (i < 7) {
+#pragma unroll
+          for (int q = 0; q < MT; ++q) an[q] = lds_afrag(cur, q, i + 1);
+        }
+        const bf16x8 b0 = deq_octet<BITS>(c0, i);
+        const bf16x8 b1 = deq_octet<BITS>(c1, i);
+#pragma unroll
+        for (int q = 0; q < MT; ++q) {
+          if (q < mt_valid) {
+            acc0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[q], b0, acc0[q], 0, 0, 0);
+            acc1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[q], b1, acc1[q], 0, 0, 0);
+          }
+        }
+        if (i < 7) {
+#pragma unroll
+          for (int q = 0; q < MT; ++q) af[q] = an[q];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8 b0 = deq_octet<BITS>(c0, i);
+        const bf16x8 b1 = deq_octet<BITS>(c1, i);
+#pragma unroll
+        for (int q = 0; q < MT; ++q) {
+          if (q < mt_valid) {
+            const bf16x8 af = lds_afrag(cur, q, i);
+            acc0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b0, acc0[q], 0, 0, 0);
+            acc1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b1, acc1[q], 0, 0, 0);
+          }
         }
       }
     }
