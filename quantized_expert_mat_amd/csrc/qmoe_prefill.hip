@@ -19,9 +19,10 @@
 //            selected router logits (computed here when selection is by sel_bias)
 //   group    one workgroup: counting sort of the (token, slot) pairs by expert
 //            (counts, exclusive scan, row claims); per-expert row runs; m-tile table
-//   gateup   grouped GEMM: rows of one expert x 64 intermediate columns per
-//            workgroup, gate and up fused, h = bf16(silu(g) * u)
-//   down     grouped GEMM: rows x 128 output columns per workgroup -> float32 rows
+//   gateup   grouped GEMM: rows of one expert x 16 intermediate columns per wave
+//            (4 waves per thin-tile workgroup, 8 per thick one), gate and up fused,
+//            h = bf16(silu(g) * u)
+//   down     grouped GEMM: rows x 32 output columns per wave -> float32 rows
 //   combine  y = x_b + sum_k w_k o_k + sum_s o_s, fixed order per token
 //
 // Weights are dequantised in registers by the lane that feeds them to the MFMA (no
@@ -47,8 +48,8 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kChunkT = 2048;      // tokens per pass (bounds the workspace)
 constexpr int kBM = 64;            // rows (token-expert pairs) per thick m-tile
-constexpr int kGuCols = 64;        // intermediate columns per gate/up workgroup
-constexpr int kDnCols = 128;       // output columns per down workgroup
+constexpr int kGuCols = 16;        // intermediate columns per gate/up wave
+constexpr int kDnCols = 32;        // output columns per down wave
 constexpr int kSortMax = 16384;    // routed (token, expert) pairs per pass
 constexpr int kGroupWaves = 1024 / kWave;  // waves of the grouping workgroup
 
@@ -594,9 +595,9 @@ __device__ inline void job_row(const Geo& g, const uint8_t* mat, int row, int P,
   wsb = reinterpret_cast<const unsigned*>(blk + sb_offset(BITS)) + (row % P) * G;
 }
 
-template <int BITS, bool DOWN>
+template <int BITS, bool DOWN, int NWV>
 __device__ inline bool make_job(const PArgs& a, const int4* list, Job& jb) {
-  const int NT = DOWN ? (a.H + kDnCols - 1) / kDnCols : a.I / kGuCols;
+  const int NT = DOWN ? (a.H + NWV * kDnCols - 1) / (NWV * kDnCols) : (a.I + NWV * kGuCols - 1) / (NWV * kGuCols);
   const int item = work_item(list[0].x * NT);
   if (item < 0) return false;
   const int4 td = list[1 + item / NT];
@@ -613,13 +614,16 @@ __device__ inline bool make_job(const PArgs& a, const int4* list, Job& jb) {
   jb.G = G;
   jb.sbmask = kk < G ? 0xFFFFFFFFu : 0u;
   if (!DOWN) {
-    const int j = nt * kGuCols + wave * 16 + (lane & 15);
+    // a wave past the last column (wide workgroups on a narrow layer) reads row 0
+    // and stores nothing
+    const int base = nt * (NWV * kGuCols) + wave * kGuCols;
+    jb.on[0] = jb.on[1] = base < a.I;
+    const int j = jb.on[0] ? base + (lane & 15) : 0;
     job_row<BITS>(g, W, j, g.Ph, g.Gh, kk, jb.wc[0], jb.wc1[0], jb.wsb[0]);
     job_row<BITS>(g, W + g.off_up, j, g.Ph, g.Gh, kk, jb.wc[1], jb.wc1[1], jb.wsb[1]);
     jb.col[0] = jb.col[1] = j;
-    jb.on[0] = jb.on[1] = true;
   } else {
-    const int base = nt * kDnCols + wave * 32;
+    const int base = nt * (NWV * kDnCols) + wave * kDnCols;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       jb.on[s] = base + 16 * s < a.H;
@@ -701,35 +705,39 @@ __device__ inline const uint16_t* a_row(const PArgs& a, const Job& jb, int r) {
 }
 
 // Activations of chunk ch for one LDS stage. A stage holds MT subtiles of 32
-// (kk, i) pieces x 16 rows x 16 B; thread t moves pieces t + 256 v, v < 2 MT:
-// row m = t & 15 of subtile v >> 1, piece c = (t >> 4) + 16 (v & 1). Positions
-// past K (K < 256) re-read the row start: those products meet zero weights.
-template <int MT>
+// (kk, i) pieces x 16 rows x 16 B, 512 pieces per subtile; with 64 NWV threads,
+// thread t moves pieces p = t + 64 NWV v (v < 8 MT / NWV): subtile p >> 9, row
+// m = p & 15 (= t & 15), piece c = (p >> 4) & 31. Positions past K (K < 256)
+// re-read the row start: those products meet zero weights.
+template <int MT, int NWV>
 struct AStage {
-  u32x4 v[2 * MT];
+  static constexpr int kN = 8 * MT / NWV;
+  u32x4 v[kN];
 };
 
-template <int MT>
-__device__ inline void load_achunk(AStage<MT>& st, const uint16_t* const* rowp, int ch, int K,
+template <int MT, int NWV>
+__device__ inline void load_achunk(AStage<MT, NWV>& st, const uint16_t* const* rowp, int ch, int K,
                                    int mt_valid) {
 #pragma unroll
-  for (int v = 0; v < 2 * MT; ++v) {
-    if ((v >> 1) >= mt_valid) continue;
-    const int c = (threadIdx.x >> 4) + 16 * (v & 1);
+  for (int v = 0; v < AStage<MT, NWV>::kN; ++v) {
+    const int sub = (64 * NWV * v) >> 9;  // a compile-time constant (threadIdx.x < 64 NWV)
+    if (sub >= mt_valid) continue;
+    const int c = ((int)(threadIdx.x >> 4) + 4 * NWV * v) & 31;
     int k = ch * kKC2 + 64 * (c >> 3) + 8 * (c & 7);
     k = k < K ? k : 8 * (c & 7);
-    st.v[v] = *reinterpret_cast<const u32x4*>(rowp[v >> 1] + k);
+    st.v[v] = *reinterpret_cast<const u32x4*>(rowp[sub] + k);
   }
 }
 
-template <int MT>
-__device__ inline void store_achunk(const AStage<MT>& st, uint8_t* stage, int mt_valid) {
+template <int MT, int NWV>
+__device__ inline void store_achunk(const AStage<MT, NWV>& st, uint8_t* stage, int mt_valid) {
   const int m = threadIdx.x & 15;
 #pragma unroll
-  for (int v = 0; v < 2 * MT; ++v) {
-    if ((v >> 1) >= mt_valid) continue;
-    const int c = (threadIdx.x >> 4) + 16 * (v & 1);
-    *reinterpret_cast<u32x4*>(stage + (v >> 1) * kSubBytes + c * 256 + m * 16) = st.v[v];
+  for (int v = 0; v < AStage<MT, NWV>::kN; ++v) {
+    const int sub = (64 * NWV * v) >> 9;
+    if (sub >= mt_valid) continue;
+    const int c = ((int)(threadIdx.x >> 4) + 4 * NWV * v) & 31;
+    *reinterpret_cast<u32x4*>(stage + sub * kSubBytes + c * 256 + m * 16) = st.v[v];
   }
 }
 
@@ -749,6 +757,7 @@ __device__ inline void store_rows(const PArgs& a, const Job& jb, const f32x4& c0
     const int m = mbase + r;
     if (m >= jb.nrows) continue;
     if (!DOWN) {
+      if (!jb.on[0]) continue;
       const float gv = c0[r], uv = c1[r];
       const float h = gv / (1.f + __expf(-gv)) * uv;
       a.hbuf[(size_t)(jb.row0 + m) * a.I + jb.col[0]] = (uint16_t)(pack_bf16(h, 0.f) & 0xFFFFu);
@@ -760,11 +769,11 @@ __device__ inline void store_rows(const PArgs& a, const Job& jb, const f32x4& c0
   }
 }
 
-template <int BITS, bool DOWN, int MT>
-__global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
+template <int BITS, bool DOWN, int MT, int NWV>
+__global__ __launch_bounds__(64 * NWV) void gemm_grouped(PArgs a) {
   extern __shared__ uint8_t lds[];
   Job jb;
-  if (!make_job<BITS, DOWN>(a, MT == 1 ? a.thin : a.thick, jb)) return;
+  if (!make_job<BITS, DOWN, NWV>(a, MT == 1 ? a.thin : a.thick, jb)) return;
   const int mt_valid = (jb.nrows + 15) >> 4;
   const int lane = threadIdx.x & 63;
   const uint16_t* rowp[MT];
@@ -780,9 +789,9 @@ __global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
   // activations: LDS stage ch & 1 holds chunk ch, chunk ch + 1 is in registers;
   // weights: chunks ch and ch + 1 in registers, ch + 2 requested during chunk ch
   uint8_t* lds_sb = lds + 2 * MT * kSubBytes;
-  AStage<MT> st;
+  AStage<MT, NWV> st;
   WFrag p0, p1, r0, r1;
-  load_achunk<MT>(st, rowp, 0, jb.K, mt_valid);
+  load_achunk<MT, NWV>(st, rowp, 0, jb.K, mt_valid);
   {
     const u32x4 v0 = load_sbpiece(jb, 0, 0), v1 = load_sbpiece(jb, 0, 1);
     load_wpair<BITS>(jb, 0, p0, p1);
@@ -790,7 +799,7 @@ __global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
     store_sbpiece(lds_sb, 0, 0, v0);
     store_sbpiece(lds_sb, 0, 1, v1);
   }
-  store_achunk<MT>(st, lds, mt_valid);
+  store_achunk<MT, NWV>(st, lds, mt_valid);
 
   auto chunk = [&](int ch, WFrag& f0, WFrag& f1) {
     const uint8_t* cur = lds + (ch & 1) * (MT * kSubBytes);
@@ -798,7 +807,7 @@ __global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
     __syncthreads();  // stage cur is written; stage nxt is no longer read
     WFrag c0 = f0, c1 = f1;
     read_sb(lds_sb, ch, c0.sb, c1.sb);
-    if (ch + 1 < nch) load_achunk<MT>(st, rowp, ch + 1, jb.K, mt_valid);
+    if (ch + 1 < nch) load_achunk<MT, NWV>(st, rowp, ch + 1, jb.K, mt_valid);
     // one set of the next block's (scale, bias) words: set 0 during chunk 4q - 2,
     // set 1 during chunk 4q - 1
     const int bset = ((ch + 2) & 3) == 0 ? 0 : 1;
@@ -854,7 +863,7 @@ __global__ __launch_bounds__(256) void gemm_grouped(PArgs a) {
         }
       }
     }
-    if (ch + 1 < nch) store_achunk<MT>(st, nxt, mt_valid);
+    if (ch + 1 < nch) store_achunk<MT, NWV>(st, nxt, mt_valid);
     if (bnext) store_sbpiece(lds_sb, bq, bset, sbv);
   };
   for (int ch = 0; ch < nch; ch += 2) {
@@ -908,32 +917,66 @@ __global__ void clear_err(unsigned* err) {
 
 dim3 xcd_grid(int items) { return dim3((unsigned)(8 * ((items + 7) / 8))); }
 
+// Waves per workgroup: a thin tile's four waves cover 64 intermediate (128 output)
+// columns. A thick tile's activation chunk (32 KB from L2 through LDS per chunk)
+// serves eight waves, 128 (256) columns, where the layer is that wide: half the
+// activation traffic per weight, and one such workgroup (two waves per SIMD) per CU.
+constexpr int kThinW = 4, kThickW = 8;
+
 // Dynamic LDS of a GEMM workgroup: two activation stages, then each wave's 4 KB of
-// (scale, bias) areas. The thick tiles' 80 KB exceed the default 64 KB limit.
-constexpr size_t kLdsThin = 2 * kSubBytes + 16384, kLdsThick = 2 * kThickMT * kSubBytes + 16384;
+// (scale, bias) areas. The thick tiles' 80 / 96 KB exceed the default 64 KB limit.
+constexpr size_t lds_bytes(int mt, int nwv) { return 2 * (size_t)mt * kSubBytes + 4096 * (size_t)nwv; }
 
 template <int BITS>
 hipError_t gemm_lds_attrs() {
   hipError_t e = hipSuccess;
-  const void* k[2] = {reinterpret_cast<const void*>(&gemm_grouped<BITS, false, kThickMT>),
-                      reinterpret_cast<const void*>(&gemm_grouped<BITS, true, kThickMT>)};
-  for (int i = 0; i < 2 && e == hipSuccess; ++i)
-    e = hipFuncSetAttribute(k[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsThick);
+  const void* k[4] = {reinterpret_cast<const void*>(&gemm_grouped<BITS, false, kThickMT, kThinW>),
+                      reinterpret_cast<const void*>(&gemm_grouped<BITS, true, kThickMT, kThinW>),
+                      reinterpret_cast<const void*>(&gemm_grouped<BITS, false, kThickMT, kThickW>),
+                      reinterpret_cast<const void*>(&gemm_grouped<BITS, true, kThickMT, kThickW>)};
+  const size_t b[4] = {lds_bytes(kThickMT, kThinW), lds_bytes(kThickMT, kThinW), lds_bytes(kThickMT, kThickW),
+                       lds_bytes(kThickMT, kThickW)};
+  for (int i = 0; i < 4 && e == hipSuccess; ++i)
+    e = hipFuncSetAttribute(k[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)b[i]);
   return e;
+}
+
+// Column tiles of a gate/up or down pass for workgroups of nwv waves.
+inline int nt_of(const PArgs& a, bool down, int nwv) {
+  return down ? (a.H + nwv * kDnCols - 1) / (nwv * kDnCols) : (a.I + nwv * kGuCols - 1) / (nwv * kGuCols);
 }
 
 // The gate/up and down passes, thin (one m-tile) and thick (kThickMT m-tiles) items.
 template <int BITS>
-void launch_gemms(const PArgs& a, int thin_max, int thick_max, int nt_gu, int nt_dn, hipStream_t stream) {
-  const size_t lds_thin = kLdsThin, lds_thick = kLdsThick;
-  hipLaunchKernelGGL((gemm_grouped<BITS, false, 1>), xcd_grid(thin_max * nt_gu), dim3(256), lds_thin, stream, a);
-  if (thick_max > 0)
-    hipLaunchKernelGGL((gemm_grouped<BITS, false, kThickMT>), xcd_grid(thick_max * nt_gu), dim3(256), lds_thick,
-                       stream, a);
-  hipLaunchKernelGGL((gemm_grouped<BITS, true, 1>), xcd_grid(thin_max * nt_dn), dim3(256), lds_thin, stream, a);
-  if (thick_max > 0)
-    hipLaunchKernelGGL((gemm_grouped<BITS, true, kThickMT>), xcd_grid(thick_max * nt_dn), dim3(256), lds_thick,
-                       stream, a);
+void launch_gemms(const PArgs& a, int thin_max, int thick_max, hipStream_t stream) {
+  const dim3 thin_blk(64 * kThinW);
+  const size_t lds_thin = lds_bytes(1, kThinW);
+  // eight-wave thick workgroups where every wave has columns in both passes
+  const bool wide = a.I >= kThickW * kGuCols && a.H >= kThickW * kDnCols;
+  hipLaunchKernelGGL((gemm_grouped<BITS, false, 1, kThinW>), xcd_grid(thin_max * nt_of(a, false, kThinW)),
+                     thin_blk, lds_thin, stream, a);
+  if (thick_max > 0) {
+    if (wide)
+      hipLaunchKernelGGL((gemm_grouped<BITS, false, kThickMT, kThickW>),
+                         xcd_grid(thick_max * nt_of(a, false, kThickW)), dim3(64 * kThickW),
+                         lds_bytes(kThickMT, kThickW), stream, a);
+    else
+      hipLaunchKernelGGL((gemm_grouped<BITS, false, kThickMT, kThinW>),
+                         xcd_grid(thick_max * nt_of(a, false, kThinW)), thin_blk,
+                         lds_bytes(kThickMT, kThinW), stream, a);
+  }
+  hipLaunchKernelGGL((gemm_grouped<BITS, true, 1, kThinW>), xcd_grid(thin_max * nt_of(a, true, kThinW)),
+                     thin_blk, lds_thin, stream, a);
+  if (thick_max > 0) {
+    if (wide)
+      hipLaunchKernelGGL((gemm_grouped<BITS, true, kThickMT, kThickW>),
+                         xcd_grid(thick_max * nt_of(a, true, kThickW)), dim3(64 * kThickW),
+                         lds_bytes(kThickMT, kThickW), stream, a);
+    else
+      hipLaunchKernelGGL((gemm_grouped<BITS, true, kThickMT, kThinW>),
+                         xcd_grid(thick_max * nt_of(a, true, kThinW)), thin_blk,
+                         lds_bytes(kThickMT, kThinW), stream, a);
+  }
 }
 
 }  // namespace
@@ -1016,10 +1059,9 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
     const int nz = c.n_experts < TK ? c.n_experts : TK;
     const int thin_max = nz + c.n_shared;
     const int thick_max = TK / 17 + c.n_shared * (n / 17);
-    const int nt_gu = c.inter / kGuCols, nt_dn = (c.hidden + kDnCols - 1) / kDnCols;
-    if (c.bits == 4) launch_gemms<4>(a, thin_max, thick_max, nt_gu, nt_dn, stream);
-    else if (c.bits == 3) launch_gemms<3>(a, thin_max, thick_max, nt_gu, nt_dn, stream);
-    else launch_gemms<2>(a, thin_max, thick_max, nt_gu, nt_dn, stream);
+    if (c.bits == 4) launch_gemms<4>(a, thin_max, thick_max, stream);
+    else if (c.bits == 3) launch_gemms<3>(a, thin_max, thick_max, stream);
+    else launch_gemms<2>(a, thin_max, thick_max, stream);
     const size_t nthreads = (size_t)n * (c.hidden / 4);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
                        stream, a);
