@@ -182,6 +182,8 @@ moe_status moe_expert_forward(const moe_config* cfg, const void* packed_expert, 
  * MOE_F_PREFILL_BF16: all T tokens at once as an expert-grouped bf16 GEMM with
  *   float32 accumulation; rounding points x_b = bf16(x), A = bf16(x_n) (router from
  *   the unrounded x_n), W = bf16(q*s+b), h = bf16(silu(g)*u); y = x_b + ....
+ *   W is q*s+b rounded once as defined for scales |s| < 2^104 (the path multiplies by
+ *   s*2^24 inside a fused multiply-add; larger scales are outside its range).
  *   x dev [T][H] float32; y dev [T][H] float32; sel_bias, boosted as in moe_route;
  *   idx_out, w_out dev [T][K] or NULL. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_layer_weights* layer, int32_t T,
