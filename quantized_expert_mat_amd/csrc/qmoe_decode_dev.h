@@ -1165,9 +1165,10 @@ __device__ __forceinline__ void load_shared_spec(const DecodeArgs& a, const Lds&
 
 // Phase A of the specialised kernel. Thread t holds the 16 x values [8t, 8t + 8)
 // and [H/2 + 8t, H/2 + 8t + 8): polled straight into registers (layer 0: read from
-// x0), squared and summed for the RMSNorm, normalised, dotted with its columns of
-// the workgroup's two router rows (and of the shared-expert gate) and encoded into
-// digits, with two workgroup barriers in all; the chunks a thread encodes are the
+// x0), squared and summed for the RMSNorm and, unnormalised, dotted with its columns
+// of the workgroup's two router rows (and of the shared-expert gate); one workgroup
+// barrier joins the four sums, the RMSNorm factor scales the dot products into the
+// logits, and the normalised values are encoded into digits; the chunks a thread encodes are the
 // ones encode_vectors gives it, so the digits and sums land where the general
 // path puts them. The logits are published before the digits are formed: the
 // encoding then overlaps the logits exchange (nothing reads the digits before
@@ -1228,30 +1229,22 @@ __device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, 
       for (int i = 0; i < 8; ++i) s.xres[base - r0 + i] = v[8 * h + i];
     }
   }
+  // the shared expert's gate/up slots (phase B) and down slot (phase C), requested as
+  // soon as the input has arrived
+  load_shared_spec<BITS>(a, s, l, sh);
+  {
+    // this lane's down slot of the shared expert (the last down job)
+    const DnJob j = down_job(a, s, l, kDnPre - 1);
+    dp.d[kDnPre - 1] = ld_slot<BITS>(j.on ? j.blk : get_layer(a, s, l).shared, j.on ? j.slot : 0, false);
+  }
   const bool norm = (a.flags & MOE_F_RMSNORM) != 0;
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ss = fmaf(v[i], v[i], ss);
-  ss = wave_sum(ss);
-  if (lane == 0) s.sm->redf[w][0] = ss;
-  if (!ok) s.sm->ok = 0;
-  __syncthreads();
-  if (!s.sm->ok) return false;
-  SUBSTAMP(14);
-  load_shared_spec<BITS>(a, s, l, sh);
-  {
-    // this lane's down slot of the shared expert (the last down job): phase C
-    // reduces it while the routed experts' down slots are still arriving
-    const DnJob j = down_job(a, s, l, kDnPre - 1);
-    dp.d[kDnPre - 1] = ld_slot<BITS>(j.on ? j.blk : get_layer(a, s, l).shared, j.on ? j.slot : 0, false);
-  }
-  float rinv = 1.f;
-  if (norm) {
-    ss = 0.f;
-    for (int i = 0; i < kNW; ++i) ss += s.sm->redf[i][0];
-    rinv = 1.f / sqrtf(ss / (float)H + a.eps);
-  }
-  // x_n = (x * gamma) * rinv
+  // x * gamma; the router logits and the shared-expert gate are linear in the
+  // normalised input, so their dot products run on x * gamma beside the sum of
+  // squares, all four reductions share one barrier, and the RMSNorm factor scales
+  // the sums afterwards
   const float* gamma = get_layer(a, s, l).gamma;
   if (gamma) {
 #pragma unroll
@@ -1260,8 +1253,6 @@ __device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, 
       v[4 * q] *= g4.x; v[4 * q + 1] *= g4.y; v[4 * q + 2] *= g4.z; v[4 * q + 3] *= g4.w;
     }
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] *= rinv;
   // the router rows (and gate) prefetched at the end of the previous phase C, this
   // thread's columns
   float acc0 = 0.f, acc1 = 0.f;
@@ -1278,9 +1269,11 @@ __device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, 
     acc1 = fmaf(r1.z, v[4 * q + 2], acc1);
     acc1 = fmaf(r1.w, v[4 * q + 3], acc1);
   }
+  ss = wave_sum(ss);
   acc0 = wave_sum(acc0);
   acc1 = wave_sum(acc1);
   if (lane == 0) {
+    s.sm->redf[w][0] = ss;
     s.sm->redf[w][1] = acc0;
     s.sm->redf[w][2] = acc1;
   }
@@ -1297,13 +1290,26 @@ __device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, 
     part = wave_sum(part);
     if (lane == 0) s.sm->sgp[w][0] = part;
   }
+  if (!ok) s.sm->ok = 0;
   __syncthreads();
+  if (!s.sm->ok) return false;
+  SUBSTAMP(14);
+  float rinv = 1.f;
+  if (norm) {
+    ss = 0.f;
+    for (int i = 0; i < kNW; ++i) ss += s.sm->redf[i][0];
+    rinv = 1.f / sqrtf(ss / (float)H + a.eps);
+  }
+  // x_n = (x * gamma) * rinv
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] *= rinv;
   SUBSTAMP(8);
   // publish this workgroup's two logits
   if (tid < 2 * kRep) {
     const int j = tid / kRep, rp = tid % kRep;
     float lg = 0.f;
     for (int i = 0; i < kNW; ++i) lg += s.sm->redf[i][1 + j];
+    lg *= rinv;
     const int e = blockIdx.x * (kSpecE / kSpecNwg) + j;
     const unsigned long long pv = ((unsigned long long)epoch << 32) | __float_as_uint(lg);
     __hip_atomic_store(xbuf_of(a.lx, a.e_pad, epoch) + (size_t)rp * a.e_pad + lx_pos(e, a.lx_c), pv,
@@ -1313,6 +1319,7 @@ __device__ __forceinline__ bool phase_a_spec(const DecodeArgs& a, const Lds& s, 
   if (a.any_sgate && tid == 0) {
     float z = 0.f;
     for (int i = 0; i < kNW; ++i) z += s.sm->sgp[i][0];
+    z *= rinv;
     s.sm->sgc[0] = get_layer(a, s, l).sgate ? 1.f / (1.f + expf(-z)) : 1.f;
   }
   SUBSTAMP(9);
