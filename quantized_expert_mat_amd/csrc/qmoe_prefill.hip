@@ -32,6 +32,7 @@
 // exact): lane group kk = lane/16 covers group kk of the chunk, positions
 // [64kk, 64kk+64), and MFMA step i (i = 0..7) the octet [64kk+8i, 64kk+8i+8) of it,
 // so each lane dequantises whole groups of one packed slot.
+#include <mutex>
 #include <string>
 
 #include "qmoe_internal.h"
@@ -52,6 +53,7 @@ constexpr int kGuCols = 16;        // intermediate columns per gate/up wave
 constexpr int kDnCols = 32;        // output columns per down wave
 constexpr int kSortMax = 16384;    // routed (token, expert) pairs per pass
 constexpr int kGroupWaves = 1024 / kWave;  // waves of the grouping workgroup
+constexpr int kMaxAttrDevices = 64;        // devices whose kernel attributes are tracked
 
 // ---------------------------------------------------------------------------
 // Workspace layout of one prefill pass
@@ -1019,20 +1021,35 @@ moe_status prefill_forward(const moe_config& c, const moe_layer_weights* lw, int
   a.obuf = reinterpret_cast<float*>(ws + pl.obuf);
   a.sgc = reinterpret_cast<float*>(ws + pl.sgc);
 
-  static bool attr_done = false;
-  const size_t group_lds_max = sizeof(int) * (2 * (size_t)kMaxE + kGroupWaves);
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&group_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)group_lds_max);
-    if (e == hipSuccess) e = gemm_lds_attrs<2>();
-    if (e == hipSuccess) e = gemm_lds_attrs<3>();
-    if (e == hipSuccess) e = gemm_lds_attrs<4>();
+  // the kernels' dynamic-LDS limits, raised once per device (the grouping kernel and
+  // the thick GEMM tiles use more than the default 64 KB)
+  {
+    static std::mutex mu;
+    static bool attr_done[kMaxAttrDevices] = {};
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
     if (e != hipSuccess) {
-      *msg = std::string("hipFuncSetAttribute: ") + hipGetErrorString(e);
+      *msg = std::string("hipStreamGetDevice: ") + hipGetErrorString(e);
       return MOE_ERR_HIP;
     }
-    attr_done = true;
+    if (dev < 0 || dev >= kMaxAttrDevices) {
+      *msg = "device ordinal beyond the library's limit";
+      return MOE_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!attr_done[dev]) {
+      const size_t group_lds_max = sizeof(int) * (2 * (size_t)kMaxE + kGroupWaves);
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&group_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)group_lds_max);
+      if (e == hipSuccess) e = gemm_lds_attrs<2>();
+      if (e == hipSuccess) e = gemm_lds_attrs<3>();
+      if (e == hipSuccess) e = gemm_lds_attrs<4>();
+      if (e != hipSuccess) {
+        *msg = std::string("hipFuncSetAttribute: ") + hipGetErrorString(e);
+        return MOE_ERR_HIP;
+      }
+      attr_done[dev] = true;
+    }
   }
 
   hipLaunchKernelGGL(clear_err, dim3(1), dim3(64), 0, stream, a.err);
