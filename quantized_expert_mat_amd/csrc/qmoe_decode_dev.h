@@ -1801,25 +1801,27 @@ __device__ __forceinline__ bool select_topk_spec(const DecodeArgs& a, const Lds&
   unsigned ck = 0u;
   int cte = 0;
   float clg = 0.f;
+  // each round: the largest key of the active tier (wave-uniform), its lane and
+  // slot, and that key cleared, all with selects (no divergent branch per round)
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const bool tier = k < nbw;
-    unsigned& A0 = tier ? kb0 : kn0;
-    unsigned& A1 = tier ? kb1 : kn1;
-    const unsigned m = max(A0, A1);
+    const unsigned a0 = tier ? kb0 : kn0, a1 = tier ? kb1 : kn1;
+    const unsigned m = max(a0, a1);
     const unsigned W = wave_max_u32(m);
     const int L0 = __builtin_ctzll(__ballot(m == W));
-    const int slot = __builtin_amdgcn_readlane(A0 == m ? 0 : 1, L0);
-    if (lane == L0) {
-      if (slot == 0) A0 = 0u;
-      else A1 = 0u;
-    }
+    const int slot = __builtin_amdgcn_readlane(a0 == m ? 0 : 1, L0);
+    const bool win = lane == L0;
+    const bool c0 = win && slot == 0, c1 = win && slot != 0;
+    kb0 = tier && c0 ? 0u : kb0;
+    kb1 = tier && c1 ? 0u : kb1;
+    kn0 = !tier && c0 ? 0u : kn0;
+    kn1 = !tier && c1 ? 0u : kn1;
     const float lgw = readlane_f(slot == 0 ? lg0 : lg1, L0);
-    if (lane == k) {
-      ck = W;
-      cte = ((tier ? 1 : 0) << 16) | (w * (E / kNW) + 2 * L0 + slot);
-      clg = lgw;
-    }
+    const bool mine = lane == k;
+    ck = mine ? W : ck;
+    cte = mine ? (((tier ? 1 : 0) << 16) | (w * (E / kNW) + 2 * L0 + slot)) : cte;
+    clg = mine ? lgw : clg;
   }
   if (lane < K) {
     s.sm->cand_key[w * K + lane] = ck;
@@ -1840,7 +1842,8 @@ __device__ __forceinline__ bool select_topk_spec(const DecodeArgs& a, const Lds&
   my_lg = 0.f;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    unsigned& A = k < nbd ? mt : mn;
+    const bool tier = k < nbd;  // wave-uniform
+    const unsigned A = tier ? mt : mn;
     unsigned v = A;
     v = max(v, (unsigned)dpp_i<kQuad1032>((int)v));
     v = max(v, (unsigned)dpp_i<kQuad2301>((int)v));
@@ -1850,11 +1853,12 @@ __device__ __forceinline__ bool select_topk_spec(const DecodeArgs& a, const Lds&
     const int L0 = __builtin_ctzll(__ballot(A == W && cv));
     const int e = __builtin_amdgcn_readlane(te, L0) & 0xFFFF;
     const float lw = readlane_f(lgc, L0);
-    if (lane == L0) A = 0u;
-    if (lane == k) {
-      my_idx = e;
-      my_lg = lw;
-    }
+    const bool win = lane == L0;
+    mt = tier && win ? 0u : mt;
+    mn = !tier && win ? 0u : mn;
+    const bool mine = lane == k;
+    my_idx = mine ? e : my_idx;
+    my_lg = mine ? lw : my_lg;
   }
   return true;
 }
