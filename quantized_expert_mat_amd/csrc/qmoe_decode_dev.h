@@ -603,6 +603,28 @@ __device__ __forceinline__ void encode_vectors(float* src, int nvec, int n, floa
   }
 }
 
+// encode_vectors for the routed h of the specialised shape (K * I = 4096 values, two
+// chunks of 8 per thread): both chunks are read from LDS before either is encoded,
+// so the two encodings' dependent DPP and conversion chains overlap.
+__device__ __forceinline__ void encode_h_spec(const float* src, unsigned* dig, float* sum) {
+  constexpr int n = kSpecI, G = n / kGroup, cpv = n / 8;
+  static_assert(kSpecK * cpv == 2 * kThreads, "two chunks of the routed h per thread");
+  float v[2][8];
+  int gi[2], dw[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = h * kThreads + (int)threadIdx.x, j = c / cpv, cc = c % cpv;
+    const float4* p = reinterpret_cast<const float4*>(src + (size_t)j * n + (size_t)cc * 8);
+    const float4 v0 = p[0], v1 = p[1];
+    v[h][0] = v0.x; v[h][1] = v0.y; v[h][2] = v0.z; v[h][3] = v0.w;
+    v[h][4] = v1.x; v[h][5] = v1.y; v[h][6] = v1.z; v[h][7] = v1.w;
+    gi[h] = j * G + cc / 8;
+    dw[h] = cc % 8;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) encode_chunk8(v[h], dig, sum, gi[h], dw[h], true);
+}
+
 // ------------------------------------------------------------ dequant dot
 struct Dig {
   unsigned d[48];
@@ -2240,7 +2262,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
     const Xv sh{hv.base + (size_t)K * I, a.S * I, hv.n_pad};
     static_assert(kSpecS * kSpecI / 2 == kThreads * kSpecShHPer, "the shared h is one round of chunks");
     if (!wg_all(s.sm, xwait<kSpecShHPer>(a, sh, 0, hs + K * I, epoch_of(a, t, l), dp.shp))) return false;
-    encode_vectors<false>(hs + K * I, a.S, I, 1.f, nullptr, s.hdig + K * Gi * kDigitStride,
+    encode_vectors<false>(hs + K * I, kSpecS, kSpecI, 1.f, nullptr, s.hdig + K * Gi * kDigitStride,
                           s.hsum + 4 * K * Gi);
     __syncthreads();
     // the routed h is requested before the shared pass, so its round trip overlaps
@@ -2254,7 +2276,7 @@ __device__ __forceinline__ bool phase_c(const DecodeArgs& a, const Lds& s, int t
     down_from_regs<BITS, STREAM>(a, s, l, dp, a.npass_routed, a.npass);
     if (!wg_all(s.sm, xwait<kSpecRtHPer>(a, rt, 0, hs, epoch_of(a, t, l), rtp))) return false;
     SUBSTAMP(13);
-    encode_vectors<false>(hs, K, I, 1.f, nullptr, s.hdig, s.hsum);
+    encode_h_spec(hs, s.hdig, s.hsum);
     __syncthreads();
   } else {
     {
